@@ -1,0 +1,285 @@
+"""CPU oracle for the QSA (Qwen Sparse Attention) hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the
+HIP library and its Python binding) never calls it, and this module imports
+nothing from the product package.
+
+Plain, slow and direct: numpy in float64, except at the rounding points the
+method defines (listed per function).  No blocking, fusion or reordering
+beyond what each definition states.
+
+Pages cited (titles as published):
+  [card]    "Qwen3.8-Flash-Next - 面向 Qwen4 架构的实验性预览权重发布"
+            (aiboss88.com), model-card paragraph on the structure.
+  [ailearn] "Qwen3.8-Flash-Next 没有缩小模型，它重写了每个参数何时上场"
+            (ailearn.mscapital.top): the config table "公开 Config 的结构快照",
+            section "03 · Attention" with the BLOCK SCORE and CAUSAL SPARSE SET
+            equations and the five-step QSA list.
+  [sysgeek] "Qwen3.8-Flash-Next：全新架构，迈向极致性价比" (sysgeek.cn),
+            the QSA paragraph of the Attention section.
+
+Readings where the pages leave a step open (each also stated where it is used):
+  * block key = plain mean of the 4 token keys (no RMSNorm, no block RoPE);
+  * score = sum_h w_h * ReLU(q_h . kbar_b / sqrt(128)); with w = 1 this ranks
+    blocks exactly like the pages' unweighted, unscaled score;
+  * ties in the top-K go to the lower block index;
+  * core RoPE: rotate-half on dims 0..63, pairs (j, j+32), base 1e7, angles in
+    float64;
+  * softmax scale 1/sqrt(256) = 1/16; Q head h reads KV head floor(h/12).
+
+Arrays holding bf16 data are passed as float64 arrays whose values are exactly
+representable in bf16 (the caller decodes bf16 losslessly).
+
+Parity pins: every function here is checked against facts that do not come
+from this file (closed forms, invariants, brute force, library routines); see
+the tests whose names start with test_oracle_.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Shapes of the QSA layer ([card] structure paragraph; [ailearn] config table).
+R = 4                 # micro-block ratio r: tokens per block
+TOKEN_BUDGET = 2048   # K, tokens kept from completed blocks
+K_B = 512             # block budget ceil(K / r)   ([ailearn] CAUSAL SPARSE SET)
+H_I, D_I = 4, 128     # indexer: 4 query heads over 1 shared key, width 128
+H_Q, H_KV, D = 24, 2, 256
+GROUP = H_Q // H_KV   # 12 query heads per KV head
+D_ROPE = 64           # rotated dims of the core heads
+ROPE_BASE = 1.0e7
+SOFTMAX_SCALE = 1.0 / 16.0                       # 1/sqrt(256), a power of two
+SCORE_SCALE = np.float32(1.0 / np.sqrt(128.0))   # 1/sqrt(d_I), rounded once to fp32
+
+
+# ---------------------------------------------------------------- bf16 helper
+
+def round_to_bf16(x) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float64.
+
+    bf16 keeps the upper 16 bits of the IEEE-754 binary32 pattern.
+    """
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if np.isnan(f).any():
+        raise ValueError("NaN reached a bf16 rounding point")
+    u = f.view(np.uint32).astype(np.uint64)
+    half = np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
+    hi = ((u + half) >> np.uint64(16)) & np.uint64(0xFFFF)
+    return (hi.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------- indexer: pooling
+
+def pool_block_keys(idx_k: np.ndarray, n_blocks: int) -> np.ndarray:
+    """Mean of each non-overlapping 4-token micro-block of the indexer key.
+
+    [ailearn] §03, first QSA step (average-pool the keys over non-overlapping
+    4-token micro-blocks) and the indexer figure caption (pooling on the key
+    side).  Reading: the block key is the plain mean; the pages' RMSNorm and
+    block RoPE that follow need trained weights and are not applied.
+
+    Rounding points: the sum is taken in float32 in token order
+    ((k0 + k1) + k2) + k3, multiplied by 0.25 in float32, then rounded to bf16.
+
+    idx_k: [L][128] token keys (bf16 values).  Returns [n_blocks][128].
+    """
+    k = np.asarray(idx_k, dtype=np.float64)
+    assert k.shape[0] >= R * n_blocks
+    # t[j] holds token j of every block; the arithmetic is elementwise per block.
+    t = k[:R * n_blocks].reshape(n_blocks, R, D_I).astype(np.float32)
+    s = t[:, 0] + t[:, 1]
+    s = s + t[:, 2]
+    s = s + t[:, 3]
+    return round_to_bf16(s * np.float32(0.25))
+
+
+# -------------------------------------------------------- indexer: scoring
+
+def completed_blocks(i: int) -> int:
+    """n_c(i): blocks b whose last token p_b + r - 1 = 4b + 3 is at or before i.
+
+    [ailearn] §03, BLOCK SCORE equation: a block is scored only when
+    p_b + r - 1 <= i (reading p_b = r*b, the block's first token); every other
+    block scores minus infinity and is never a candidate.
+    """
+    return (i + 1) // R
+
+
+def block_scores(q_i: np.ndarray, w_i: np.ndarray, kbar: np.ndarray) -> np.ndarray:
+    """Indexer score of each candidate block for one query.
+
+    [ailearn] §03 BLOCK SCORE equation and third QSA step: the 4 indexer query
+    heads each take a dot product with the shared pooled key, ReLU is applied,
+    and the heads are summed.  Reading: each head is also weighted by w_h and
+    the dot is scaled by 1/sqrt(128); with w = 1 this orders blocks as the
+    unweighted form does.
+
+    Rounding points (float32 decides the selection on both sides):
+      dot_h = sum_d q_h[d] kbar[d]              in float64
+      t_h   = float32(dot_h)
+      u_h   = float32(max(t_h, 0) * SCORE_SCALE)
+      s     = ((w0*u0 + w1*u1) + w2*u2) + w3*u3 each product and sum rounded to float32
+      -0 is returned as +0.
+
+    q_i: [4][128], w_i: [4] float32, kbar: [n][128] (the n candidate blocks).
+    Returns float32 [n].
+    """
+    q = np.asarray(q_i, dtype=np.float64)
+    kb = np.asarray(kbar, dtype=np.float64).reshape(-1, D_I)
+    w = np.asarray(w_i, dtype=np.float32)
+    dots = q @ kb.T                                   # [4][n] float64
+    t = dots.astype(np.float32)
+    u = np.maximum(t, np.float32(0.0)) * SCORE_SCALE  # float32
+    acc = np.zeros(kb.shape[0], dtype=np.float32)
+    for h in range(H_I):
+        acc = acc + w[h] * u[h]
+    acc[acc == 0] = np.float32(0.0)
+    return acc
+
+
+# ------------------------------------------------------ indexer: selection
+
+def select_blocks(scores: np.ndarray, budget: int) -> np.ndarray:
+    """B_i: the min(budget, n_c) best candidates, returned in ascending block order.
+
+    [ailearn] §03 CAUSAL SPARSE SET equation (top-K_B of the block scores,
+    K_B = ceil(K/r) = 512) and fourth QSA step (at most 512 complete blocks).
+    Reading: the order is score descending, then block index ascending, so
+    equal scores keep the lower block; fewer candidates than the budget means
+    all of them are kept.
+    """
+    s = np.asarray(scores, dtype=np.float32).astype(np.float64)
+    n = s.shape[0]
+    k_eff = min(int(budget), n)
+    order = np.lexsort((np.arange(n), -s))
+    return np.sort(order[:k_eff]).astype(np.int64)
+
+
+def sparse_token_set(blocks: np.ndarray, i: int) -> np.ndarray:
+    """S_i = Expand(B_i) united with the current unfinished tail {r*n_c(i), ..., i}.
+
+    [ailearn] §03 CAUSAL SPARSE SET equation and its note that the unfinished
+    current block is kept because it is causally visible.  Returns token
+    positions in ascending order of block, then the tail.
+    """
+    b = np.asarray(blocks, dtype=np.int64)
+    expanded = (R * b[:, None] + np.arange(R)[None, :]).reshape(-1)
+    tail = np.arange(R * completed_blocks(i), i + 1, dtype=np.int64)
+    return np.concatenate([expanded, tail])
+
+
+# ------------------------------------------------------------ core attention
+
+def rope(x: np.ndarray, pos) -> np.ndarray:
+    """Partial rotary embedding on the first 64 of 256 dims.
+
+    [card] structure paragraph and [ailearn] config table (rotary dim 64) and
+    second QSA step (the core uses 64 of 256 dims).  Reading: rotate-half with
+    pairs (j, j+32), angle theta_j = pos * 1e7^(-j/32), everything in float64;
+    dims 64..255 pass through.
+
+    x: [..., 256]; pos: scalar or array broadcast against x[..., 0].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    p = np.asarray(pos, dtype=np.float64)[..., None]
+    j = np.arange(D_ROPE // 2, dtype=np.float64)
+    theta = p * ROPE_BASE ** (-2.0 * j / D_ROPE)
+    c, s = np.cos(theta), np.sin(theta)
+    y = x.copy()
+    x1, x2 = x[..., :D_ROPE // 2], x[..., D_ROPE // 2:D_ROPE]
+    y[..., :D_ROPE // 2] = x1 * c - x2 * s
+    y[..., D_ROPE // 2:D_ROPE] = x2 * c + x1 * s
+    return y
+
+
+def attend(q_i: np.ndarray, k_raw: np.ndarray, v: np.ndarray, tokens: np.ndarray,
+           i: int):
+    """Exact GQA softmax attention of query i over the token set S_i.
+
+    [ailearn] §03 fifth QSA step: the 24-query / 2-KV core attends exactly over
+    the original tokens of S_i.  Q and K are rotated at their own positions;
+    logits are scaled by 1/16; head h reads KV head floor(h/12).
+
+    q_i: [24][256] raw query; k_raw, v: [L][2][256] raw cache rows (K not
+    rotated).  Returns (O [24][256], lse [24]) in float64, lse = log sum exp of
+    the scaled logits.
+    """
+    S = np.asarray(tokens, dtype=np.int64)
+    qr = rope(np.asarray(q_i, dtype=np.float64), i)
+    kr = rope(np.asarray(k_raw, dtype=np.float64)[S], S[:, None])   # [n][2][256]
+    vs = np.asarray(v, dtype=np.float64)[S]                         # [n][2][256]
+    out = np.empty((H_Q, D), dtype=np.float64)
+    lse = np.empty(H_Q, dtype=np.float64)
+    for h in range(H_Q):
+        g = h // GROUP
+        logits = (kr[:, g, :] @ qr[h]) * SOFTMAX_SCALE
+        m = logits.max()
+        p = np.exp(logits - m)
+        l = p.sum()
+        out[h] = (p @ vs[:, g, :]) / l
+        lse[h] = m + np.log(l)
+    return out, lse
+
+
+# ---------------------------------------------------------------- pipeline
+
+def qsa_query(idx_q_i, w_i, kbar, q_i, k_raw, v, i: int, budget: int):
+    """All steps for one query at position i: score, select, expand, attend.
+
+    kbar must hold at least n_c(i) pooled block keys of the query's sequence;
+    k_raw and v hold the raw cache rows of that sequence ([L][2][256]).
+    Returns (blocks, out, lse).
+    """
+    n_c = completed_blocks(i)
+    s = block_scores(idx_q_i, w_i, np.asarray(kbar)[:n_c])
+    blocks = select_blocks(s, budget)
+    tokens = sparse_token_set(blocks, i)
+    out, lse = attend(q_i, k_raw, v, tokens, i)
+    return blocks, out, lse
+
+
+def selection_gap(scores: np.ndarray, q_i, w_i, kbar, budget: int):
+    """Boundary gap and rounding allowance used to compare a float32 selection.
+
+    Returns (gap, delta, s_k): gap = s_(K) - s_(K+1) of the sorted scores (inf
+    when every candidate is kept), s_k = s_(K), and delta = 2^-15 * max_b
+    sum_h w_h sum_d |q_h[d] kbar_b[d]| / sqrt(128), an upper bound on how far
+    a float32-accumulated score can sit from this oracle's score (128-term
+    dot products carry a relative error below 2^-17; 4x slack).
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.shape[0]
+    k_eff = min(int(budget), n)
+    srt = np.sort(s)[::-1]
+    gap = np.inf if k_eff >= n else srt[k_eff - 1] - srt[k_eff]
+    s_k = srt[k_eff - 1] if k_eff > 0 else np.inf
+    absdots = np.abs(np.asarray(q_i, np.float64)) @ np.abs(np.asarray(kbar, np.float64)).T
+    mag = (np.asarray(w_i, np.float64)[:, None] * absdots).sum(0) / np.sqrt(128.0)
+    delta = 2.0 ** -15 * (mag.max() if mag.size else 0.0)
+    return gap, delta, s_k
+
+
+def dense_causal_gqa(q_i: np.ndarray, k_raw: np.ndarray, v: np.ndarray, i: int):
+    """Textbook causal GQA attention of query i over every token 0..i.
+
+    Deliberately separate from attend(): token-by-token loops, no token set.
+    Used to pin the sparse path, which must equal this whenever the budget
+    covers every completed block.
+    """
+    qr = rope(np.asarray(q_i, dtype=np.float64), i)
+    out = np.zeros((H_Q, D), dtype=np.float64)
+    lse = np.zeros(H_Q, dtype=np.float64)
+    k_raw = np.asarray(k_raw, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    for h in range(H_Q):
+        g = h // GROUP
+        logits = [float(rope(k_raw[j, g], j) @ qr[h]) / 16.0 for j in range(i + 1)]
+        m = max(logits)
+        weights = [np.exp(x - m) for x in logits]
+        total = sum(weights)
+        acc = np.zeros(D)
+        for j in range(i + 1):
+            acc += weights[j] * v[j, g]
+        out[h] = acc / total
+        lse[h] = m + np.log(total)
+    return out, lse

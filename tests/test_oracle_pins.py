@@ -1,0 +1,363 @@
+"""Pins for the CPU oracle: each test checks it against a fact that does not
+come from the oracle itself (hand-worked values, closed forms, invariants,
+brute force on tiny inputs, or a library routine for a special case).
+
+CPU only.  The pages cited are listed in the oracle's header.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import qsa_oracle as O
+from block_sparse_long_02_amd import workloads as W
+
+
+def bf16_vals(t: torch.Tensor) -> np.ndarray:
+    return t.float().double().numpy()
+
+
+# ------------------------------------------------------------------ constants
+
+def test_oracle_constants_match_pages(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "qsa_constants.json")))
+    for name in ["H_Q", "H_KV", "D", "D_ROPE", "H_I", "D_I", "R", "TOKEN_BUDGET", "K_B"]:
+        assert getattr(O, name) == g[name]["value"], name
+    # K_B = ceil(K / r)
+    assert O.K_B == math.ceil(O.TOKEN_BUDGET / O.R)
+    assert O.GROUP * O.H_KV == O.H_Q
+
+
+# ---------------------------------------------------------------------- bf16
+
+def test_oracle_bf16_rne_hand_cases():
+    one = 1.0
+    cases = {
+        one + 2.0 ** -8: 1.0,                  # halfway, even neighbour is 1.0
+        one + 3 * 2.0 ** -8: one + 2.0 ** -6,  # halfway, even neighbour above
+        one + 2.0 ** -8 + 2.0 ** -20: one + 2.0 ** -7,  # just above halfway
+        -(one + 2.0 ** -8): -1.0,
+        0.0: 0.0,
+        3.0e38: 3.00405527047391e+38,          # below the largest bf16 (3.3895e38)
+        3.4e38: float("inf"),                  # above the midpoint 3.3961e38
+    }
+    for x, want in cases.items():
+        got = O.round_to_bf16(np.float32(x)).item()
+        assert got == want, (x, float(got), want)
+
+
+def test_oracle_bf16_rne_matches_torch():
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(200000, generator=g) * torch.exp(torch.randn(200000, generator=g) * 8)
+    ref = x.to(torch.bfloat16).double().numpy()
+    got = O.round_to_bf16(x.numpy())
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------- pooling
+
+def test_oracle_pool_identical_tokens():
+    g = torch.Generator().manual_seed(1)
+    tok = torch.randn(7, 128, generator=g).to(torch.bfloat16)
+    keys = tok.repeat_interleave(4, dim=0)           # every block = 4 copies
+    pooled = O.pool_block_keys(bf16_vals(keys), 7)
+    assert np.array_equal(pooled, bf16_vals(tok))
+
+
+def test_oracle_pool_equals_rounded_exact_mean():
+    # Moderate-range bf16 inputs: the float32 sum of 4 of them is exact, so the
+    # pooled key must be the exact mean rounded once to bf16 (by torch).
+    g = torch.Generator().manual_seed(2)
+    keys = torch.randn(64 * 4, 128, generator=g).to(torch.bfloat16)
+    kv = bf16_vals(keys)
+    pooled = O.pool_block_keys(kv, 64)
+    exact = np.zeros((64, 128))
+    for b in range(64):
+        for d in range(128):
+            m = sum(Fraction(kv[4 * b + t, d]) for t in range(4)) / 4
+            exact[b, d] = float(m)          # exact: a float32-representable value
+    ref = torch.tensor(exact, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(pooled, ref)
+
+
+def test_oracle_pool_order_of_addition(golden_dir):
+    case = json.load(open(os.path.join(golden_dir, "hand_worked_query.json")))["pool_order_case"]
+    keys = np.zeros((4, 128))
+    keys[:, 0] = case["tokens"]
+    assert O.pool_block_keys(keys, 1)[0, 0] == case["expected"]
+
+
+# ------------------------------------------------------------------- scoring
+
+def test_oracle_candidates_closed_form():
+    # brute force over b of the condition p_b + r - 1 <= i with p_b = r*b
+    for i in range(0, 200):
+        brute = sum(1 for b in range(100) if 4 * b + 4 - 1 <= i)
+        assert O.completed_blocks(i) == brute
+
+
+def _grid(shape, g):
+    return torch.clamp(torch.round(torch.randn(shape, generator=g) * 8) / 8, -4, 4).double().numpy()
+
+
+def test_oracle_score_one_hot_weights_and_relu():
+    g = torch.Generator().manual_seed(3)
+    q = _grid((4, 128), g)
+    kb = _grid((300, 128), g) / 4        # multiples of 1/32, like pooled grid keys
+    for h in range(4):
+        w = np.zeros(4, np.float32)
+        w[h] = 1.0
+        s = O.block_scores(q, w, kb)
+        # exact rational dot of head h only
+        for b in range(0, 300, 7):
+            dot = sum(Fraction(q[h, d]) * Fraction(kb[b, d]) for d in range(128))
+            if dot <= 0:
+                assert s[b] == 0.0
+            else:
+                # s = dot * c with c = 1/sqrt(128): compare to the real value
+                real = float(dot) / math.sqrt(128.0)
+                assert abs(float(s[b]) - real) <= 2.0 ** -22 * real
+        # changing the other heads' queries must not change the score
+        q2 = q.copy()
+        for hh in range(4):
+            if hh != h:
+                q2[hh] = -q2[hh] + 0.5
+        assert np.array_equal(O.block_scores(q2, w, kb), s)
+
+
+def test_oracle_score_unit_weights_rank_like_pages():
+    # The pages' score is sum_h ReLU(<q_h, kbar_b>) (no weights, no scale).
+    # With w = 1 the oracle's score must order blocks the same way.
+    g = torch.Generator().manual_seed(4)
+    q = _grid((4, 128), g)
+    kb = _grid((400, 128), g) / 4
+    s = O.block_scores(q, np.ones(4, np.float32), kb)
+    pages = []
+    for b in range(400):
+        tot = Fraction(0)
+        for h in range(4):
+            dot = sum(Fraction(q[h, d]) * Fraction(kb[b, d]) for d in range(128))
+            tot += max(dot, Fraction(0))
+        pages.append(tot)
+    # s = c * sum_h ReLU(dot_h) up to a relative rounding error below 2^-21
+    # (four float32 roundings of non-negative terms); grid dots are multiples of
+    # 2^-8, so distinct page scores differ far more than that and must keep their
+    # order strictly, while equal page scores may differ only by that rounding.
+    c = 1 / math.sqrt(128.0)
+    for a in range(400):
+        assert abs(float(s[a]) - c * float(pages[a])) <= 2.0 ** -21 * c * float(pages[a])
+        for b in range(a + 1, 400):
+            if pages[a] > pages[b]:
+                assert s[a] > s[b]
+            elif pages[a] < pages[b]:
+                assert s[a] < s[b]
+            else:
+                assert abs(float(s[a]) - float(s[b])) <= 2.0 ** -20 * float(s[a])
+
+
+def test_oracle_score_positive_homogeneity():
+    g = torch.Generator().manual_seed(6)
+    q = bf16_vals(torch.randn(4, 128, generator=g).to(torch.bfloat16))
+    kb = bf16_vals(torch.randn(100, 128, generator=g).to(torch.bfloat16))
+    w = torch.softmax(torch.randn(4, generator=g), 0).numpy().astype(np.float32)
+    s1 = O.block_scores(q, w, kb)
+    s2 = O.block_scores(q, w, 2.0 * kb)
+    assert np.array_equal(s2, 2.0 * s1)
+    assert (s1 >= 0).all()
+    # every head negative => score exactly +0
+    s3 = O.block_scores(np.abs(q), w, -np.abs(kb))
+    assert np.all(s3 == 0) and not np.signbit(s3).any()
+
+
+# ----------------------------------------------------------------- selection
+
+def test_oracle_select_matches_full_sort():
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        n = int(rng.integers(1, 60))
+        # few distinct values => many ties
+        s = rng.integers(0, 5, size=n).astype(np.float32) * np.float32(0.25)
+        budget = int(rng.integers(1, 70))
+        brute = sorted(range(n), key=lambda b: (-float(s[b]), b))[:min(budget, n)]
+        assert list(O.select_blocks(s, budget)) == sorted(brute)
+
+
+def test_oracle_select_counts_and_ties(golden_dir):
+    s = np.zeros(1000, np.float32)
+    assert len(O.select_blocks(s, 512)) == 512
+    assert list(O.select_blocks(s, 512)) == list(range(512))   # all tied: lowest ids
+    assert len(O.select_blocks(s[:37], 512)) == 37
+    # 513 identical planted blocks among noise: the highest-index one is dropped
+    rng = np.random.default_rng(8)
+    s = rng.random(5000).astype(np.float32)
+    planted = np.sort(rng.choice(5000, 513, replace=False))
+    s[planted] = 7.0
+    sel = O.select_blocks(s, 512)
+    assert list(sel) == list(planted[:512])
+    case = json.load(open(os.path.join(golden_dir, "hand_worked_query.json")))["tie_variant"]
+    keys = np.zeros((14, 128))
+    keys[:, 0] = case["token_key_dim0"]
+    kb = O.pool_block_keys(keys, 3)
+    q = np.zeros((4, 128))
+    q[0, 0] = 1.0
+    w = np.array([1, 0, 0, 0], np.float32)
+    sc = O.block_scores(q, w, kb)
+    assert list(O.select_blocks(sc, case["budget"])) == case["expected_blocks"]
+
+
+def test_oracle_planted_blocks_recovered():
+    b = W.decode_128k(n_seq=3, ctx=8192)
+    for s in range(3):
+        L = b.seq_lens_host()[s]
+        kb = O.pool_block_keys(bf16_vals(b.idx_k[s]), L // 4)
+        sc = O.block_scores(bf16_vals(b.idx_q[s]), b.w[s].numpy(), kb)
+        sel = set(O.select_blocks(sc, 512).tolist())
+        assert set(b.planted[s]) <= sel
+
+
+# ------------------------------------------------------------- sparse set
+
+def test_oracle_sparse_set_size_and_dense_case():
+    rng = np.random.default_rng(9)
+    for i in range(0, 300):
+        n_c = O.completed_blocks(i)
+        for budget in (1, 3, 16, 512):
+            k_eff = min(budget, n_c)
+            blocks = np.sort(rng.choice(max(n_c, 1), k_eff, replace=False)) if k_eff else np.zeros(0, int)
+            S = O.sparse_token_set(blocks, i)
+            assert len(S) == 4 * k_eff + (i + 1) % 4
+            assert len(set(S.tolist())) == len(S) and S.max() <= i
+            if n_c <= budget:
+                assert sorted(S.tolist()) == list(range(i + 1))
+
+
+def test_oracle_hand_worked_query(golden_dir):
+    case = json.load(open(os.path.join(golden_dir, "hand_worked_query.json")))
+    i = case["query_position"]
+    keys = np.zeros((16, 128))
+    keys[:14, 0] = case["token_key_dim0"]
+    kb = O.pool_block_keys(keys, O.completed_blocks(i))
+    assert O.completed_blocks(i) == case["completed_blocks"]
+    assert list(kb[:, 0]) == case["pooled_dim0"]
+    q = np.zeros((4, 128))
+    q[0, 0] = 1.0
+    w = np.array([1, 0, 0, 0], np.float32)
+    blocks = O.select_blocks(O.block_scores(q, w, kb), case["budget"])
+    assert list(blocks) == case["expected_blocks"]
+    S = O.sparse_token_set(blocks, i)
+    assert list(S) == case["expected_tokens"]
+    # zero core query => uniform weights; V dim 0 = token position
+    L = 16
+    k_raw = np.random.default_rng(1).standard_normal((L, 2, 256))
+    v = np.zeros((L, 2, 256))
+    v[:, :, 0] = np.arange(L)[:, None]
+    out, lse = O.attend(np.zeros((24, 256)), k_raw, v, S, i)
+    assert np.allclose(out[:, 0], case["expected_out_dim0_with_zero_q_and_v_equal_position"], atol=1e-12)
+    assert np.allclose(lse, math.log(10), atol=1e-12)
+
+
+# ---------------------------------------------------------------------- RoPE
+
+def test_oracle_rope_properties():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((5, 256))
+    assert np.allclose(O.rope(x, 0), x, atol=0, rtol=0)
+    for p in (1, 17, 4096, 1048575):
+        y = O.rope(x, p)
+        assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+        assert np.array_equal(y[:, 64:], x[:, 64:])
+        assert np.all(np.abs(y[:, :64] - x[:, :64]).max(axis=0) > 0)
+    # relative position: <rope(q,p), rope(k,p')> depends on p - p' only
+    q, k = rng.standard_normal(256), rng.standard_normal(256)
+    for p, pp, shift in [(10, 3, 4096), (1000, 999, 100000), (5, 5, 77)]:
+        a = O.rope(q, p) @ O.rope(k, pp)
+        b = O.rope(q, p + shift) @ O.rope(k, pp + shift)
+        assert abs(a - b) < 1e-9 * (1 + abs(a))
+
+
+def test_oracle_rope_angles_read_back():
+    # rotating e_j moves it by angle theta_j = p * 1e7^(-j/32) into the plane (j, j+32)
+    for p in (1, 3, 1000, 123457):
+        for j in (0, 1, 7, 31):
+            e = np.zeros(256)
+            e[j] = 1.0
+            y = O.rope(e, p)
+            ang = math.atan2(y[j + 32], y[j])
+            want = math.remainder(p * 10.0 ** (-7.0 * j / 32.0), 2 * math.pi)
+            assert abs(math.remainder(ang - want, 2 * math.pi)) < 1e-9
+
+
+# ------------------------------------------------------------------ attention
+
+def _small_cache(L, seed):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((L, 2, 256))
+    v = rng.standard_normal((L, 2, 256))
+    q = rng.standard_normal((24, 256))
+    return q, k, v
+
+
+def test_oracle_sparse_equals_dense_when_budget_covers():
+    q, k, v = _small_cache(23, 11)
+    for i in (0, 3, 4, 13, 22):
+        n_c = O.completed_blocks(i)
+        blocks = np.arange(n_c)                 # budget >= n_c keeps every block
+        S = O.sparse_token_set(blocks, i)
+        o1, l1 = O.attend(q, k, v, S, i)
+        o2, l2 = O.dense_causal_gqa(q, k, v, i)
+        assert np.allclose(o1, o2, atol=1e-12, rtol=1e-12)
+        assert np.allclose(l1, l2, atol=1e-12, rtol=1e-12)
+
+
+def test_oracle_dense_matches_torch_sdpa():
+    # Library routine for the dense special case: torch's scaled dot product
+    # attention in float64 on rotated inputs, KV heads repeated per group.
+    q, k, v = _small_cache(40, 12)
+    i = 39
+    qr = torch.tensor(O.rope(q, i))[None, :, None, :]                  # [1][24][1][256]
+    kr = torch.tensor(O.rope(k, np.arange(40)[:, None]))                # [40][2][256]
+    kk = kr.permute(1, 0, 2).repeat_interleave(12, dim=0)[None]         # [1][24][40][256]
+    vv = torch.tensor(v).permute(1, 0, 2).repeat_interleave(12, dim=0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qr, kk, vv, scale=1 / 16)[0, :, 0]
+    out, _ = O.dense_causal_gqa(q, k, v, i)
+    assert np.allclose(out, ref.numpy(), atol=1e-12)
+
+
+def test_oracle_attention_reveals_attended_set():
+    # zero query => uniform softmax over S_i: out = mean of V over S_i exactly
+    L = 64
+    _, k, _ = _small_cache(L, 13)
+    v = np.zeros((L, 2, 256))
+    v[:, :, 0] = np.arange(L)[:, None]
+    v[:, :, 1] = (np.arange(L) ** 2)[:, None]
+    v[:, 1, 2] = 3.25                        # constant channel
+    i = 57
+    blocks = np.array([2, 5, 9])
+    S = O.sparse_token_set(blocks, i)
+    out, lse = O.attend(np.zeros((24, 256)), k, v, S, i)
+    assert np.allclose(out[:, 0], np.mean(S), atol=1e-12)
+    assert np.allclose(out[:, 1], np.mean(S.astype(float) ** 2), atol=1e-9)
+    assert np.allclose(out[12:, 2], 3.25, atol=1e-14)
+    assert np.allclose(lse, math.log(len(S)), atol=1e-12)
+
+
+def test_oracle_query_pipeline_on_generated_prefill():
+    # End-to-end on a small planted prefill: planted blocks of the segment are
+    # selected, and budget >= n_c reproduces dense attention.
+    b = W.tiny_prefill(T=192)
+    kb = O.pool_block_keys(bf16_vals(b.idx_k[0]), 192 // 4)
+    k_raw = bf16_vals(b.k[0]).transpose(1, 0, 2)
+    v = bf16_vals(b.v[0]).transpose(1, 0, 2)
+    for i in (5, 70, 130, 191):
+        blocks, out, lse = O.qsa_query(bf16_vals(b.idx_q[i]), b.w[i].numpy(), kb,
+                                       bf16_vals(b.q[i]), k_raw, v, i, b.budget)
+        assert len(blocks) == min(b.budget, O.completed_blocks(i))
+        seg_planted = b.planted[i // 64]
+        assert set(seg_planted) <= set(blocks.tolist())
+        if O.completed_blocks(i) <= b.budget:
+            o2, l2 = O.dense_causal_gqa(bf16_vals(b.q[i]), k_raw, v, i)
+            assert np.allclose(out, o2, atol=1e-12)

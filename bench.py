@@ -1,0 +1,273 @@
+"""QSA hot-path benchmark on one MI355X.
+
+Headline (`value`): chunked prefill at 1M context -- a 32,768-token query
+chunk on a 1,015,808-token cached prefix (batch 1, budget 512 blocks + tail):
+query tokens per second for one step = pool the chunk's new blocks, select
+blocks for every query, sparse attention.  Alongside it (`decode`): a decode
+step for 32 sequences of 131,072 cached tokens + the new one.
+
+Inputs are seeded synthetic tensors generated directly in HBM; the timed
+region starts with everything resident.  Timing uses HIP events on the stream
+the kernels run on.  `roofline` is for the dominant kernel (the attention
+kernel of the prefill step): algorithmic bytes per launch / its mean
+duration, against 8 TB/s.  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--only prefill|decode]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QSA tokens/s (prefill, decode) at 128K–1M ctx; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0
+TOKEN_GATHER_BYTES = 2 * 2 * 256 * 2      # 2 KV heads x (K + V) x 256 dims x bf16
+Q_ROW_BYTES = 24 * 256 * 2
+BLOCK_KEY_BYTES = 128 * 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def set_sizes(runner):
+    """Sum over query rows of |S_i| = 4*K_i + tail_i, and of n_c."""
+    import numpy as np
+    cnt = runner.sel_count.cpu().numpy().astype(np.int64)
+    pos = np.asarray(runner.b.q_pos_host(), dtype=np.int64)
+    tails = (pos + 1) % 4
+    return int((4 * cnt + tails).sum()), int(((pos + 1) // 4).sum())
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_file, key):
+    """HBM bytes per launch from committed counter runs, if they were taken on
+    the current source of the kernel's file; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))[key]
+    except (KeyError, ValueError):
+        return None
+    if d.get("source_sha") != src_hash(kernel_file):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def time_prefill(args):
+    import torch
+    from block_sparse_long_02_amd import workloads as W
+    from block_sparse_long_02_amd.runner import QSARunner
+
+    t0 = time.time()
+    b = W.chunked_prefill_1m(device="cuda")
+    r = QSARunner(b)
+    torch.cuda.synchronize()
+    log(f"prefill workload ready in {time.time() - t0:.1f}s")
+    for _ in range(args.warmup):
+        r.step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        ev[k][0].record()
+        r.pool()
+        ev[k][1].record()
+        r.select()
+        ev[k][2].record()
+        r.attend()
+        ev[k][3].record()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    stage = {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps
+             for i, n in enumerate(["pool", "select", "attend"])}
+    sum_s, sum_nc = set_sizes(r)
+    n_q = r.n_q
+    attend_bytes = sum_s * TOKEN_GATHER_BYTES + n_q * (2 * Q_ROW_BYTES + 24 * 4 + r.budget * 4)
+    attend_gbs = attend_bytes / (stage["attend"] * 1e-3) / 1e9
+    index_flops = sum_nc * 1024 * (1 + 1 / 16)
+    res = dict(
+        n_q=n_q, ms_per_step=total_ms / args.steps, stages_ms=stage,
+        value=n_q / (total_ms / args.steps * 1e-3),
+        sum_set=sum_s, sum_candidates=sum_nc,
+        attend=dict(bytes=attend_bytes, gbs=attend_gbs),
+        index=dict(flops=index_flops, tflops=index_flops / (stage["select"] * 1e-3) / 1e12),
+        runner=r, batch=b)
+    return res
+
+
+def time_decode(args):
+    import torch
+    from block_sparse_long_02_amd import workloads as W
+    from block_sparse_long_02_amd.runner import QSARunner
+
+    t0 = time.time()
+    b = W.decode_128k(device="cuda")
+    r = QSARunner(b)
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")   # 512 MB > MALL
+    torch.cuda.synchronize()
+    log(f"decode workload ready in {time.time() - t0:.1f}s")
+    for _ in range(args.warmup):
+        r.step()
+    steps = []
+    for _ in range(args.steps):
+        flush.fill_(1)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record()
+        r.pool()
+        r.select()
+        e1.record()
+        r.attend()
+        e2.record()
+        steps.append((e0, e1, e2))
+    torch.cuda.synchronize()
+    sel_ms = sum(a.elapsed_time(b_) for a, b_, _ in steps) / len(steps)
+    att_ms = sum(b_.elapsed_time(c) for _, b_, c in steps) / len(steps)
+    ms = sel_ms + att_ms
+    sum_s, sum_nc = set_sizes(r)
+    n_seq = r.n_seq
+    step_bytes = sum_nc * BLOCK_KEY_BYTES + sum_s * TOKEN_GATHER_BYTES + n_seq * (
+        2 * Q_ROW_BYTES + 4 * 128 * 2 + 16)
+    return dict(value=n_seq / (ms * 1e-3), ms_per_step=ms,
+                stages_ms=dict(select=sel_ms, attend=att_ms),
+                hbm=dict(bytes=step_bytes, gbs=step_bytes / (ms * 1e-3) / 1e9),
+                runner=r, batch=b)
+
+
+def cpu_baseline(pre, budget_s):
+    """Time the CPU oracle on a bounded sample of the prefill workload."""
+    import numpy as np
+    from oracle import qsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    b, r = pre["batch"], pre["runner"]
+
+    def f64(t):
+        return t.detach().float().cpu().double().numpy()
+
+    prefix = b.meta["prefix"]
+    chunk = b.meta["chunk"]
+    # pooled prefix blocks are cache state (not timed); the chunk's new blocks are step work
+    idx_k = f64(b.idx_k[0])
+    kb_prefix = O.pool_block_keys(idx_k[:prefix], prefix // 4)
+    t0 = time.time()
+    kb_new = O.pool_block_keys(idx_k[prefix:prefix + chunk], chunk // 4)
+    t_pool = time.time() - t0
+    kbar = np.concatenate([kb_prefix, kb_new])
+    rng = np.random.default_rng(0)
+    rows = []
+    t_rows = 0.0
+    order = rng.permutation(chunk)
+    for row in order:
+        if t_rows > budget_s:
+            break
+        p = prefix + int(row)
+        t1 = time.time()
+        n_c = O.completed_blocks(p)
+        s = O.block_scores(f64(b.idx_q[row]), b.w[row].cpu().numpy(), kbar[:n_c])
+        blocks = O.select_blocks(s, b.budget)
+        tokens = O.sparse_token_set(blocks, p)
+        import torch
+        t = torch.as_tensor(tokens, device=b.k.device)
+        k_rows = f64(b.k[0][:, t, :]).transpose(1, 0, 2)
+        v_rows = f64(b.v[0][:, t, :]).transpose(1, 0, 2)
+        O.attend(f64(b.q[row]), k_rows, v_rows, tokens, p)
+        t_rows += time.time() - t1
+        rows.append(int(row))
+    per_row = t_rows / len(rows)
+    est = t_pool + per_row * chunk
+    return dict(value=chunk / est, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=(f"{len(rows)} of {chunk} query rows (random), full per-row pipeline "
+                        f"(score {1015808 // 4}+ blocks, select, expand, attend) plus pooling of "
+                        f"the chunk's {chunk // 4} new blocks; time scaled to the whole chunk"),
+                seconds=round(t_pool + t_rows, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the QSA path here is "
+              "single-GPU and has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_long_02_amd import qsa
+    qsa.lib()
+    assert torch.cuda.is_available()
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic"}
+    if args.only != "decode":
+        pre = time_prefill(args)
+        log(f"prefill: {pre['ms_per_step']:.3f} ms/step, stages {pre['stages_ms']}")
+        attend_file = os.path.join(ROOT, "block_sparse_long_02_amd", "csrc", "qsa_attend.hip")
+        out.update(value=round(pre["value"], 1), unit="tokens/s",
+                   ms_per_step=round(pre["ms_per_step"], 4))
+        out["config"] = {
+            "workload": "chunked prefill: 32768-token chunk on a 1015808-token cached prefix "
+                        "(1048576 total), batch 1, budget 512 blocks + tail",
+            "global_batch": 1, "seq_len": 1048576, "query_tokens": pre["n_q"], "budget": 512}
+        out["roofline"] = {
+            "kernel": "attend_kernel (sparse prefill attention)",
+            "bound": "hbm", "achieved": round(pre["attend"]["gbs"], 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(pre["attend"]["gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(attend_file, "attend_prefill_1m"),
+            "algorithmic_bytes_per_launch": pre["attend"]["bytes"],
+            "mean_launch_ms": round(pre["stages_ms"]["attend"], 4)}
+        out["stages_ms"] = {k: round(v, 4) for k, v in pre["stages_ms"].items()}
+        out["index_select"] = {"algorithmic_tflop": round(pre["index"]["flops"] / 1e12, 3),
+                               "tflops": round(pre["index"]["tflops"], 1),
+                               "frac_of_bf16_mfma_peak": round(pre["index"]["tflops"] / MFMA_BF16_PEAK_TFS, 4)}
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
+        del pre
+        torch.cuda.empty_cache()
+    if args.only != "prefill":
+        dec = time_decode(args)
+        log(f"decode: {dec['ms_per_step']:.4f} ms/step, stages {dec['stages_ms']}")
+        d = {"value": round(dec["value"], 1), "unit": "tokens/s",
+             "ms_per_step": round(dec["ms_per_step"], 4),
+             "config": {"workload": "decode: 32 sequences x (131072 cached + 1 new) tokens, "
+                                    "budget 512 blocks + tail, MALL flushed before each step"},
+             "roofline": {"bound": "hbm", "scope": "whole step",
+                          "achieved": round(dec["hbm"]["gbs"], 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(dec["hbm"]["gbs"] / HBM_PEAK_GBS, 4),
+                          "algorithmic_bytes": dec["hbm"]["bytes"]},
+             "stages_ms": {k: round(v, 4) for k, v in dec["stages_ms"].items()}}
+        if args.only == "decode":
+            out.update(value=d["value"], unit="tokens/s", ms_per_step=d["ms_per_step"],
+                       config=d["config"], roofline=d["roofline"])
+        else:
+            out["decode"] = d
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

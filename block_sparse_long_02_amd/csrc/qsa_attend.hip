@@ -1,0 +1,401 @@
+// Sparse attention over the QSA token set (a4 expand + tail, a5 query RoPE,
+// a6 prefill, a7 split-K decode with a combine pass).
+//
+// Method (page "Qwen3.8-Flash-Next 没有缩小模型，它重写了每个参数何时上场",
+// section "03 · Attention", CAUSAL SPARSE SET equation and fifth QSA step):
+// query i attends exactly over S_i = its selected micro-blocks expanded to
+// their 4 tokens plus the unfinished tail {4 n_c, ..., i}; 24 query heads share
+// 2 KV heads (head h reads KV head h/12); width 256, rotary on dims 0..63.
+//
+// Design (gfx950): one wave streams tiles of 8 micro-blocks (32 tokens)
+// straight from HBM into registers -- no LDS staging, since a micro-block of
+// one KV head is a single 2 KB run in both caches.  Per tile it computes
+// S^T = K Q^T with bf16 MFMA 16x16x32 (tokens as rows, the 12 heads of the
+// KV group padded to 16 as columns).  The MFMA output gives each lane the 4
+// tokens of one micro-block for one head, which is exactly the k-slice the
+// P V product needs from P, so P never leaves registers; the V cache is laid
+// out [block][dim][4 tokens] so the matching V operand is one 8-byte run per
+// (block, dim).  Online softmax in float32 (base-2 exponent), output
+// accumulators in float32.
+#include <math.h>
+
+#include "qsa_common.hpp"
+
+namespace qsa {
+
+constexpr int kTileMB = 8;                    // micro-blocks per tile
+constexpr int kWaves = 4;
+constexpr int kMaxList = kMaxBudget + 1;      // selected blocks + tail block
+constexpr int kPartFloats = kGroup * kHeadDim + 2 * 16;  // O[12][256], m[16], l[16]
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Largest s with cu_q[s] <= row.
+__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu_q, int n_seq, int row) {
+  int lo = 0, hi = n_seq - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
+  uint32_t w = v[e >> 1];
+  return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+struct AttnShared {
+  int list[kMaxList + 8];            // micro-block ids, tail block last
+  float cs[kRopeDim / 2][2];         // cos, sin of the query position
+  float m[kWaves][16];
+  float l[kWaves][16];
+  float o[kWaves][kGroup][kHeadDim];
+};
+
+// mode kFinal: one workgroup per (row, KV head) writes out / lse.
+// otherwise: n_splits workgroups per (row, KV head) write partials.
+template <bool kFinal>
+__global__ void __launch_bounds__(256, 2)
+attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
+              const int32_t* __restrict__ seq_len, int n_seq, int n_rows,
+              const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+              int64_t seq_stride, int64_t head_stride,
+              const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int budget,
+              int n_splits, uint16_t* __restrict__ out, float* __restrict__ lse,
+              float* __restrict__ part) {
+  __shared__ AttnShared sh;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+
+  const int wg = blockIdx.x;
+  const int split = wg % n_splits;
+  const int g = (wg / n_splits) & 1;
+  const int row = wg / (2 * n_splits);
+  if (row >= n_rows) return;
+
+  // ---- which sequence / position, and is the selection usable?
+  const int s = find_seq(cu_q, n_seq, row);
+  const int q_begin = cu_q[s], q_end = cu_q[s + 1];
+  const int L = seq_len[s];
+  const int pos = L - (q_end - q_begin) + (row - q_begin);
+  const int n_c = (pos + 1) >> 2;
+  const int tail_len = (pos + 1) & 3;
+  const int cnt = sel_count[row];
+  const bool bad = row >= q_end || pos < 0 || cnt < 0 || cnt > budget || cnt > n_c ||
+                   (cnt < min(budget, n_c));
+  if (bad) {
+    if (kFinal) {
+      for (int i = threadIdx.x; i < kGroup * kHeadDim; i += 256)
+        out[((int64_t)row * kQHeads + g * kGroup) * kHeadDim + i] = 0x7FC0;  // NaN
+      if (lse && threadIdx.x < kGroup) lse[(int64_t)row * kQHeads + g * kGroup + threadIdx.x] = __int_as_float(0x7FC00000);
+    } else {
+      float* pp = part + ((int64_t)(row * 2 + g) * n_splits + split) * kPartFloats;
+      for (int i = threadIdx.x; i < kPartFloats; i += 256) pp[i] = __int_as_float(0x7FC00000);
+    }
+    return;
+  }
+  const int n_mb = cnt + (tail_len > 0 ? 1 : 0);
+
+  // ---- block list and the query's rotary angles into LDS
+  for (int i = threadIdx.x; i < cnt; i += 256) {
+    int id = sel[(int64_t)row * budget + i];
+    sh.list[i] = min(max(id, 0), n_c - 1);   // ids come ascending from the selection
+  }
+  if (threadIdx.x == 0 && tail_len > 0) sh.list[cnt] = n_c;
+  if (threadIdx.x < kRopeDim / 2) {
+    double sd, cd;
+    sincos((double)pos * rope_inv_freq(threadIdx.x), &sd, &cd);
+    sh.cs[threadIdx.x][0] = (float)cd;
+    sh.cs[threadIdx.x][1] = (float)sd;
+  }
+  __syncthreads();
+
+  // ---- query fragment: B operand of S^T = K Q^T.  Lane holds head `col` of
+  // this KV group, dims 32*ks + 8*grp .. +7.  Heads 12..15 are zero padding.
+  u32x4 qf[8];
+  // heads 12..15 of the tile are padding: their address is clamped to a real
+  // head and the value replaced by zero
+  const int head = g * kGroup + min(col, kGroup - 1);
+  const uint16_t* qrow = q + ((int64_t)row * kQHeads + head) * kHeadDim + 8 * grp;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const u32x4 v = ldg16(qrow + 32 * ks);
+    qf[ks] = col < kGroup ? v : u32x4{0, 0, 0, 0};
+  }
+  {
+    // rotate-half on dims 0..63: pair j = 8*grp + e sits in qf[0] (x1) and qf[1] (x2)
+    u32x4 r0, r1;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float y1[2], y2[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int e = 2 * w + h2, j = 8 * grp + e;
+        const float c = sh.cs[j][0], sn = sh.cs[j][1];
+        const float x1 = bf16_elem(qf[0], e), x2 = bf16_elem(qf[1], e);
+        y1[h2] = x1 * c - x2 * sn;
+        y2[h2] = x2 * c + x1 * sn;
+      }
+      r0[w] = pack_bf16x2(y1[0], y1[1]);
+      r1[w] = pack_bf16x2(y2[0], y2[1]);
+    }
+    if (col < kGroup) { qf[0] = r0; qf[1] = r1; }
+  }
+
+  // ---- this wave's tiles
+  const int n_tiles = (n_mb + kTileMB - 1) / kTileMB;
+  const int parts = n_splits * kWaves;
+  const int my_part = split * kWaves + wave;
+  const int per = (n_tiles + parts - 1) / parts;
+  const int t_begin = my_part * per;
+  const int t_end = min(n_tiles, t_begin + per);
+  const int tail_slot = tail_len > 0 ? cnt : -1;
+
+  const uint16_t* kbase = kc + (int64_t)s * seq_stride + (int64_t)g * head_stride;
+  const uint16_t* vbase = vc + (int64_t)s * seq_stride + (int64_t)g * head_stride;
+  const float scale = kLog2e / 16.0f;
+
+  f32x4 o[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int base = t * kTileMB;
+    // K rows: lane is token row `col` of each 16-token half
+    const int sk0 = base + (col >> 2), sk1 = base + 4 + (col >> 2);
+    const int idk0 = sh.list[min(sk0, n_mb - 1)], idk1 = sh.list[min(sk1, n_mb - 1)];
+    // V / P k-slices: micro-blocks base+grp and base+4+grp
+    const int sv0 = base + grp, sv1 = base + 4 + grp;
+    const int idv0 = sh.list[min(sv0, n_mb - 1)], idv1 = sh.list[min(sv1, n_mb - 1)];
+
+    const uint16_t* kp0 = kbase + ((int64_t)idk0 * kBlock + (col & 3)) * kHeadDim + 8 * grp;
+    const uint16_t* kp1 = kbase + ((int64_t)idk1 * kBlock + (col & 3)) * kHeadDim + 8 * grp;
+    const uint16_t* vp0 = vbase + (int64_t)idv0 * (kBlock * kHeadDim) + 8 * col;
+    const uint16_t* vp1 = vbase + (int64_t)idv1 * (kBlock * kHeadDim) + 8 * col;
+    u32x4 ka[8], kb[8], va[8], vb[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) { ka[ks] = ldg16(kp0 + 32 * ks); kb[ks] = ldg16(kp1 + 32 * ks); }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) { va[c] = ldg16(vp0 + 128 * c); vb[c] = ldg16(vp1 + 128 * c); }
+
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s0 = mfma_16x16x32(ka[ks], qf[ks], s0);
+      s1 = mfma_16x16x32(kb[ks], qf[ks], s1);
+    }
+    // s0[i]: token i of micro-block slot sv0, head col; s1[i]: slot sv1.
+    const bool v0 = sv0 < n_mb, v1 = sv1 < n_mb;
+    {
+      // Cache rows past the query inside the tail block (and padding slots)
+      // may hold anything: zero their V so that p = 0 cannot meet a NaN.
+      const int n0 = !v0 ? 0 : (sv0 == tail_slot ? tail_len : 4);
+      const int n1 = !v1 ? 0 : (sv1 == tail_slot ? tail_len : 4);
+      const uint32_t a01 = (n0 > 0 ? 0xFFFFu : 0u) | (n0 > 1 ? 0xFFFF0000u : 0u);
+      const uint32_t a23 = (n0 > 2 ? 0xFFFFu : 0u) | (n0 > 3 ? 0xFFFF0000u : 0u);
+      const uint32_t b01 = (n1 > 0 ? 0xFFFFu : 0u) | (n1 > 1 ? 0xFFFF0000u : 0u);
+      const uint32_t b23 = (n1 > 2 ? 0xFFFFu : 0u) | (n1 > 3 ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        va[c][0] &= a01; va[c][1] &= a23; va[c][2] &= a01; va[c][3] &= a23;
+        vb[c][0] &= b01; vb[c][1] &= b23; vb[c][2] &= b01; vb[c][3] &= b23;
+      }
+    }
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok0 = v0 && (sv0 != tail_slot || i < tail_len);
+      const bool ok1 = v1 && (sv1 != tail_slot || i < tail_len);
+      x[i] = ok0 ? s0[i] * scale : -INFINITY;
+      x[4 + i] = ok1 ? s1[i] * scale : -INFINITY;
+    }
+    float mt = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = exp2f(m_run - m_new);   // 0 on the first tile
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { p[i] = exp2f(x[i] - m_new); ps += p[i]; }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+
+    // output rows are heads 4*grp + i: fetch their rescale factors
+    float a_row[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a_row[i] = __shfl(alpha, 4 * grp + i, 64);
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[n][i] *= a_row[i];
+    }
+
+    u32x4 pa;
+    pa[0] = pack_bf16x2(p[0], p[1]);
+    pa[1] = pack_bf16x2(p[2], p[3]);
+    pa[2] = pack_bf16x2(p[4], p[5]);
+    pa[3] = pack_bf16x2(p[6], p[7]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      // dims 32c + 2*col (even tile) and 32c + 2*col + 1 (odd tile)
+      u32x4 be = {va[c][0], va[c][1], vb[c][0], vb[c][1]};
+      u32x4 bo = {va[c][2], va[c][3], vb[c][2], vb[c][3]};
+      o[2 * c] = mfma_16x16x32(pa, be, o[2 * c]);
+      o[2 * c + 1] = mfma_16x16x32(pa, bo, o[2 * c + 1]);
+    }
+  }
+
+  // ---- merge the 4 waves in LDS
+  if (grp == 0) { sh.m[wave][col] = m_run; sh.l[wave][col] = l_run; }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hr = 4 * grp + i;
+    if (hr < kGroup) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        sh.o[wave][hr][32 * c + 2 * col] = o[2 * c][i];
+        sh.o[wave][hr][32 * c + 2 * col + 1] = o[2 * c + 1][i];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int d = threadIdx.x;   // one output dim per thread
+  float* pp = kFinal ? nullptr : part + ((int64_t)(row * 2 + g) * n_splits + split) * kPartFloats;
+  for (int h = 0; h < kGroup; ++h) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, sh.m[w][h]);
+    float lsum = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = sh.l[w][h] > 0.f ? exp2f(sh.m[w][h] - mx) : 0.f;
+      lsum += sh.l[w][h] * f;
+      acc += sh.o[w][h][d] * f;
+    }
+    if (kFinal) {
+      out[((int64_t)row * kQHeads + g * kGroup + h) * kHeadDim + d] =
+          (uint16_t)f32_to_bf16_bits(acc / lsum);
+      if (lse && d == 0) lse[(int64_t)row * kQHeads + g * kGroup + h] = (mx + log2f(lsum)) * kLn2;
+    } else {
+      pp[h * kHeadDim + d] = acc;
+      if (d == 0) { pp[kGroup * kHeadDim + h] = mx; pp[kGroup * kHeadDim + 16 + h] = lsum; }
+    }
+  }
+}
+
+// c[i] = i for i = 0..n (the row offsets of a one-query-per-sequence batch).
+__global__ void iota_kernel(int32_t* __restrict__ c, int32_t n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i <= n) c[i] = i;
+}
+
+// Combine the n_splits partials of every (row, KV head): one workgroup per
+// (row, KV head), one output dim per thread.
+__global__ void __launch_bounds__(256)
+combine_kernel(const float* __restrict__ part, int n_splits, int n_rows,
+               uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int row = blockIdx.x >> 1, g = blockIdx.x & 1;
+  if (row >= n_rows) return;
+  const int d = threadIdx.x;
+  const float* base = part + (int64_t)(row * 2 + g) * n_splits * kPartFloats;
+  for (int h = 0; h < kGroup; ++h) {
+    float mx = -INFINITY;
+    for (int sp = 0; sp < n_splits; ++sp) mx = fmaxf(mx, base[sp * kPartFloats + kGroup * kHeadDim + h]);
+    float lsum = 0.f, acc = 0.f;
+    for (int sp = 0; sp < n_splits; ++sp) {
+      const float* pp = base + sp * kPartFloats;
+      const float l = pp[kGroup * kHeadDim + 16 + h];
+      const float f = l > 0.f ? exp2f(pp[kGroup * kHeadDim + h] - mx) : 0.f;
+      lsum += l * f;
+      acc += pp[h * kHeadDim + d] * f;
+    }
+    out[((int64_t)row * kQHeads + g * kGroup + h) * kHeadDim + d] = (uint16_t)f32_to_bf16_bits(acc / lsum);
+    if (lse && d == 0) lse[(int64_t)row * kQHeads + g * kGroup + h] = (mx + log2f(lsum)) * kLn2;
+  }
+}
+
+}  // namespace qsa
+
+namespace {
+
+constexpr int kDecodeSplits = 8;
+
+int check_attend_common(const void* q, const void* k_cache, const void* v_cache,
+                        int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
+                        const int32_t* sel_count, int32_t budget, const void* out) {
+  using namespace qsa_host;
+  if (!q || !k_cache || !v_cache || !sel || !sel_count || !out) return QSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return QSA_ERR_INVALID_ARG;
+  if (!stride_ok(kv_seq_stride) || !stride_ok(kv_head_stride)) return QSA_ERR_INVALID_ARG;
+  if (budget < 1 || budget > QSA_MAX_BUDGET) return QSA_ERR_INVALID_ARG;
+  return QSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_len, int32_t n_seq,
+                       int32_t n_q, int32_t max_q_len, const void* k_cache, const void* v_cache,
+                       int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
+                       const int32_t* sel_count, int32_t budget, void* out, float* lse,
+                       void* stream) {
+  if (n_q < 0 || n_seq < 0 || max_q_len < 0) return QSA_ERR_INVALID_ARG;
+  if (n_q == 0) return QSA_OK;
+  if (n_seq == 0 || !cu_q || !seq_len) return QSA_ERR_INVALID_ARG;
+  int st = check_attend_common(q, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
+                               budget, out);
+  if (st != QSA_OK) return st;
+  if ((int64_t)n_q * 2 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(qsa::attend_kernel<true>, dim3(n_q * 2), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t*)q, cu_q, seq_len, n_seq, n_q, (const uint16_t*)k_cache,
+                     (const uint16_t*)v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
+                     budget, 1, (uint16_t*)out, lse, (float*)nullptr);
+  return qsa_host::launch_status();
+}
+
+size_t qsa_attend_decode_workspace(int32_t n_seq) {
+  if (n_seq <= 0) return 0;
+  return (size_t)n_seq * 2 * kDecodeSplits * qsa::kPartFloats * sizeof(float) +
+         (size_t)(n_seq + 1) * sizeof(int32_t) + 256;
+}
+
+int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq, const void* k_cache,
+                      const void* v_cache, int64_t kv_seq_stride, int64_t kv_head_stride,
+                      const int32_t* sel, const int32_t* sel_count, int32_t budget, void* out,
+                      float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  using namespace qsa_host;
+  if (n_seq < 0) return QSA_ERR_INVALID_ARG;
+  if (n_seq == 0) return QSA_OK;
+  if (!seq_len) return QSA_ERR_INVALID_ARG;
+  int st = check_attend_common(q, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
+                               budget, out);
+  if (st != QSA_OK) return st;
+  if (!workspace || !aligned16(workspace)) return QSA_ERR_INVALID_ARG;
+  if (ws_bytes < qsa_attend_decode_workspace(n_seq)) return QSA_ERR_WORKSPACE_TOO_SMALL;
+  if ((int64_t)n_seq * 2 * kDecodeSplits > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  float* part = (float*)workspace;
+  // one query per sequence: cu_q = 0, 1, ..., n_seq, written by a tiny kernel
+  int32_t* cu = (int32_t*)((char*)workspace +
+                           (size_t)n_seq * 2 * kDecodeSplits * qsa::kPartFloats * sizeof(float));
+  hipLaunchKernelGGL(qsa::iota_kernel, dim3((n_seq + 256) / 256), dim3(256), 0,
+                     (hipStream_t)stream, cu, n_seq);
+  hipLaunchKernelGGL(qsa::attend_kernel<false>, dim3(n_seq * 2 * kDecodeSplits), dim3(256), 0,
+                     (hipStream_t)stream, (const uint16_t*)q, (const int32_t*)cu, seq_len, n_seq,
+                     n_seq, (const uint16_t*)k_cache, (const uint16_t*)v_cache, kv_seq_stride,
+                     kv_head_stride, sel, sel_count, budget, kDecodeSplits, (uint16_t*)nullptr,
+                     (float*)nullptr, part);
+  hipLaunchKernelGGL(qsa::combine_kernel, dim3(n_seq * 2), dim3(256), 0, (hipStream_t)stream,
+                     (const float*)part, kDecodeSplits, n_seq, (uint16_t*)out, lse);
+  return launch_status();
+}
+
+}  // extern "C"

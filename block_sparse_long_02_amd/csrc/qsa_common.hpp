@@ -1,0 +1,96 @@
+// Shared device and host helpers for the QSA kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qsa.h"
+
+namespace qsa {
+
+// ----------------------------------------------------------------- types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = QSA_BLOCK;
+constexpr int kIdxHeads = QSA_IDX_HEADS;
+constexpr int kIdxDim = QSA_IDX_DIM;
+constexpr int kQHeads = QSA_Q_HEADS;
+constexpr int kKVHeads = QSA_KV_HEADS;
+constexpr int kGroup = kQHeads / kKVHeads;  // 12 query heads per KV head
+constexpr int kHeadDim = QSA_HEAD_DIM;
+constexpr int kRopeDim = QSA_ROPE_DIM;
+constexpr int kMaxBudget = QSA_MAX_BUDGET;
+
+// -------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even float32 -> bf16 bits (inputs finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ------------------------------------------------------------------- MFMA
+// D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16).  Lane l supplies
+// A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16]; it receives
+// D[4*(l/16) + i][l%16] for i = 0..3.
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Rotary inverse frequency 1e7^(-j/32) of rotation pair j (float64).
+__device__ __forceinline__ double rope_inv_freq(int j) {
+  return pow(1.0e7, -(double)j / (double)(kRopeDim / 2));
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
+
+// --------------------------------------------------------- block helpers
+// Exclusive prefix sum over a 256-thread workgroup.  `tmp` holds >= 4 ints of
+// LDS.  Returns the exclusive prefix of `v`; `total` receives the sum.
+__device__ __forceinline__ int block_excl_scan_256(int v, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    int t = tmp[w];
+    if (w < wave) base += t;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
+}  // namespace qsa
+
+// ------------------------------------------------------------ host helpers
+namespace qsa_host {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool stride_ok(int64_t s) { return s >= 0 && (s % 8) == 0; }
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH_FAILED;
+}
+
+}  // namespace qsa_host

@@ -1,0 +1,84 @@
+"""One QSA layer's device state and the ABI calls of a prefill or decode step.
+
+The runner owns the caches and output buffers of one batch (torch device
+memory) and issues, per step, exactly the libqsa calls of the hot path:
+pool the newly completed blocks, select blocks for every query, attend.
+It does no arithmetic of its own.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import qsa
+from .workloads import QSABatch, R, v_cache_layout
+
+
+class QSARunner:
+    def __init__(self, batch: QSABatch, decode: bool | None = None):
+        b = batch
+        assert b.idx_q.is_cuda, "batch must live on the GPU"
+        self.b = b
+        self.decode = (b.meta.get("kind") == "decode") if decode is None else decode
+        dev = b.idx_q.device
+        lens = b.seq_lens_host()
+        cu = b.cu_q_host()
+        self.n_seq, self.n_q = b.n_seq, b.n_q
+        self.max_q_len = b.max_q_len()
+        self.max_blocks = b.max_blocks()
+        self.budget = b.budget
+        cap = b.l_cap
+
+        # caches: K rotated once at its positions (cache-write time), V re-laid out
+        self.k_cache = b.k.clone()
+        for s in range(self.n_seq):
+            qsa.rope_apply(self.k_cache[s], row_stride=256, head_stride=cap * 256, n_heads=2,
+                           n_rows=lens[s], pos0=0)
+        self.v_cache = v_cache_layout(b.v)
+        self.block_keys = torch.zeros((self.n_seq, cap // R, 128), dtype=torch.bfloat16, device=dev)
+
+        # blocks already in the cache before this step, and the ones the step completes
+        before = [(lens[s] - (cu[s + 1] - cu[s])) // R for s in range(self.n_seq)]
+        after = [lens[s] // R for s in range(self.n_seq)]
+        zero = torch.zeros(self.n_seq, dtype=torch.int32, device=dev)
+        t_before = torch.tensor(before, dtype=torch.int32, device=dev)
+        if max(before) > 0:
+            qsa.pool_block_keys(b.idx_k, self.block_keys, zero, t_before, max(before))
+        self.pool_begin = t_before
+        self.pool_end = torch.tensor(after, dtype=torch.int32, device=dev)
+        self.pool_span = max(a - c for a, c in zip(after, before))
+
+        self.sel = torch.empty((self.n_q, self.budget), dtype=torch.int32, device=dev)
+        self.sel_count = torch.empty((self.n_q,), dtype=torch.int32, device=dev)
+        self.out = torch.empty((self.n_q, 24, 256), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((self.n_q, 24), dtype=torch.float32, device=dev)
+        ws = qsa.index_select_workspace(self.n_q, self.max_blocks)
+        self.ws_index = torch.empty((max(ws, 16),), dtype=torch.uint8, device=dev)
+        wsd = qsa.attend_decode_workspace(self.n_seq) if self.decode else 16
+        self.ws_decode = torch.empty((max(wsd, 16),), dtype=torch.uint8, device=dev)
+
+    # the three calls of a step ------------------------------------------
+    def pool(self, stream=None):
+        if self.pool_span > 0:
+            qsa.pool_block_keys(self.b.idx_k, self.block_keys, self.pool_begin, self.pool_end,
+                                self.pool_span, stream=stream)
+
+    def select(self, stream=None):
+        b = self.b
+        qsa.index_select(b.idx_q, b.w, b.cu_q, b.seq_len, self.max_q_len, self.max_blocks,
+                         self.block_keys, self.budget, self.sel, self.sel_count, self.ws_index,
+                         stream=stream)
+
+    def attend(self, stream=None):
+        b = self.b
+        if self.decode:
+            qsa.attend_decode(b.q, b.seq_len, self.k_cache, self.v_cache, self.sel, self.sel_count,
+                              self.budget, self.out, self.lse, self.ws_decode, stream=stream)
+        else:
+            qsa.attend_prefill(b.q, b.cu_q, b.seq_len, self.max_q_len, self.k_cache, self.v_cache,
+                               self.sel, self.sel_count, self.budget, self.out, self.lse,
+                               stream=stream)
+
+    def step(self, stream=None):
+        self.pool(stream)
+        self.select(stream)
+        self.attend(stream)

@@ -101,6 +101,12 @@ class QSABatch:
     def max_blocks(self) -> int:
         return max(self.seq_lens_host()) // R
 
+    def to(self, device) -> "QSABatch":
+        """Copy every tensor to `device` (same values)."""
+        names = ["seq_len", "cu_q", "idx_q", "w", "idx_k", "q", "k", "v"]
+        kw = {n: getattr(self, n).to(device) for n in names}
+        return QSABatch(budget=self.budget, planted=self.planted, meta=dict(self.meta), **kw)
+
 
 def _cap(n_tokens: int) -> int:
     """Cache capacity in tokens: whole micro-blocks, at least one."""
@@ -335,3 +341,11 @@ def ragged_decode(device="cpu", seed=1004, n_seq=8, lo=4096, hi=1048572, exact_g
     ties = [bool(x) for x in torch.randperm(n_seq, generator=g).lt(n_seq // 2).tolist()]
     return make_decode(seq_lens=lens, budget=512, n_plant=32, seed=seed, device=device,
                        near_tie=ties, exact_grid=exact_grid)
+
+
+def v_cache_layout(v: torch.Tensor) -> torch.Tensor:
+    """[n_seq][2][cap][256] token-major values -> [n_seq][2][cap/4][256][4]
+    (micro-block-major, dim-major inside a block), the layout libqsa reads."""
+    n_seq, h, cap, d = v.shape
+    assert cap % R == 0
+    return v.reshape(n_seq, h, cap // R, R, d).transpose(-1, -2).contiguous()

@@ -192,7 +192,7 @@ def rope(x: np.ndarray, pos) -> np.ndarray:
     return y
 
 
-def attend(q_i: np.ndarray, k_raw: np.ndarray, v: np.ndarray, tokens: np.ndarray,
+def attend(q_i: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, tokens: np.ndarray,
            i: int):
     """Exact GQA softmax attention of query i over the token set S_i.
 
@@ -200,14 +200,16 @@ def attend(q_i: np.ndarray, k_raw: np.ndarray, v: np.ndarray, tokens: np.ndarray
     the original tokens of S_i.  Q and K are rotated at their own positions;
     logits are scaled by 1/16; head h reads KV head floor(h/12).
 
-    q_i: [24][256] raw query; k_raw, v: [L][2][256] raw cache rows (K not
-    rotated).  Returns (O [24][256], lse [24]) in float64, lse = log sum exp of
-    the scaled logits.
+    q_i: [24][256] raw query; tokens: the positions of S_i; k_rows, v_rows:
+    [len(tokens)][2][256] the raw cache rows of those tokens (K not rotated).
+    Returns (O [24][256], lse [24]) in float64, lse = log sum exp of the
+    scaled logits.
     """
     S = np.asarray(tokens, dtype=np.int64)
     qr = rope(np.asarray(q_i, dtype=np.float64), i)
-    kr = rope(np.asarray(k_raw, dtype=np.float64)[S], S[:, None])   # [n][2][256]
-    vs = np.asarray(v, dtype=np.float64)[S]                         # [n][2][256]
+    kr = rope(np.asarray(k_rows, dtype=np.float64), S[:, None])     # [n][2][256]
+    vs = np.asarray(v_rows, dtype=np.float64)                       # [n][2][256]
+    assert kr.shape[0] == S.shape[0] and vs.shape[0] == S.shape[0]
     out = np.empty((H_Q, D), dtype=np.float64)
     lse = np.empty(H_Q, dtype=np.float64)
     for h in range(H_Q):
@@ -234,7 +236,7 @@ def qsa_query(idx_q_i, w_i, kbar, q_i, k_raw, v, i: int, budget: int):
     s = block_scores(idx_q_i, w_i, np.asarray(kbar)[:n_c])
     blocks = select_blocks(s, budget)
     tokens = sparse_token_set(blocks, i)
-    out, lse = attend(q_i, k_raw, v, tokens, i)
+    out, lse = attend(q_i, np.asarray(k_raw)[tokens], np.asarray(v)[tokens], tokens, i)
     return blocks, out, lse
 
 

@@ -1,0 +1,102 @@
+"""Helpers shared by the parity tests: feed a generated batch to the oracle
+and compare the HIP path's results with it.  Only tests import this."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import qsa_oracle as O
+
+# attention tolerance (bf16 in/out, float32 accumulation)
+MAX_ABS = 1e-2
+REL_L2 = 5e-3
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+class OracleView:
+    """Oracle-side view of one QSABatch (float64 arrays, per sequence)."""
+
+    def __init__(self, b):
+        self.b = b
+        self.lens = b.seq_lens_host()
+        self.cu = b.cu_q_host()
+        self.pos = b.q_pos_host()
+        self.seq = b.q_seq_host()
+        self._kb = {}
+
+    def kbar(self, s):
+        if s not in self._kb:
+            self._kb[s] = O.pool_block_keys(np64(self.b.idx_k[s]), self.lens[s] // O.R)
+        return self._kb[s]
+
+    def rows(self, s, tokens):
+        """Raw K and V rows [n][2][256] of the listed tokens of sequence s."""
+        t = torch.as_tensor(np.asarray(tokens), dtype=torch.long, device=self.b.k.device)
+        k = np64(self.b.k[s][:, t, :]).transpose(1, 0, 2)
+        v = np64(self.b.v[s][:, t, :]).transpose(1, 0, 2)
+        return k, v
+
+    def scores(self, row):
+        s, p = self.seq[row], self.pos[row]
+        n_c = O.completed_blocks(p)
+        return O.block_scores(np64(self.b.idx_q[row]), self.b.w[row].cpu().numpy(),
+                              self.kbar(s)[:n_c])
+
+    def select(self, row):
+        return O.select_blocks(self.scores(row), self.b.budget)
+
+    def attend(self, row, blocks):
+        s, p = self.seq[row], self.pos[row]
+        tokens = O.sparse_token_set(np.asarray(blocks, dtype=np.int64), p)
+        k, v = self.rows(s, tokens)
+        return O.attend(np64(self.b.q[row]), k, v, tokens, p)
+
+    def dense(self, row):
+        """Textbook causal GQA over every token 0..pos (for budget >= n_c)."""
+        s, p = self.seq[row], self.pos[row]
+        k, v = self.rows(s, np.arange(p + 1))
+        return O.dense_causal_gqa(np64(self.b.q[row]), k, v, p)
+
+
+def check_selection(view: OracleView, row: int, gpu_ids, gpu_count: int, exact: bool = False):
+    """Rule for float32 selections: bit-exact when the oracle's boundary gap
+    exceeds the rounding allowance delta (always, for exact-grid inputs);
+    otherwise every choice must lie within delta of the boundary score.
+    Returns 'exact' or 'near'."""
+    b = view.b
+    s, p = view.seq[row], view.pos[row]
+    n_c = O.completed_blocks(p)
+    k_eff = min(b.budget, n_c)
+    assert gpu_count == k_eff, (row, gpu_count, k_eff)
+    ids = np.asarray(gpu_ids[:gpu_count], dtype=np.int64)
+    assert np.all(np.asarray(gpu_ids[gpu_count:]) == -1), row
+    assert np.all(np.diff(ids) > 0), ("not strictly ascending", row)
+    assert k_eff == 0 or (ids[0] >= 0 and ids[-1] < n_c), row
+    sc = view.scores(row)
+    want = O.select_blocks(sc, b.budget)
+    gap, delta, s_k = O.selection_gap(sc, np64(b.idx_q[row]), b.w[row].cpu().numpy(),
+                                      view.kbar(s)[:n_c], b.budget)
+    if exact or gap > delta:
+        assert np.array_equal(ids, want), (row, np.setdiff1d(ids, want)[:8], np.setdiff1d(want, ids)[:8])
+        return "exact"
+    chosen = np.zeros(n_c, bool)
+    chosen[ids] = True
+    assert np.all(sc[chosen] >= s_k - delta), row
+    assert np.all(sc[~chosen] <= s_k + delta), row
+    return "near"
+
+
+def check_attention(gpu_out, gpu_lse, ref_out, ref_lse, label=""):
+    """Max-abs and relative-L2 bounds on one row's [24][256] output."""
+    o = np64(gpu_out)
+    err = np.abs(o - ref_out)
+    assert np.isfinite(o).all(), label
+    assert err.max() <= MAX_ABS, (label, err.max())
+    rel = np.linalg.norm(o - ref_out) / np.linalg.norm(ref_out)
+    assert rel <= REL_L2, (label, rel)
+    if gpu_lse is not None:
+        assert np.abs(np64(gpu_lse) - ref_lse).max() <= 1e-2, label
+    return err.max(), rel

@@ -1,0 +1,98 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call
+(so no GPU is needed).  Pointer arguments here are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_long_02_amd import qsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+ALIGNED = 0x100000       # fake, 16-byte aligned device addresses (never touched)
+MISALIGNED = 0x100002
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qsa.LIB_PATH):
+        pytest.fail("libqsa.so is not built (run __graft_entry__.build())")
+    return qsa.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in qsa.SIGNATURES, n
+
+
+def test_status_strings_and_version(L):
+    for code, name in qsa.STATUS.items():
+        assert qsa.status_string(code) == name
+    assert qsa.status_string(99) == "QSA_ERR_UNKNOWN"
+    assert qsa.abi_version() == 1
+
+
+def test_workspace_queries(L):
+    assert L.qsa_index_select_workspace(0, 100) == 0
+    small = L.qsa_index_select_workspace(10, 1000)
+    big = L.qsa_index_select_workspace(10, 1 << 18)
+    assert small > 10 * 4096 * 8 and big > small       # candidate lists, then samples
+    assert L.qsa_attend_decode_workspace(0) == 0
+    assert L.qsa_attend_decode_workspace(32) >= 32 * 2 * 12 * 256 * 4
+
+
+def _select(L, **kw):
+    a = dict(idx_q=ALIGNED, w=ALIGNED, cu_q=ALIGNED, seq_len=ALIGNED, n_seq=1, n_q=4, max_q_len=4,
+             max_blocks=100, bk=ALIGNED, bk_stride=128 * 100, budget=16, sel=ALIGNED,
+             cnt=ALIGNED, ws=ALIGNED, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.qsa_index_select(a["idx_q"], a["w"], a["cu_q"], a["seq_len"], a["n_seq"], a["n_q"],
+                              a["max_q_len"], a["max_blocks"], a["bk"], a["bk_stride"],
+                              a["budget"], a["sel"], a["cnt"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_index_select_rejects_bad_arguments(L):
+    assert _select(L, budget=0) == 1
+    assert _select(L, budget=513) == 1
+    assert _select(L, idx_q=None) == 1
+    assert _select(L, w=MISALIGNED) == 1
+    assert _select(L, bk_stride=12) == 1
+    assert _select(L, n_q=-1) == 1
+    assert _select(L, max_q_len=0) == 1
+    assert _select(L, max_blocks=(1 << 20) + 1) == 2
+    assert _select(L, ws_bytes=1024) == 3
+    assert _select(L, n_q=0) == 0          # nothing to do: no HIP call either
+
+
+def test_attention_and_pool_reject_bad_arguments(L):
+    A = ALIGNED
+    # prefill: budget, alignment, null
+    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 0, A, None, None) == 1
+    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, MISALIGNED, 1024, 512, A, A, 16, A, None, None) == 1
+    assert L.qsa_attend_prefill(A, None, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, None) == 1
+    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1020, 512, A, A, 16, A, None, None) == 1
+    assert L.qsa_attend_prefill(A, A, A, 1, 0, 4, A, A, 1024, 512, A, A, 16, A, None, None) == 0
+    # decode: workspace too small, bad budget
+    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 100, None) == 3
+    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 600, A, A, A, 1 << 30, None) == 1
+    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, MISALIGNED, 1 << 30, None) == 1
+    # pooling and rope
+    assert L.qsa_pool_block_keys(None, 128, A, 128, A, A, 1, 4, None) == 1
+    assert L.qsa_pool_block_keys(A, 129, A, 128, A, A, 1, 4, None) == 1
+    assert L.qsa_pool_block_keys(A, 128, A, 128, A, A, 0, 4, None) == 0
+    assert L.qsa_pool_block_keys(A, 128, A, 128, A, A, -1, 4, None) == 1
+    assert L.qsa_rope_apply(MISALIGNED, 256, 256, 2, None, 0, 10, None) == 1
+    assert L.qsa_rope_apply(A, 256, 256, 2, None, 0, 0, None) == 0
+    assert L.qsa_rope_apply(A, 256, 256, 2, None, (1 << 22), 10, None) == 2

@@ -1,0 +1,284 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Selections: bit-exact for exact-grid inputs and whenever the oracle's
+boundary gap exceeds the float32 rounding allowance, otherwise within it.
+Attention: max-abs 1e-2 and relative L2 5e-3 per query row (bf16 in/out,
+float32 accumulation).  Pooling: bit-exact.  RoPE helper: within one bf16 ulp.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_02_amd import qsa
+from block_sparse_long_02_amd import workloads as W
+from block_sparse_long_02_amd.runner import QSARunner
+from oracle import qsa_oracle as O
+from tests._harness import OracleView, check_attention, check_selection, np64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qsa.lib()   # the native library must load
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy()
+
+
+# ------------------------------------------------------------------ pooling
+
+def test_pool_bit_exact_and_bounded():
+    g = torch.Generator().manual_seed(0)
+    n_seq, cap = 3, 1024
+    idx_k = torch.randn(n_seq, cap, 128, generator=g).to(torch.bfloat16)
+    idx_k[1, :8] = torch.tensor([16777216.0, 1.0, -16777216.0, 1.0] * 2).to(torch.bfloat16)[:, None]
+    begin, end = [0, 0, 100], [256, 77, 101]
+    sentinel = torch.full((n_seq, cap // 4, 128), 0x1234, dtype=torch.int16)
+    for max_span in (256, 16):            # 16: fewer workgroups than blocks
+        bk = sentinel.clone().cuda().view(torch.bfloat16)
+        qsa.pool_block_keys(idx_k.cuda(), bk, torch.tensor(begin, dtype=torch.int32).cuda(),
+                            torch.tensor(end, dtype=torch.int32).cuda(), max_span)
+        _sync()
+        got = _bits(bk)
+        for s in range(n_seq):
+            ref = torch.tensor(O.pool_block_keys(np64(idx_k[s]), end[s]), dtype=torch.float32)
+            ref_bits = ref.to(torch.bfloat16).view(torch.int16).numpy()
+            assert np.array_equal(got[s, begin[s]:end[s]], ref_bits[begin[s]:end[s]]), (s, max_span)
+            assert np.all(got[s, :begin[s]] == 0x1234) and np.all(got[s, end[s]:] == 0x1234)
+    # the order-of-addition case: 2^24 + 1 - 2^24 + 1 pools to 0.25
+    assert float(bk[1, 0, 0].float()) == 0.25
+
+
+# --------------------------------------------------------------------- RoPE
+
+def _ordered(bits):
+    """bf16 bit patterns (int16) -> integers in the order of the values (+0 == -0)."""
+    b = bits.astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b < 0, -mag, mag)
+
+
+def _ulps(got_bf16, ref_f64):
+    ref_bits = torch.tensor(ref_f64, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy()
+    return np.abs(_ordered(_bits(got_bf16)) - _ordered(ref_bits))
+
+
+def test_rope_helper_within_one_ulp():
+    g = torch.Generator().manual_seed(1)
+    n = 300
+    x = torch.randn(n, 2, 256, generator=g).to(torch.bfloat16)
+    pos = torch.randint(0, 1 << 20, (n,), generator=g, dtype=torch.int32)
+    pos[:4] = torch.tensor([0, 1, 4095, (1 << 20) - 1], dtype=torch.int32)
+    xd = x.cuda().clone()
+    qsa.rope_apply(xd, row_stride=512, head_stride=256, n_heads=2, n_rows=n, pos=pos.cuda())
+    _sync()
+    ref = O.rope(np64(x), pos.numpy().astype(np.float64)[:, None])
+    assert np.array_equal(_bits(xd)[..., 64:], _bits(x)[..., 64:])     # untouched dims
+    assert _ulps(xd, ref).max() <= 1
+    # pos = NULL: consecutive positions from pos0
+    xe = x.cuda().clone()
+    qsa.rope_apply(xe, row_stride=512, head_stride=256, n_heads=2, n_rows=n, pos0=1000)
+    _sync()
+    ref2 = O.rope(np64(x), (1000 + np.arange(n, dtype=np.float64))[:, None])
+    assert _ulps(xe, ref2).max() <= 1
+
+
+# ----------------------------------------------- attention on oracle choices
+
+def _load_oracle_selection(r, view, rows):
+    sel = torch.full((r.n_q, r.budget), -1, dtype=torch.int32)
+    cnt = torch.zeros((r.n_q,), dtype=torch.int32)
+    chosen = {}
+    for row in range(r.n_q):
+        ids = view.select(row)
+        sel[row, :len(ids)] = torch.as_tensor(ids, dtype=torch.int32)
+        cnt[row] = len(ids)
+        chosen[row] = ids
+    r.sel.copy_(sel.cuda())
+    r.sel_count.copy_(cnt.cuda())
+    return chosen
+
+
+def test_attend_prefill_on_oracle_selection_tiny():
+    b = W.tiny_prefill(T=512)
+    view = OracleView(b)
+    r = QSARunner(b.to("cuda"))
+    chosen = _load_oracle_selection(r, view, range(b.n_q))
+    r.attend()
+    _sync()
+    worst = 0.0
+    for row in range(b.n_q):
+        ref_o, ref_l = view.attend(row, chosen[row])
+        e, rel = check_attention(r.out[row], r.lse[row], ref_o, ref_l, f"row {row}")
+        worst = max(worst, rel)
+    print(f"tiny prefill attention: worst rel-L2 {worst:.2e}")
+
+
+def test_attend_decode_on_oracle_selection():
+    b = W.make_decode(seq_lens=[2051, 9003, 40002, 16384, 5], budget=512, n_plant=32, seed=11)
+    view = OracleView(b)
+    r = QSARunner(b.to("cuda"))
+    chosen = _load_oracle_selection(r, view, range(b.n_q))
+    r.attend()
+    _sync()
+    for row in range(b.n_q):
+        ref_o, ref_l = view.attend(row, chosen[row])
+        check_attention(r.out[row], r.lse[row], ref_o, ref_l, f"decode row {row}")
+    # split-K decode equals the one-workgroup prefill kernel on the same choices
+    out_d, lse_d = r.out.clone(), r.lse.clone()
+    qsa.attend_prefill(r.b.q, r.b.cu_q, r.b.seq_len, 1, r.k_cache, r.v_cache, r.sel, r.sel_count,
+                       r.budget, r.out, r.lse)
+    _sync()
+    assert (r.out.float() - out_d.float()).abs().max().item() <= 2e-3
+    assert (r.lse - lse_d).abs().max().item() <= 1e-4
+
+
+# ------------------------------------------------------------- selection
+
+def _select_and_check(b, exact=False, rows=None):
+    view = OracleView(b)
+    r = QSARunner(b.to("cuda"))
+    r.pool()
+    r.select()
+    _sync()
+    sel, cnt = r.sel.cpu().numpy(), r.sel_count.cpu().numpy()
+    rows = range(b.n_q) if rows is None else rows
+    kinds = {"exact": 0, "near": 0}
+    for row in rows:
+        kinds[check_selection(view, row, sel[row], int(cnt[row]), exact=exact)] += 1
+    return r, view, kinds
+
+
+def test_index_select_tiny_prefill():
+    _, _, kinds = _select_and_check(W.tiny_prefill(T=512))
+    print("tiny prefill selection:", kinds)
+
+
+def test_index_select_exact_grid_prefill():
+    b = W.make_prefill(prefix=0, chunk=3001, budget=100, seg=256, n_plant=16, seed=21,
+                       exact_grid=True)
+    _select_and_check(b, exact=True)
+
+
+def test_index_select_exact_grid_sampled_path():
+    # more than 4096 candidates per row: sample, threshold, filter, select
+    b = W.make_prefill(prefix=40000, chunk=77, budget=512, seg=32, n_plant=32, seed=22,
+                       exact_grid=True)
+    _select_and_check(b, exact=True)
+
+
+def test_index_select_exact_grid_decode():
+    b = W.make_decode(seq_lens=[20001, 37002, 70003, 5000, 3], budget=512, n_plant=32, seed=23,
+                      exact_grid=True)
+    _select_and_check(b, exact=True)
+
+
+def test_index_select_decode_rule():
+    b = W.make_decode(seq_lens=[131073, 20001, 4100, 99999], budget=512, n_plant=32, seed=24)
+    _, _, kinds = _select_and_check(b)
+    print("decode selection:", kinds)
+
+
+def test_index_select_near_ties():
+    b = W.make_decode(seq_lens=[9001, 30002, 70003, 4099], budget=512, n_plant=32, seed=25,
+                      near_tie=[True, True, False, True])
+    r, view, _ = _select_and_check(b)
+    sel = r.sel.cpu().numpy()
+    for s in (0, 1, 3):
+        assert set(b.planted[s]) == set(sel[s].tolist())   # the 512 tied blocks, not the 0.99 one
+
+
+def test_index_select_budget_sweep_and_tiny_rows():
+    for budget in (1, 7, 64, 511, 512):
+        b = W.make_prefill(prefix=0, chunk=700, budget=budget, seg=64, n_plant=8, seed=26 + budget,
+                           exact_grid=True)
+        _select_and_check(b, exact=True)
+
+
+def test_index_select_fallback_all_ties():
+    # identical block keys: every score ties, the list overflows, the exact
+    # fallback must keep the lowest 512 block ids
+    b = W.make_decode(seq_lens=[40001, 20002], budget=512, n_plant=0, seed=27)
+    b.idx_k[:] = b.idx_k[0, 0].clone()
+    r, view, _ = _select_and_check(b, exact=True)
+    sel = r.sel.cpu().numpy()
+    assert np.array_equal(sel[0], np.arange(512)) and np.array_equal(sel[1], np.arange(512))
+
+
+def test_index_select_fallback_short_list():
+    # only the sampled blocks (every 16th) score high, so the threshold lets
+    # through fewer than K entries and the exact fallback must take over
+    b = W.make_decode(seq_lens=[4 * 8192 + 1], budget=512, n_plant=0, seed=28)
+    u = b.idx_q[0].float().sum(0)
+    u = u / u.norm()
+    for blk in range(0, 8192, 16):
+        b.idx_k[0, 4 * blk:4 * blk + 4] = (math.sqrt(128) * (1 + blk / 1e4) * u).to(torch.bfloat16)
+    r, view, _ = _select_and_check(b, exact=True)
+    assert np.array_equal(r.sel.cpu().numpy()[0], np.arange(0, 8192, 16))
+
+
+# ------------------------------------------------------------- end to end
+
+def _end_to_end(b, rows, dense=False):
+    view = OracleView(b)
+    r = QSARunner(b if b.idx_q.is_cuda else b.to("cuda"))
+    r.step()
+    _sync()
+    sel, cnt = r.sel.cpu().numpy(), r.sel_count.cpu().numpy()
+    kinds = {"exact": 0, "near": 0}
+    worst = 0.0
+    for row in rows:
+        kinds[check_selection(view, row, sel[row], int(cnt[row]))] += 1
+        if dense:
+            ref_o, ref_l = view.dense(row)
+        else:
+            ref_o, ref_l = view.attend(row, sel[row][:cnt[row]])
+        _, rel = check_attention(r.out[row], r.lse[row], ref_o, ref_l, f"row {row}")
+        worst = max(worst, rel)
+    return kinds, worst
+
+
+def test_end_to_end_tiny_prefill():
+    b = W.tiny_prefill(T=512)
+    kinds, worst = _end_to_end(b, range(b.n_q))
+    print("tiny prefill:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_end_to_end_dense_equivalence():
+    # T <= 2048 with budget 512: every row keeps every completed block, so the
+    # output is plain causal GQA attention over 0..i
+    b = W.prefill_8k(T=2048)
+    rows = [0, 1, 2, 3, 4, 5, 63, 64, 1000, 2045, 2046, 2047]
+    kinds, worst = _end_to_end(b, rows[:6], dense=True)   # naive loops: keep short rows
+    kinds, worst = _end_to_end(b, rows)
+    print("dense case:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_end_to_end_prefill_8k_sampled():
+    b = W.prefill_8k(T=8192)
+    rng = np.random.default_rng(3)
+    rows = sorted(set(rng.choice(8192, 40, replace=False).tolist()) | {2047, 2048, 2051, 8190, 8191})
+    kinds, worst = _end_to_end(b, rows)
+    print("prefill 8k:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_end_to_end_decode_reduced():
+    b = W.decode_128k(n_seq=6, ctx=32768)
+    kinds, worst = _end_to_end(b, range(6))
+    print("decode:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_end_to_end_ragged_decode_reduced():
+    b = W.ragged_decode(n_seq=6, lo=4096, hi=200000)
+    kinds, worst = _end_to_end(b, range(6))
+    print("ragged decode:", kinds, f"worst rel-L2 {worst:.2e}")

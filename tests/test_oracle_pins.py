@@ -255,7 +255,7 @@ def test_oracle_hand_worked_query(golden_dir):
     k_raw = np.random.default_rng(1).standard_normal((L, 2, 256))
     v = np.zeros((L, 2, 256))
     v[:, :, 0] = np.arange(L)[:, None]
-    out, lse = O.attend(np.zeros((24, 256)), k_raw, v, S, i)
+    out, lse = O.attend(np.zeros((24, 256)), k_raw[S], v[S], S, i)
     assert np.allclose(out[:, 0], case["expected_out_dim0_with_zero_q_and_v_equal_position"], atol=1e-12)
     assert np.allclose(lse, math.log(10), atol=1e-12)
 
@@ -307,7 +307,7 @@ def test_oracle_sparse_equals_dense_when_budget_covers():
         n_c = O.completed_blocks(i)
         blocks = np.arange(n_c)                 # budget >= n_c keeps every block
         S = O.sparse_token_set(blocks, i)
-        o1, l1 = O.attend(q, k, v, S, i)
+        o1, l1 = O.attend(q, k[S], v[S], S, i)
         o2, l2 = O.dense_causal_gqa(q, k, v, i)
         assert np.allclose(o1, o2, atol=1e-12, rtol=1e-12)
         assert np.allclose(l1, l2, atol=1e-12, rtol=1e-12)
@@ -338,7 +338,7 @@ def test_oracle_attention_reveals_attended_set():
     i = 57
     blocks = np.array([2, 5, 9])
     S = O.sparse_token_set(blocks, i)
-    out, lse = O.attend(np.zeros((24, 256)), k, v, S, i)
+    out, lse = O.attend(np.zeros((24, 256)), k[S], v[S], S, i)
     assert np.allclose(out[:, 0], np.mean(S), atol=1e-12)
     assert np.allclose(out[:, 1], np.mean(S.astype(float) ** 2), atol=1e-9)
     assert np.allclose(out[12:, 2], 3.25, atol=1e-14)

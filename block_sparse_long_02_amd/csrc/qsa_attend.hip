@@ -62,8 +62,8 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
               const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
               int64_t seq_stride, int64_t head_stride,
               const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int budget,
-              int n_splits, uint16_t* __restrict__ out, float* __restrict__ lse,
-              float* __restrict__ part) {
+              int n_splits, int one_per_seq, uint16_t* __restrict__ out,
+              float* __restrict__ lse, float* __restrict__ part) {
   __shared__ AttnShared sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -75,8 +75,9 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   if (row >= n_rows) return;
 
   // ---- which sequence / position, and is the selection usable?
-  const int s = find_seq(cu_q, n_seq, row);
-  const int q_begin = cu_q[s], q_end = cu_q[s + 1];
+  // one_per_seq: row s is the single query of sequence s (decode)
+  const int s = one_per_seq ? row : find_seq(cu_q, n_seq, row);
+  const int q_begin = one_per_seq ? row : cu_q[s], q_end = one_per_seq ? row + 1 : cu_q[s + 1];
   const int L = seq_len[s];
   const int pos = L - (q_end - q_begin) + (row - q_begin);
   const int n_c = (pos + 1) >> 2;
@@ -290,35 +291,29 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   }
 }
 
-// c[i] = i for i = 0..n (the row offsets of a one-query-per-sequence batch).
-__global__ void iota_kernel(int32_t* __restrict__ c, int32_t n) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i <= n) c[i] = i;
-}
-
-// Combine the n_splits partials of every (row, KV head): one workgroup per
-// (row, KV head), one output dim per thread.
+// Combine the n_splits partials of every (row, KV head, head): one workgroup
+// per (row, query head), one output dim per thread.
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ part, int n_splits, int n_rows,
                uint16_t* __restrict__ out, float* __restrict__ lse) {
-  const int row = blockIdx.x >> 1, g = blockIdx.x & 1;
+  const int h = blockIdx.x % kGroup;
+  const int g = (blockIdx.x / kGroup) & 1;
+  const int row = blockIdx.x / (2 * kGroup);
   if (row >= n_rows) return;
   const int d = threadIdx.x;
   const float* base = part + (int64_t)(row * 2 + g) * n_splits * kPartFloats;
-  for (int h = 0; h < kGroup; ++h) {
-    float mx = -INFINITY;
-    for (int sp = 0; sp < n_splits; ++sp) mx = fmaxf(mx, base[sp * kPartFloats + kGroup * kHeadDim + h]);
-    float lsum = 0.f, acc = 0.f;
-    for (int sp = 0; sp < n_splits; ++sp) {
-      const float* pp = base + sp * kPartFloats;
-      const float l = pp[kGroup * kHeadDim + 16 + h];
-      const float f = l > 0.f ? exp2f(pp[kGroup * kHeadDim + h] - mx) : 0.f;
-      lsum += l * f;
-      acc += pp[h * kHeadDim + d] * f;
-    }
-    out[((int64_t)row * kQHeads + g * kGroup + h) * kHeadDim + d] = (uint16_t)f32_to_bf16_bits(acc / lsum);
-    if (lse && d == 0) lse[(int64_t)row * kQHeads + g * kGroup + h] = (mx + log2f(lsum)) * kLn2;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < n_splits; ++sp) mx = fmaxf(mx, base[sp * kPartFloats + kGroup * kHeadDim + h]);
+  float lsum = 0.f, acc = 0.f;
+  for (int sp = 0; sp < n_splits; ++sp) {
+    const float* pp = base + sp * kPartFloats;
+    const float l = pp[kGroup * kHeadDim + 16 + h];
+    const float f = l > 0.f ? exp2f(pp[kGroup * kHeadDim + h] - mx) : 0.f;
+    lsum += l * f;
+    acc += pp[h * kHeadDim + d] * f;
   }
+  out[((int64_t)row * kQHeads + g * kGroup + h) * kHeadDim + d] = (uint16_t)f32_to_bf16_bits(acc / lsum);
+  if (lse && d == 0) lse[(int64_t)row * kQHeads + g * kGroup + h] = (mx + log2f(lsum)) * kLn2;
 }
 
 }  // namespace qsa
@@ -358,14 +353,13 @@ int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_le
   hipLaunchKernelGGL(qsa::attend_kernel<true>, dim3(n_q * 2), dim3(256), 0, (hipStream_t)stream,
                      (const uint16_t*)q, cu_q, seq_len, n_seq, n_q, (const uint16_t*)k_cache,
                      (const uint16_t*)v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
-                     budget, 1, (uint16_t*)out, lse, (float*)nullptr);
+                     budget, 1, 0, (uint16_t*)out, lse, (float*)nullptr);
   return qsa_host::launch_status();
 }
 
 size_t qsa_attend_decode_workspace(int32_t n_seq) {
   if (n_seq <= 0) return 0;
-  return (size_t)n_seq * 2 * kDecodeSplits * qsa::kPartFloats * sizeof(float) +
-         (size_t)(n_seq + 1) * sizeof(int32_t) + 256;
+  return (size_t)n_seq * 2 * kDecodeSplits * qsa::kPartFloats * sizeof(float);
 }
 
 int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq, const void* k_cache,
@@ -381,20 +375,16 @@ int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq, cons
   if (st != QSA_OK) return st;
   if (!workspace || !aligned16(workspace)) return QSA_ERR_INVALID_ARG;
   if (ws_bytes < qsa_attend_decode_workspace(n_seq)) return QSA_ERR_WORKSPACE_TOO_SMALL;
-  if ((int64_t)n_seq * 2 * kDecodeSplits > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  if ((int64_t)n_seq * 2 * qsa::kGroup > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
   float* part = (float*)workspace;
-  // one query per sequence: cu_q = 0, 1, ..., n_seq, written by a tiny kernel
-  int32_t* cu = (int32_t*)((char*)workspace +
-                           (size_t)n_seq * 2 * kDecodeSplits * qsa::kPartFloats * sizeof(float));
-  hipLaunchKernelGGL(qsa::iota_kernel, dim3((n_seq + 256) / 256), dim3(256), 0,
-                     (hipStream_t)stream, cu, n_seq);
   hipLaunchKernelGGL(qsa::attend_kernel<false>, dim3(n_seq * 2 * kDecodeSplits), dim3(256), 0,
-                     (hipStream_t)stream, (const uint16_t*)q, (const int32_t*)cu, seq_len, n_seq,
-                     n_seq, (const uint16_t*)k_cache, (const uint16_t*)v_cache, kv_seq_stride,
-                     kv_head_stride, sel, sel_count, budget, kDecodeSplits, (uint16_t*)nullptr,
-                     (float*)nullptr, part);
-  hipLaunchKernelGGL(qsa::combine_kernel, dim3(n_seq * 2), dim3(256), 0, (hipStream_t)stream,
-                     (const float*)part, kDecodeSplits, n_seq, (uint16_t*)out, lse);
+                     (hipStream_t)stream, (const uint16_t*)q, (const int32_t*)nullptr, seq_len,
+                     n_seq, n_seq, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
+                     kv_seq_stride, kv_head_stride, sel, sel_count, budget, kDecodeSplits, 1,
+                     (uint16_t*)nullptr, (float*)nullptr, part);
+  hipLaunchKernelGGL(qsa::combine_kernel, dim3(n_seq * 2 * qsa::kGroup), dim3(256), 0,
+                     (hipStream_t)stream, (const float*)part, kDecodeSplits, n_seq, (uint16_t*)out,
+                     lse);
   return launch_status();
 }
 

@@ -22,20 +22,29 @@
 //                       the total order, then the ids sorted ascending.
 // Exactness does not depend on the sample: if the list holds >= K entries it
 // contains the true top K (all of them score >= the K-th score >= tau).  A row
-// whose list is short or overflows goes to
-//   5. fallback      -- an exact radix select that recomputes its scores on
-//                       every pass (slow, needs no score storage).
+// whose list is short or overflows is selected inside step 4 by an exact
+// radix select that recomputes its scores on every pass (slow, needs no score
+// storage, rare).
 #include <math.h>
 
 #include "qsa_common.hpp"
 
 namespace qsa {
 
+// m-tiles (of 4 queries x 4 heads) per workgroup in the prefill score GEMM
+#ifndef QSA_PREFILL_MT
+#define QSA_PREFILL_MT 6
+#endif
+constexpr int kPrefillMT = QSA_PREFILL_MT;
+// waves per SIMD the prefill score GEMM is compiled for
+#ifndef QSA_SCORE_WAVES
+#define QSA_SCORE_WAVES 2
+#endif
+constexpr int kScoreWaves = QSA_SCORE_WAVES;
 constexpr int kCandCap = 4096;      // list capacity per row
 constexpr int kSampleStride = 16;   // every 16th block is sampled
 constexpr int kSampleExtra = 1536;  // aimed-for surplus of list entries over K
 constexpr int kBins = 2048;         // 11-bit radix digits
-constexpr int kFallbackWGs = 64;
 // 1/sqrt(128) rounded once to float32
 constexpr float kScoreScale = 0x1.6a09e6p-4f;
 
@@ -62,13 +71,20 @@ __device__ __forceinline__ RowGeom row_geom(const int32_t* __restrict__ cu_q,
   return r;
 }
 
+// max(x, +0) on the bit pattern: negative floats (sign bit set) are negative
+// int32 values, so a signed integer max gives +0 for them and x otherwise
+// (-0 also maps to +0).  One instruction instead of a NaN-quieting fmaxf.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // The float32 epilogue shared by every pass: heads in acc[0..3].
 __device__ __forceinline__ float block_score(f32x4 acc, const float* __restrict__ w) {
 #pragma clang fp contract(off)
-  const float u0 = fmaxf(acc[0], 0.f) * kScoreScale;
-  const float u1 = fmaxf(acc[1], 0.f) * kScoreScale;
-  const float u2 = fmaxf(acc[2], 0.f) * kScoreScale;
-  const float u3 = fmaxf(acc[3], 0.f) * kScoreScale;
+  const float u0 = relu_bits(acc[0]) * kScoreScale;
+  const float u1 = relu_bits(acc[1]) * kScoreScale;
+  const float u2 = relu_bits(acc[2]) * kScoreScale;
+  const float u3 = relu_bits(acc[3]) * kScoreScale;
   float s = w[0] * u0;
   s = s + w[1] * u1;
   s = s + w[2] * u2;
@@ -80,21 +96,38 @@ __device__ __forceinline__ float block_score(f32x4 acc, const float* __restrict_
 // Workgroup = one tile of 4*MT query rows of one sequence x a chunk of
 // `chunk_cols` virtual columns.  Virtual column v is block v*stride (stride 16
 // in the sample pass, 1 in the filter pass).  A row r = 4*(query) + head of the
-// tile is MFMA row r%16 of m-tile r/16; each wave takes 16-column tiles
-// round-robin, U tiles per trip so that U*4 KB of block keys are in flight.
-template <int MT, int U, bool kSample>
-__global__ void __launch_bounds__(256)
+// tile is MFMA row r%16 of m-tile r/16; each wave takes every 4th 16-column
+// tile and software-pipelines them (see the main loop).
+//
+// Filter-pass output per row:
+//   * rows with n_c <= kCandCap keep every candidate: entry b goes to slot b
+//     (no atomics; the threshold kernel already set the count to n_c);
+//   * other rows append (key, b) for key >= tau: hits are staged in LDS and
+//     each workgroup reserves its slots with one global atomic per row.
+template <int MT>
+struct ScoreStage {
+  static constexpr int kCap = MT == 1 ? 1024 : 128;   // staged hits per row
+};
+
+template <int MT, bool kSample>
+__global__ void __launch_bounds__(256, MT == 1 ? 4 : kScoreWaves)
 score_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
              const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len, int n_seq,
              int n_q, int tiles_per_seq, int max_blocks, const uint16_t* __restrict__ bk,
              int64_t bk_stride, int chunk_cols, const uint32_t* __restrict__ thresh,
              int32_t* __restrict__ cnt, u32x2* __restrict__ cand,
-             uint32_t* __restrict__ samples, int ns_stride) {
+             uint16_t* __restrict__ samples, int ns_stride) {
   constexpr int QT = 4 * MT;
   constexpr int stride = kSample ? kSampleStride : 1;
+  constexpr int kCapL = kSample ? 1 : ScoreStage<MT>::kCap;
   __shared__ float s_w[QT][4];
+  __shared__ f32x4 s_wc[QT];      // w_h * (1/sqrt(128)) for the pre-filter
+  __shared__ float s_tlo[QT];     // pre-filter threshold, a little below tau
   __shared__ int s_nc[QT];
   __shared__ uint32_t s_th[QT];
+  __shared__ int s_cnt[QT];
+  __shared__ int s_base[QT];
+  __shared__ u32x2 s_buf[QT][kCapL];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -122,11 +155,22 @@ score_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
     s_nc[j] = (kSample && nc <= kCandCap) ? 0 : nc;    // sample only rows that need it
     const uint32_t th = kSample ? 0u : thresh[rj];
     s_th[j] = ok && !kSample ? th : 0xFFFFFFFFu;
+    s_cnt[j] = 0;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const float wv = w[(int64_t)rj * 4 + h];
       s_w[j][h] = ok ? wv : 0.f;
+      s_wc[j][h] = ok ? wv * kScoreScale : 0.f;
     }
+    // Pre-filter bound.  The defined score and the fast one (fma chain with
+    // w*c folded in) both round non-negative terms a handful of times, so each
+    // lies within 2^-21 (relative) of c * sum_h w_h ReLU(t_h); a candidate
+    // with score >= tau therefore has fast score >= tau * (1 - 2^-19); the
+    // absolute 2^-100 covers rounding at subnormal scale.  Rows that keep
+    // every candidate pass everything (-1).
+    const float tau = __uint_as_float(s_th[j]);
+    s_tlo[j] = (!ok || kSample) ? INFINITY
+                                : (nc <= kCandCap ? -1.f : tau * (1.f - 0x1p-19f) - 0x1p-100f);
   }
 
   // A fragments: m-tile mt, k-step ks -> row mt*16 + col (query mt*4 + col/4,
@@ -146,50 +190,123 @@ score_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
   }
   __syncthreads();
 
+  const bool collect_all = !kSample && nc_last <= kCandCap;
   const uint16_t* bseq = bk + (int64_t)s * bk_stride;
-  for (int c0 = v0 + wave * 16 * U; c0 < v1; c0 += 64 * U) {
-    u32x4 bf[U][4];
-    int vcol[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      vcol[u] = c0 + u * 16 + col;
-      const int b = min(vcol[u], v1 - 1) * stride;     // in-bounds row for masked columns
-      const uint16_t* src = bseq + (int64_t)b * kIdxDim + 8 * grp;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bf[u][ks] = ldg16(src + 32 * ks);
+  // exact score of m-tile mt's row for this lane's block, and where it goes
+  auto emit_exact = [&](const f32x4& acc, int mt, int vcol, int b) {
+    const int j = mt * 4 + grp;
+    const int nc = s_nc[j];
+    if (!(vcol < v1 && b < nc)) return;
+    const uint32_t key = __float_as_uint(block_score(acc, s_w[j]));
+    const int64_t rbase = (int64_t)(row0 + j) * kCandCap;
+    if (kSample) {
+      samples[(int64_t)(row0 + j) * ns_stride + vcol] = (uint16_t)(key >> 16);
+    } else if (nc <= kCandCap) {
+      cand[rbase + b] = u32x2{key, (uint32_t)b};
+    } else if (key >= s_th[j]) {
+      const int slot = atomicAdd(&s_cnt[j], 1);
+      if (slot < kCapL) {
+        s_buf[j][slot] = u32x2{key, (uint32_t)b};
+      } else {                                          // rare: LDS stage full
+        const int g = atomicAdd(&cnt[row0 + j], 1);
+        if (g < kCandCap) cand[rbase + g] = u32x2{key, (uint32_t)b};
+      }
     }
+  };
+  // B fragments of the 16-column tile starting at c0 (clamped: in bounds)
+  auto load_tile = [&](u32x4 (&bf)[4], int c0) {
+    const int b = min(c0 + col, v1 - 1) * stride;
+    const uint16_t* src = bseq + (int64_t)b * kIdxDim + 8 * grp;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int b = vcol[u] * stride;
+    for (int ks = 0; ks < 4; ++ks) bf[ks] = ldg16(src + 32 * ks);
+  };
+  auto mfma_tile = [&](const u32x4 (&bf)[4], f32x4 (&acc)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc[mt] = mfma_16x16x32(af[mt][ks], bf[ks], acc[mt]);
+    }
+  };
+  // pre-filter constants of this lane's rows, held in registers
+  f32x4 r_wc[MT];
+  float r_tlo[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    r_wc[mt] = s_wc[mt * 4 + grp];
+    r_tlo[mt] = s_tlo[mt * 4 + grp];
+  }
+  auto epilogue = [&](const f32x4 (&acc)[MT], int c0) {
+    const int vcol = c0 + col;
+    const int b = vcol * stride;
+    if (kSample || collect_all) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) emit_exact(acc[mt], mt, vcol, b);
+    } else {
+      // branch-free conservative pre-filter for every m-tile (columns past
+      // the row's candidates may pass; emit_exact drops them)
+      uint32_t pass_bits = 0;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 wc = r_wc[mt];
+        float fast = relu_bits(acc[mt][3]) * wc[3];
+        fast = fmaf(relu_bits(acc[mt][2]), wc[2], fast);
+        fast = fmaf(relu_bits(acc[mt][1]), wc[1], fast);
+        fast = fmaf(relu_bits(acc[mt][0]), wc[0], fast);
+        pass_bits |= (fast >= r_tlo[mt] ? 1u : 0u) << mt;
+      }
+      if (__ballot(pass_bits != 0)) {                   // rare: exact arithmetic
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma_16x16x32(af[mt][ks], bf[u][ks], acc);
-        // lane holds the 4 heads of query j = mt*4 + grp for block b
-        const int j = mt * 4 + grp;
-        const bool live = vcol[u] < v1 && b < s_nc[j];
-        const float sc = block_score(acc, s_w[j]);
-        const uint32_t key = __float_as_uint(sc);
-        if (kSample) {
-          if (live) samples[(int64_t)(row0 + j) * ns_stride + vcol[u]] = key;
-        } else {
-          const bool hit = live && key >= s_th[j];
-          const unsigned long long mask = __ballot(hit);
-          if (mask) {
-            const uint32_t gm = (uint32_t)(mask >> (16 * grp)) & 0xFFFFu;
-            const int n = __popc(gm);
-            const int rank = __popc(gm & ((1u << col) - 1u));
-            int base = 0;
-            if (hit && rank == 0) base = atomicAdd(&cnt[row0 + j], n);
-            const int leader = 16 * grp + (gm ? __ffs(gm) - 1 : 0);
-            base = __shfl(base, leader, 64);
-            if (hit) {
-              const int slot = base + rank;
-              if (slot < kCandCap) cand[(int64_t)(row0 + j) * kCandCap + slot] = u32x2{key, (uint32_t)b};
-            }
-          }
-        }
+        for (int mt = 0; mt < MT; ++mt)
+          if (pass_bits & (1u << mt)) emit_exact(acc[mt], mt, vcol, b);
+      }
+    }
+  };
+
+  // Software pipeline over this wave's column tiles c, c+64, c+128, ...:
+  // the MFMAs of tile t+1 are issued before the epilogue of tile t, and the
+  // block keys of tile t+2 are in flight meanwhile.
+  {
+    u32x4 bX[4], bY[4];
+    f32x4 aX[MT], aY[MT];
+    int c = v0 + wave * 16;
+    if (c < v1) {
+      load_tile(bX, c);
+      load_tile(bY, c + 64);
+      mfma_tile(bX, aX);                 // aX: tile c
+      load_tile(bX, c + 128);
+      for (;;) {
+        // aX = tile c, bY = tile c+64, bX = tile c+128 (in flight)
+        const int c1 = c + 64;
+        if (c1 < v1) mfma_tile(bY, aY);  // aY: tile c+64
+        epilogue(aX, c);
+        if (c1 >= v1) break;
+        load_tile(bY, c1 + 128);         // bY: tile c+192
+        const int c2 = c1 + 64;
+        if (c2 < v1) mfma_tile(bX, aX);  // aX: tile c+128
+        epilogue(aY, c1);
+        if (c2 >= v1) break;
+        load_tile(bX, c2 + 128);         // bX: tile c+256
+        c = c2;
+      }
+    }
+  }
+
+  if (!kSample) {
+    // flush staged hits: one global reservation per row
+    __syncthreads();
+    if (threadIdx.x < QT) {
+      const int j = threadIdx.x;
+      const int n = min(s_cnt[j], kCapL);
+      s_base[j] = n > 0 ? atomicAdd(&cnt[row0 + j], n) : 0;
+      s_cnt[j] = n;
+    }
+    __syncthreads();
+    for (int j = 0; j < QT; ++j) {
+      const int n = s_cnt[j];
+      for (int i = threadIdx.x; i < n; i += 256) {
+        const int slot = s_base[j] + i;
+        if (slot < kCandCap) cand[(int64_t)(row0 + j) * kCandCap + slot] = s_buf[j][i];
       }
     }
   }
@@ -255,27 +372,104 @@ __device__ void bitonic_sort_512(int* a) {
 }
 
 // ------------------------------------------------------------ threshold
+// Per row: rows with <= kCandCap candidates keep them all (count preset to
+// n_c, tau = 0); other rows get tau = the r-th largest sampled score, found
+// by an LDS radix select (samples staged in LDS when they fit).
+constexpr int kLdsSamples = 16384;
+
+// Samples are the top 16 bits of the sampled score keys; tau is the lower edge
+// of the r-th largest one, so at least r*16 candidates are expected above it.
 __global__ void __launch_bounds__(256)
 threshold_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len, int n_seq,
-                 int max_blocks, int budget, const uint32_t* __restrict__ samples, int ns_stride,
-                 uint32_t* __restrict__ thresh, int32_t* __restrict__ cnt,
-                 int32_t* __restrict__ fb_count) {
+                 int max_blocks, int budget, const uint16_t* __restrict__ samples, int ns_stride,
+                 uint32_t* __restrict__ thresh, int32_t* __restrict__ cnt) {
+  __shared__ uint16_t s_smp[kLdsSamples];
   __shared__ int hist[kBins];
   __shared__ int tmp[8];
   __shared__ int res[2];
   const int row = blockIdx.x;
-  if (row == 0 && threadIdx.x == 0) *fb_count = 0;
   const RowGeom g = row_geom(cu_q, seq_len, n_seq, row, max_blocks);
+  if (!g.ok) {
+    if (threadIdx.x == 0) { thresh[row] = 0xFFFFFFFFu; cnt[row] = 0; }
+    return;
+  }
+  if (g.n_c <= kCandCap) {
+    if (threadIdx.x == 0) { thresh[row] = 0u; cnt[row] = g.n_c; }
+    return;
+  }
   if (threadIdx.x == 0) cnt[row] = 0;
-  if (!g.ok) { if (threadIdx.x == 0) thresh[row] = 0xFFFFFFFFu; return; }
-  if (g.n_c <= kCandCap) { if (threadIdx.x == 0) thresh[row] = 0u; return; }
   const int k = min(budget, g.n_c);
   const int ns = (g.n_c + kSampleStride - 1) / kSampleStride;
   const int r = min(ns, (k + kSampleExtra + kSampleStride - 1) / kSampleStride);
-  const uint32_t* sp = samples + (int64_t)row * ns_stride;
-  const uint32_t tau = block_kth_largest(
-      [&](int i, bool& in) { in = true; return sp[i]; }, ns, r, 31, hist, tmp, res);
-  if (threadIdx.x == 0) thresh[row] = tau;
+  const uint16_t* sp = samples + (int64_t)row * ns_stride;
+  uint32_t t16;
+  if (ns <= kLdsSamples) {
+    for (int i = threadIdx.x; i < ns; i += 256) s_smp[i] = sp[i];
+    __syncthreads();
+    t16 = block_kth_largest([&](int i, bool& in) { in = true; return (uint32_t)s_smp[i]; }, ns, r,
+                            16, hist, tmp, res);
+  } else {
+    t16 = block_kth_largest([&](int i, bool& in) { in = true; return (uint32_t)sp[i]; }, ns, r, 16,
+                            hist, tmp, res);
+  }
+  if (threadIdx.x == 0) thresh[row] = t16 << 16;
+}
+
+// ------------------------------------------------------------- fallback
+// Exact select for a row whose list came out short or overflowed: recompute
+// the score of every candidate on every radix pass (VALU dot products, one
+// block per thread), then emit in ascending block order.  Slow but needs no
+// score storage; the sampled threshold makes it rare.
+__device__ __forceinline__ uint32_t recompute_key(const uint16_t* __restrict__ q4,
+                                                  const float* __restrict__ w4,
+                                                  const uint16_t* __restrict__ kb) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int d8 = 0; d8 < kIdxDim / 8; ++d8) {
+    const u32x4 kv = ldg16(kb + 8 * d8);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const u32x4 qv = ldg16(q4 + h * kIdxDim + 8 * d8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[h] += bf16_lo(qv[e]) * bf16_lo(kv[e]);
+        acc[h] += bf16_hi(qv[e]) * bf16_hi(kv[e]);
+      }
+    }
+  }
+  return __float_as_uint(block_score(acc, w4));
+}
+
+__device__ void exact_select_recompute(const uint16_t* __restrict__ q4, const float* __restrict__ w4,
+                                       const uint16_t* __restrict__ bseq, int n_c, int k,
+                                       int32_t* __restrict__ out, int budget, int* hist, int* tmp,
+                                       int* res) {
+  auto key_of = [&](int b, bool& in) {
+    in = true;
+    return recompute_key(q4, w4, bseq + (int64_t)b * kIdxDim);
+  };
+  const uint32_t tau = block_kth_largest(key_of, n_c, k, 31, hist, tmp, res);
+  int above = 0;
+  for (int b = threadIdx.x; b < n_c; b += 256) { bool in; above += key_of(b, in) > tau; }
+  int tot_above;
+  block_excl_scan_256(above, tmp, tot_above);
+  const int need = k - tot_above;   // ties to take, lowest block ids first
+  int ties_run = 0, out_run = 0;
+  for (int b0 = 0; b0 < n_c; b0 += 256) {
+    const int b = b0 + threadIdx.x;
+    bool in;
+    const uint32_t key = b < n_c ? key_of(b, in) : 0u;
+    const bool is_tie = b < n_c && key == tau;
+    const bool is_above = b < n_c && key > tau;
+    int tie_tot;
+    const int tie_rank = ties_run + block_excl_scan_256(is_tie ? 1 : 0, tmp, tie_tot);
+    const bool take = is_above || (is_tie && tie_rank < need);
+    int take_tot;
+    const int slot = out_run + block_excl_scan_256(take ? 1 : 0, tmp, take_tot);
+    if (take && slot < k) out[slot] = b;
+    ties_run += tie_tot;
+    out_run += take_tot;
+  }
+  for (int i = k + threadIdx.x; i < budget; i += 256) out[i] = -1;
 }
 
 // --------------------------------------------------------- final select
@@ -290,11 +484,12 @@ struct SelectShared {
 };
 
 __global__ void __launch_bounds__(256)
-final_select_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
-                    int n_seq, int max_blocks, int budget, const int32_t* __restrict__ cnt,
+final_select_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
+                    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
+                    int n_seq, int max_blocks, int budget, const uint16_t* __restrict__ bk,
+                    int64_t bk_stride, const int32_t* __restrict__ cnt,
                     const u32x2* __restrict__ cand, int32_t* __restrict__ sel,
-                    int32_t* __restrict__ sel_count, int32_t* __restrict__ fb_count,
-                    int32_t* __restrict__ fb_list) {
+                    int32_t* __restrict__ sel_count) {
   __shared__ SelectShared sh;
   const int row = blockIdx.x;
   const RowGeom g = row_geom(cu_q, seq_len, n_seq, row, max_blocks);
@@ -307,7 +502,10 @@ final_select_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict_
   const int k = min(budget, g.n_c);
   const int c = cnt[row];
   if (k > 0 && (c < k || c > kCandCap)) {
-    if (threadIdx.x == 0) fb_list[atomicAdd(fb_count, 1)] = row;
+    exact_select_recompute(idx_q + (int64_t)row * 4 * kIdxDim, w + (int64_t)row * 4,
+                           bk + (int64_t)g.seq * bk_stride, g.n_c, k, out, budget, sh.hist, sh.tmp,
+                           sh.res);
+    if (threadIdx.x == 0) sel_count[row] = k;
     return;
   }
   for (int i = threadIdx.x; i < c; i += 256) {
@@ -357,87 +555,12 @@ final_select_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict_
   if (threadIdx.x == 0) sel_count[row] = k;
 }
 
-// ------------------------------------------------------------- fallback
-// Exact select for rows whose list was short or overflowed: recompute the
-// score of every candidate on every radix pass (VALU dot products; one block
-// per thread), then emit in ascending block order.
-__device__ __forceinline__ uint32_t recompute_key(const uint16_t* __restrict__ q4,
-                                                  const float* __restrict__ w4,
-                                                  const uint16_t* __restrict__ kb) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int d8 = 0; d8 < kIdxDim / 8; ++d8) {
-    const u32x4 kv = ldg16(kb + 8 * d8);
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const u32x4 qv = ldg16(q4 + h * kIdxDim + 8 * d8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[h] += bf16_lo(qv[e]) * bf16_lo(kv[e]);
-        acc[h] += bf16_hi(qv[e]) * bf16_hi(kv[e]);
-      }
-    }
-  }
-  return __float_as_uint(block_score(acc, w4));
-}
-
-__global__ void __launch_bounds__(256)
-fallback_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
-                const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len, int n_seq,
-                int max_blocks, int budget, const uint16_t* __restrict__ bk, int64_t bk_stride,
-                const int32_t* __restrict__ fb_count, const int32_t* __restrict__ fb_list,
-                int32_t* __restrict__ sel, int32_t* __restrict__ sel_count) {
-  __shared__ int hist[kBins];
-  __shared__ int tmp[8];
-  __shared__ int res[2];
-  const int n_fb = *fb_count;
-  for (int e = blockIdx.x; e < n_fb; e += gridDim.x) {
-    const int row = fb_list[e];
-    const RowGeom g = row_geom(cu_q, seq_len, n_seq, row, max_blocks);
-    const int k = min(budget, g.n_c);
-    const uint16_t* q4 = idx_q + (int64_t)row * 4 * kIdxDim;
-    const float* w4 = w + (int64_t)row * 4;
-    const uint16_t* bseq = bk + (int64_t)g.seq * bk_stride;
-    auto key_of = [&](int b, bool& in) {
-      in = true;
-      return recompute_key(q4, w4, bseq + (int64_t)b * kIdxDim);
-    };
-    const uint32_t tau = block_kth_largest(key_of, g.n_c, k, 31, hist, tmp, res);
-    int above = 0;
-    for (int b = threadIdx.x; b < g.n_c; b += 256) { bool in; above += key_of(b, in) > tau; }
-    int tot_above;
-    block_excl_scan_256(above, tmp, tot_above);
-    const int need = k - tot_above;   // ties to take, lowest block ids first
-    int32_t* out = sel + (int64_t)row * budget;
-    int ties_run = 0, out_run = 0;
-    for (int b0 = 0; b0 < g.n_c; b0 += 256) {
-      const int b = b0 + threadIdx.x;
-      bool in;
-      const uint32_t key = b < g.n_c ? key_of(b, in) : 0u;
-      const bool is_tie = b < g.n_c && key == tau;
-      const bool is_above = b < g.n_c && key > tau;
-      int tie_tot;
-      const int tie_rank = ties_run + block_excl_scan_256(is_tie ? 1 : 0, tmp, tie_tot);
-      const bool take = is_above || (is_tie && tie_rank < need);
-      int take_tot;
-      const int slot = out_run + block_excl_scan_256(take ? 1 : 0, tmp, take_tot);
-      if (take && slot < k) out[slot] = b;
-      ties_run += tie_tot;
-      out_run += take_tot;
-    }
-    for (int i = k + threadIdx.x; i < budget; i += 256) out[i] = -1;
-    if (threadIdx.x == 0) sel_count[row] = k;
-    __syncthreads();
-  }
-}
-
 // ------------------------------------------------------------ workspace
 struct IndexWs {
   uint32_t* thresh;
   int32_t* cnt;
   u32x2* cand;
-  uint32_t* samples;
-  int32_t* fb_count;
-  int32_t* fb_list;
+  uint16_t* samples;
   int ns_stride;
   size_t bytes;
 };
@@ -451,11 +574,9 @@ inline IndexWs index_ws_layout(void* base, int n_q, int max_blocks) {
   ws.ns_stride = (max_blocks + kSampleStride - 1) / kSampleStride;
   ws.thresh = (uint32_t*)(p + off); off = align256(off + (size_t)n_q * 4);
   ws.cnt = (int32_t*)(p + off); off = align256(off + (size_t)n_q * 4);
-  ws.fb_count = (int32_t*)(p + off); off = align256(off + 4);
-  ws.fb_list = (int32_t*)(p + off); off = align256(off + (size_t)n_q * 4);
   ws.cand = (u32x2*)(p + off); off = align256(off + (size_t)n_q * kCandCap * 8);
-  ws.samples = (uint32_t*)(p + off);
-  off = align256(off + (max_blocks > kCandCap ? (size_t)n_q * ws.ns_stride * 4 : 0));
+  ws.samples = (uint16_t*)(p + off);
+  off = align256(off + (max_blocks > kCandCap ? (size_t)n_q * ws.ns_stride * 2 : 0));
   ws.bytes = off;
   return ws;
 }
@@ -491,7 +612,7 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
   hipStream_t st = (hipStream_t)stream;
 
   const bool small_tiles = max_q_len <= 4;
-  const int qt = small_tiles ? 4 : 32;
+  const int qt = small_tiles ? 4 : 4 * kPrefillMT;
   const int64_t tiles_per_seq = (max_q_len + qt - 1) / qt;
   const int64_t gx = tiles_per_seq * n_seq;
   if (gx > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
@@ -502,41 +623,39 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
     const int cols = ws.ns_stride;
     dim3 grid((unsigned)gx, (cols + chunk - 1) / chunk);
     if (small_tiles)
-      hipLaunchKernelGGL((score_kernel<1, 4, true>), grid, dim3(256), 0, st, (const uint16_t*)idx_q,
+      hipLaunchKernelGGL((score_kernel<1, true>), grid, dim3(256), 0, st, (const uint16_t*)idx_q,
                          w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq, max_blocks,
                          (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh, ws.cnt,
                          ws.cand, ws.samples, ws.ns_stride);
     else
-      hipLaunchKernelGGL((score_kernel<8, 1, true>), grid, dim3(256), 0, st, (const uint16_t*)idx_q,
+      hipLaunchKernelGGL((score_kernel<kPrefillMT, true>), grid, dim3(256), 0, st, (const uint16_t*)idx_q,
                          w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq, max_blocks,
                          (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh, ws.cnt,
                          ws.cand, ws.samples, ws.ns_stride);
   }
-  // 2. thresholds (also zero the list counters and the fallback counter)
+  // 2. thresholds (also preset the list counters)
   hipLaunchKernelGGL(threshold_kernel, dim3(n_q), dim3(256), 0, st, cu_q, seq_len, n_seq,
-                     max_blocks, budget, ws.samples, ws.ns_stride, ws.thresh, ws.cnt, ws.fb_count);
+                     max_blocks, budget, ws.samples, ws.ns_stride, ws.thresh, ws.cnt);
   // 3. filter pass
   if (max_blocks > 0) {
     dim3 grid((unsigned)gx, (max_blocks + chunk - 1) / chunk);
     if (grid.y > 65535) return QSA_ERR_UNSUPPORTED;
     if (small_tiles)
-      hipLaunchKernelGGL((score_kernel<1, 4, false>), grid, dim3(256), 0, st,
+      hipLaunchKernelGGL((score_kernel<1, false>), grid, dim3(256), 0, st,
                          (const uint16_t*)idx_q, w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq,
                          max_blocks, (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh,
                          ws.cnt, ws.cand, ws.samples, ws.ns_stride);
     else
-      hipLaunchKernelGGL((score_kernel<8, 1, false>), grid, dim3(256), 0, st,
+      hipLaunchKernelGGL((score_kernel<kPrefillMT, false>), grid, dim3(256), 0, st,
                          (const uint16_t*)idx_q, w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq,
                          max_blocks, (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh,
                          ws.cnt, ws.cand, ws.samples, ws.ns_stride);
   }
-  // 4. exact select per row
-  hipLaunchKernelGGL(final_select_kernel, dim3(n_q), dim3(256), 0, st, cu_q, seq_len, n_seq,
-                     max_blocks, budget, ws.cnt, ws.cand, sel, sel_count, ws.fb_count, ws.fb_list);
-  // 5. fallback for rows whose list was short or overflowed
-  hipLaunchKernelGGL(fallback_kernel, dim3(kFallbackWGs), dim3(256), 0, st, (const uint16_t*)idx_q,
-                     w, cu_q, seq_len, n_seq, max_blocks, budget, (const uint16_t*)block_keys,
-                     bk_seq_stride, ws.fb_count, ws.fb_list, sel, sel_count);
+  // 4. exact select per row (rows whose list came out short or overflowed
+  //    are selected exactly by recomputing their scores)
+  hipLaunchKernelGGL(final_select_kernel, dim3(n_q), dim3(256), 0, st, (const uint16_t*)idx_q, w,
+                     cu_q, seq_len, n_seq, max_blocks, budget, (const uint16_t*)block_keys,
+                     bk_seq_stride, ws.cnt, ws.cand, sel, sel_count);
   return launch_status();
 }
 

@@ -27,13 +27,15 @@
 // storage, rare).
 #include <math.h>
 
+#include <type_traits>
+
 #include "qsa_common.hpp"
 
 namespace qsa {
 
-// m-tiles (of 4 queries x 4 heads) per workgroup in the prefill score GEMM
+// m-tiles (of 4 queries x 4 heads) per wave in the prefill score GEMM
 #ifndef QSA_PREFILL_MT
-#define QSA_PREFILL_MT 6
+#define QSA_PREFILL_MT 2
 #endif
 constexpr int kPrefillMT = QSA_PREFILL_MT;
 // waves per SIMD the prefill score GEMM is compiled for
@@ -307,6 +309,255 @@ score_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
       for (int i = threadIdx.x; i < n; i += 256) {
         const int slot = s_base[j] + i;
         if (slot < kCandCap) cand[(int64_t)(row0 + j) * kCandCap + slot] = s_buf[j][i];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------- prefill GEMM
+// Prefill variant of the score GEMM: workgroup = 16*MT queries (4 waves, each
+// owning MT m-tiles of 16 rows = 4 queries x 4 heads) x a chunk of columns.
+// Block keys go through a 2-stage LDS ring of 64 columns (16 KB) shared by
+// the 4 waves: every thread loads 4 chunks of 16 bytes of the next stage into
+// registers while the current stage is multiplied, then writes them to LDS
+// (each wave instruction covers a 1 KB run of 4 columns).  Inside a stage,
+// chunk q (16 bytes) of column c sits at chunk slot q ^ (c % 16), which makes
+// the MFMA B-fragment reads (16 columns x one chunk) hit 16 distinct bank
+// groups.
+//
+// Filter epilogue.  About 1% of candidates reach the threshold, so almost
+// every stage has a hit somewhere; handling hits in the SIMT stream would cost
+// more than the MFMAs.  The stream therefore only (1) evaluates the cheap
+// pre-filter and takes its compare mask as a wave ballot, and (2) for the few
+// (tile, m-tile) pairs with a set bit, appends the raw 4-head accumulators and
+// the block id to a per-row LDS pending list.  The defined float32 score and
+// the exact tau test run once per workgroup over the pending lists, one entry
+// per lane.
+constexpr int kStageCols = 64;
+constexpr int kPending = 16;        // pending pre-filter passes per row and workgroup
+
+template <int MT, bool kSample>
+__global__ void __launch_bounds__(256, 3)
+score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
+                  const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
+                  int n_seq, int n_q, int tiles_per_seq, int max_blocks,
+                  const uint16_t* __restrict__ bk, int64_t bk_stride, int chunk_cols,
+                  const uint32_t* __restrict__ thresh, int32_t* __restrict__ cnt,
+                  u32x2* __restrict__ cand, uint16_t* __restrict__ samples, int ns_stride) {
+  constexpr int QT = 16 * MT;
+  constexpr int stride = kSample ? kSampleStride : 1;
+  constexpr int kPend = kSample ? 1 : kPending;
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[2][kStageCols * kIdxDim];
+  __shared__ float s_w[QT][4];
+  __shared__ f32x4 s_wc[QT];
+  __shared__ float s_tlo[QT];
+  __shared__ int s_nc[QT];
+  __shared__ uint32_t s_th[QT];
+  __shared__ int s_pcnt[QT];
+  __shared__ f32x4 s_pacc[QT][kPend];
+  __shared__ int s_pidx[QT][kPend];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int s = blockIdx.x / tiles_per_seq, t = blockIdx.x % tiles_per_seq;
+  const int qb = cu_q[s], qe_raw = cu_q[s + 1];
+  const int qe = min(qe_raw, n_q);
+  const int row0 = qb + t * QT;
+  if (row0 >= qe || row0 < 0) return;
+  const int pos0 = seq_len[s] - (qe_raw - qb) + t * QT;
+  const int n_rows = min(QT, qe - row0);
+  const int nc_last = (pos0 + n_rows) >> 2;
+  if (nc_last > max_blocks) return;
+  const int max_cols = kSample ? (nc_last + stride - 1) / stride : nc_last;
+  const int v0 = blockIdx.y * chunk_cols;
+  if (v0 >= max_cols) return;
+  if (kSample && nc_last <= kCandCap) return;
+  const int v1 = min(v0 + chunk_cols, max_cols);
+  const bool collect_all = !kSample && nc_last <= kCandCap;
+
+  if (threadIdx.x < QT) {
+    const int j = threadIdx.x;
+    const bool ok = j < n_rows;
+    const int rj = min(row0 + j, qe - 1);
+    const int nc = ok ? (pos0 + j + 1) >> 2 : 0;
+    s_nc[j] = (kSample && nc <= kCandCap) ? 0 : nc;
+    const uint32_t th = kSample ? 0u : thresh[rj];
+    s_th[j] = ok && !kSample ? th : 0xFFFFFFFFu;
+    s_pcnt[j] = 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float wv = w[(int64_t)rj * 4 + h];
+      s_w[j][h] = ok ? wv : 0.f;
+      s_wc[j][h] = ok ? wv * kScoreScale : 0.f;
+    }
+    // same pre-filter bound as score_kernel
+    const float tau = __uint_as_float(s_th[j]);
+    s_tlo[j] = (!ok || kSample) ? INFINITY
+                                : (nc <= kCandCap ? -1.f : tau * (1.f - 0x1p-19f) - 0x1p-100f);
+  }
+
+  // A fragments of this wave's m-tiles (rows (wave*MT + mt)*16 + col)
+  u32x4 af[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int j = (wave * MT + mt) * 4 + (col >> 2);
+    const bool ok = j < n_rows;
+    const int rj = min(row0 + j, qe - 1);
+    const uint16_t* src = idx_q + ((int64_t)rj * 4 + (col & 3)) * kIdxDim + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 v = ldg16(src + 32 * ks);
+      af[mt][ks] = ok ? v : u32x4{0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
+  f32x4 r_wc[MT];
+  float r_tlo[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    r_wc[mt] = s_wc[(wave * MT + mt) * 4 + grp];
+    r_tlo[mt] = s_tlo[(wave * MT + mt) * 4 + grp];
+  }
+
+  const uint16_t* bseq = bk + (int64_t)s * bk_stride;
+  const int n_stages = (v1 - v0 + kStageCols - 1) / kStageCols;
+  // This thread carries 4 chunks of a stage: column c = 16*wave + 4*i +
+  // lane/16, chunk slot lane%16, which holds chunk (lane%16) ^ (c%16).
+  auto load_stage = [&](u32x4 (&r)[4], int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * wave + 4 * i + (lane >> 4);
+      const int q = (lane & 15) ^ (c & 15);
+      const int vcol = min(v0 + st * kStageCols + c, v1 - 1);
+      r[i] = ldg16(bseq + (int64_t)vcol * stride * kIdxDim + q * 8);
+    }
+  };
+  auto store_stage = [&](const u32x4 (&r)[4], int st) {
+    uint16_t* dst = s_b[st & 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * wave + 4 * i + (lane >> 4);
+      *(u32x4*)(dst + c * kIdxDim + (lane & 15) * 8) = r[i];
+    }
+  };
+  // the defined score of row j for block b, and where it goes
+  auto emit_exact = [&](const f32x4& acc, int j, int vcol, int b) {
+    const int nc = s_nc[j];
+    if (!(vcol < v1 && b < nc)) return;
+    const uint32_t key = __float_as_uint(block_score(acc, s_w[j]));
+    const int64_t rbase = (int64_t)(row0 + j) * kCandCap;
+    if (kSample) {
+      samples[(int64_t)(row0 + j) * ns_stride + vcol] = (uint16_t)(key >> 16);
+    } else if (nc <= kCandCap) {
+      cand[rbase + b] = u32x2{key, (uint32_t)b};
+    } else if (key >= s_th[j]) {
+      const int g = atomicAdd(&cnt[row0 + j], 1);
+      if (g < kCandCap) cand[rbase + g] = u32x2{key, (uint32_t)b};
+    }
+  };
+
+  // One stage = 4 column tiles, explicitly pipelined: the B fragments of
+  // tile t+1 are read from LDS before the MFMAs of tile t are issued, and the
+  // epilogue of tile t runs after the MFMAs of tile t+1 are in flight.
+  auto read_b = [&](const uint16_t* sb, int ct, u32x4 (&bf)[4]) {
+    const int c = 16 * ct + col;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      bf[ks] = *(const u32x4*)(sb + c * kIdxDim + (((grp + 4 * ks) ^ col) * 8));
+  };
+  auto mfma_b = [&](const u32x4 (&bf)[4], f32x4 (&acc)[MT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc[mt] = mfma_16x16x32(af[mt][ks], bf[ks], acc[mt]);
+    }
+  };
+  auto epi = [&](auto filter_tag, const f32x4 (&acc)[MT], int vbase) {
+    constexpr bool kFilter = decltype(filter_tag)::value;
+    const int vcol = vbase + col;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int j = (wave * MT + mt) * 4 + grp;
+      if (!kFilter) {
+        emit_exact(acc[mt], j, vcol, vcol * stride);
+        continue;
+      }
+      const f32x4 wc = r_wc[mt];
+      float fast = relu_bits(acc[mt][3]) * wc[3];
+      fast = fmaf(relu_bits(acc[mt][2]), wc[2], fast);
+      fast = fmaf(relu_bits(acc[mt][1]), wc[1], fast);
+      fast = fmaf(relu_bits(acc[mt][0]), wc[0], fast);
+      const bool pass = fast >= r_tlo[mt];
+      if (__ballot(pass)) {                 // a few lanes: append raw accumulators
+        if (pass && vcol < v1 && vcol < s_nc[j]) {
+          const int slot = atomicAdd(&s_pcnt[j], 1);
+          if (slot < kPend) {
+            s_pacc[j][slot] = acc[mt];
+            s_pidx[j][slot] = vcol;
+          } else {
+            emit_exact(acc[mt], j, vcol, vcol);   // rare: list full
+          }
+        }
+      }
+    }
+  };
+  auto run = [&](auto filter_tag) {
+    u32x4 stage_regs[4];
+    load_stage(stage_regs, 0);
+    store_stage(stage_regs, 0);
+    __syncthreads();
+    for (int st = 0; st < n_stages; ++st) {
+      const bool more = st + 1 < n_stages;
+      if (more) load_stage(stage_regs, st + 1);          // in flight during this stage
+      const uint16_t* sb = s_b[st & 1];
+      const int cbase = v0 + st * kStageCols;
+      u32x4 b0[4], b1[4];
+      f32x4 a0[MT], a1[MT];
+      read_b(sb, 0, b0);
+      read_b(sb, 1, b1);
+      mfma_b(b0, a0);                       // tile 0
+      read_b(sb, 2, b0);
+      mfma_b(b1, a1);                       // tile 1
+      epi(filter_tag, a0, cbase);
+      read_b(sb, 3, b1);
+      mfma_b(b0, a0);                       // tile 2
+      epi(filter_tag, a1, cbase + 16);
+      mfma_b(b1, a1);                       // tile 3
+      epi(filter_tag, a0, cbase + 32);
+      epi(filter_tag, a1, cbase + 48);
+      if (more) store_stage(stage_regs, st + 1);
+      __syncthreads();   // stage st+1 visible; stage st's buffer free for st+2
+    }
+  };
+  if (kSample || collect_all) run(std::false_type{});
+  else run(std::true_type{});
+
+  if (!kSample && !collect_all) {
+    // exact score of every pending entry; each wave takes rows wave, wave+4, ...
+    for (int j = wave; j < QT; j += 4) {
+      const int n = min(s_pcnt[j], kPend);
+      uint32_t key = 0;
+      bool take = false;
+      int b = 0;
+      if (lane < n) {
+        key = __float_as_uint(block_score(s_pacc[j][lane], s_w[j]));
+        b = s_pidx[j][lane];
+        take = key >= s_th[j];
+      }
+      if (s_nc[j] <= kCandCap) {
+        // a row that keeps every candidate (mixed tile): slot = block id
+        if (lane < n) cand[(int64_t)(row0 + j) * kCandCap + b] = u32x2{key, (uint32_t)b};
+        continue;
+      }
+      const unsigned long long m = __ballot(take);
+      if (m) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&cnt[row0 + j], __popcll(m));
+        base = __shfl(base, 0, 64);
+        const int rank = __popcll(m & ((1ull << lane) - 1ull));
+        if (take && base + rank < kCandCap)
+          cand[(int64_t)(row0 + j) * kCandCap + base + rank] = u32x2{key, (uint32_t)b};
       }
     }
   }
@@ -612,11 +863,11 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
   hipStream_t st = (hipStream_t)stream;
 
   const bool small_tiles = max_q_len <= 4;
-  const int qt = small_tiles ? 4 : 4 * kPrefillMT;
+  const int qt = small_tiles ? 4 : 16 * kPrefillMT;
   const int64_t tiles_per_seq = (max_q_len + qt - 1) / qt;
   const int64_t gx = tiles_per_seq * n_seq;
   if (gx > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
-  const int chunk = small_tiles ? 512 : 2048;
+  const int chunk = small_tiles ? 512 : 1024;
 
   // 1. sample pass (only rows with more than kCandCap candidates need it)
   if (max_blocks > kCandCap) {
@@ -628,7 +879,7 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
                          (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh, ws.cnt,
                          ws.cand, ws.samples, ws.ns_stride);
     else
-      hipLaunchKernelGGL((score_kernel<kPrefillMT, true>), grid, dim3(256), 0, st, (const uint16_t*)idx_q,
+      hipLaunchKernelGGL((score_gemm_kernel<kPrefillMT, true>), grid, dim3(256), 0, st, (const uint16_t*)idx_q,
                          w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq, max_blocks,
                          (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh, ws.cnt,
                          ws.cand, ws.samples, ws.ns_stride);
@@ -646,7 +897,7 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
                          max_blocks, (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh,
                          ws.cnt, ws.cand, ws.samples, ws.ns_stride);
     else
-      hipLaunchKernelGGL((score_kernel<kPrefillMT, false>), grid, dim3(256), 0, st,
+      hipLaunchKernelGGL((score_gemm_kernel<kPrefillMT, false>), grid, dim3(256), 0, st,
                          (const uint16_t*)idx_q, w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq,
                          max_blocks, (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh,
                          ws.cnt, ws.cand, ws.samples, ws.ns_stride);

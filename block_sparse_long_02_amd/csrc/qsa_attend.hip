@@ -23,6 +23,10 @@
 
 namespace qsa {
 
+#ifndef QSA_ATTEND_XCD_REMAP
+#define QSA_ATTEND_XCD_REMAP 0
+#endif
+
 constexpr int kTileMB = 8;                    // micro-blocks per tile
 constexpr int kWaves = 4;
 constexpr int kMaxList = kMaxBudget + 1;      // selected blocks + tail block
@@ -68,7 +72,15 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
 
+  // Optionally remap workgroup ids so that each of the 8 XCDs (dispatched
+  // round-robin, each with its own L2) works on a contiguous range of rows.
+  // Off by default: measured slower, since most reuse of the gathered blocks
+  // comes from the shared MALL, which favours all XCDs working on nearby rows.
+#if QSA_ATTEND_XCD_REMAP
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+#else
   const int wg = blockIdx.x;
+#endif
   const int split = wg % n_splits;
   const int g = (wg / n_splits) & 1;
   const int row = wg / (2 * n_splits);
@@ -165,8 +177,8 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   for (int t = t_begin; t < t_end; ++t) {
     const int base = t * kTileMB;
     // K rows: lane is token row `col` of each 16-token half
-    const int sk0 = base + (col >> 2), sk1 = base + 4 + (col >> 2);
-    const int idk0 = sh.list[min(sk0, n_mb - 1)], idk1 = sh.list[min(sk1, n_mb - 1)];
+    const int idk0 = sh.list[min(base + (col >> 2), n_mb - 1)];
+    const int idk1 = sh.list[min(base + 4 + (col >> 2), n_mb - 1)];
     // V / P k-slices: micro-blocks base+grp and base+4+grp
     const int sv0 = base + grp, sv1 = base + 4 + grp;
     const int idv0 = sh.list[min(sv0, n_mb - 1)], idv1 = sh.list[min(sv1, n_mb - 1)];
@@ -188,12 +200,21 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
       s1 = mfma_16x16x32(kb[ks], qf[ks], s1);
     }
     // s0[i]: token i of micro-block slot sv0, head col; s1[i]: slot sv1.
-    const bool v0 = sv0 < n_mb, v1 = sv1 < n_mb;
-    {
-      // Cache rows past the query inside the tail block (and padding slots)
-      // may hold anything: zero their V so that p = 0 cannot meet a NaN.
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[i] = s0[i] * scale; x[4 + i] = s1[i] * scale; }
+    if (base + kTileMB > cnt) {
+      // the tile holds the tail block and/or padding slots (uniform branch)
+      const bool v0 = sv0 < n_mb, v1 = sv1 < n_mb;
       const int n0 = !v0 ? 0 : (sv0 == tail_slot ? tail_len : 4);
       const int n1 = !v1 ? 0 : (sv1 == tail_slot ? tail_len : 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = i < n0 ? x[i] : -INFINITY;
+        x[4 + i] = i < n1 ? x[4 + i] : -INFINITY;
+      }
+      // Cache rows past the query inside the tail block (and padding slots)
+      // may hold anything: zero their V so that p = 0 cannot meet a NaN.
       const uint32_t a01 = (n0 > 0 ? 0xFFFFu : 0u) | (n0 > 1 ? 0xFFFF0000u : 0u);
       const uint32_t a23 = (n0 > 2 ? 0xFFFFu : 0u) | (n0 > 3 ? 0xFFFF0000u : 0u);
       const uint32_t b01 = (n1 > 0 ? 0xFFFFu : 0u) | (n1 > 1 ? 0xFFFF0000u : 0u);
@@ -204,38 +225,34 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
         vb[c][0] &= b01; vb[c][1] &= b23; vb[c][2] &= b01; vb[c][3] &= b23;
       }
     }
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok0 = v0 && (sv0 != tail_slot || i < tail_len);
-      const bool ok1 = v1 && (sv1 != tail_slot || i < tail_len);
-      x[i] = ok0 ? s0[i] * scale : -INFINITY;
-      x[4 + i] = ok1 ? s1[i] * scale : -INFINITY;
-    }
     float mt = x[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);   // 0 on the first tile
+    // Lazy rescale: the reference max m_run only moves when a head's tile max
+    // exceeds it by more than 2^8, so p <= 256 and the float32 sums stay
+    // exact-enough; the 64 output rescales run only on those tiles.
+    if (__ballot(mt > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
+      l_run *= alpha;
+      m_run = m_new;
+      float a_row[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a_row[i] = __shfl(alpha, 4 * grp + i, 64);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[n][i] *= a_row[i];
+      }
+    }
     float p[8], ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { p[i] = exp2f(x[i] - m_new); ps += p[i]; }
+    for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - m_run); ps += p[i]; }
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-
-    // output rows are heads 4*grp + i: fetch their rescale factors
-    float a_row[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a_row[i] = __shfl(alpha, 4 * grp + i, 64);
-#pragma unroll
-    for (int n = 0; n < 16; ++n) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[n][i] *= a_row[i];
-    }
+    l_run += ps;
 
     u32x4 pa;
     pa[0] = pack_bf16x2(p[0], p[1]);

@@ -55,6 +55,16 @@ __device__ __forceinline__ double rope_inv_freq(int j) {
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
 
+// Map a hardware workgroup id (dispatched round-robin over the 8 XCDs of an
+// MI355X) to a logical id such that each XCD receives a contiguous range of
+// logical ids.  A bijection on [0, n): the first (n % 8) XCDs take one extra.
+__device__ __forceinline__ int xcd_remap(int hw, int n) {
+  constexpr int kXcds = 8;
+  const int xcd = hw % kXcds, k = hw / kXcds;
+  const int q = n / kXcds, r = n % kXcds;
+  return xcd * q + min(xcd, r) + k;
+}
+
 // --------------------------------------------------------- block helpers
 // Exclusive prefix sum over a 256-thread workgroup.  `tmp` holds >= 4 ints of
 // LDS.  Returns the exclusive prefix of `v`; `total` receives the sum.

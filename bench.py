@@ -120,26 +120,37 @@ def time_decode(args):
     t0 = time.time()
     b = W.decode_128k(device="cuda")
     r = QSARunner(b)
-    flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")   # 512 MB > MALL
+    # 512 MB > MALL, swept by a read before each step so that the step starts
+    # with none of its data cached and no dirty lines to write back
+    flush = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     log(f"decode workload ready in {time.time() - t0:.1f}s")
     for _ in range(args.warmup):
         r.step()
-    steps = []
-    for _ in range(args.steps):
-        flush.fill_(1)
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        e0.record()
-        r.pool()
-        r.select()
-        e1.record()
-        r.attend()
-        e2.record()
-        steps.append((e0, e1, e2))
+    # a decode step is replayed from a HIP graph, as a serving loop would;
+    # the stage split comes from two partial graphs timed the same way
+    g_step = r.capture()
+    g_sel = r.capture(("pool", "select"))
+    g_att = r.capture(("attend",))
     torch.cuda.synchronize()
-    sel_ms = sum(a.elapsed_time(b_) for a, b_, _ in steps) / len(steps)
-    att_ms = sum(b_.elapsed_time(c) for _, b_, c in steps) / len(steps)
-    ms = sel_ms + att_ms
+
+    def timed(graphs):
+        evs = []
+        for _ in range(args.steps):
+            flush.sum()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(len(graphs) + 1)]
+            e[0].record()
+            for i, g in enumerate(graphs):
+                g.replay()
+                e[i + 1].record()
+            evs.append(e)
+        torch.cuda.synchronize()
+        return [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / len(evs) for i in range(len(graphs))]
+
+    for g in (g_step, g_sel, g_att):
+        g.replay()
+    ms = timed([g_step])[0]
+    sel_ms, att_ms = timed([g_sel, g_att])
     sum_s, sum_nc = set_sizes(r)
     n_seq = r.n_seq
     step_bytes = sum_nc * BLOCK_KEY_BYTES + sum_s * TOKEN_GATHER_BYTES + n_seq * (

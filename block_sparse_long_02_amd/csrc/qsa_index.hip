@@ -38,11 +38,6 @@ namespace qsa {
 #define QSA_PREFILL_MT 2
 #endif
 constexpr int kPrefillMT = QSA_PREFILL_MT;
-// waves per SIMD the prefill score GEMM is compiled for
-#ifndef QSA_SCORE_WAVES
-#define QSA_SCORE_WAVES 2
-#endif
-constexpr int kScoreWaves = QSA_SCORE_WAVES;
 constexpr int kCandCap = 4096;      // list capacity per row
 constexpr int kSampleStride = 16;   // every 16th block is sampled
 constexpr int kSampleExtra = 1536;  // aimed-for surplus of list entries over K
@@ -94,221 +89,100 @@ __device__ __forceinline__ float block_score(f32x4 acc, const float* __restrict_
   return s == 0.f ? 0.f : s;   // canonical +0
 }
 
-// ----------------------------------------------------------- score GEMM
-// Workgroup = one tile of 4*MT query rows of one sequence x a chunk of
-// `chunk_cols` virtual columns.  Virtual column v is block v*stride (stride 16
-// in the sample pass, 1 in the filter pass).  A row r = 4*(query) + head of the
-// tile is MFMA row r%16 of m-tile r/16; each wave takes every 4th 16-column
-// tile and software-pipelines them (see the main loop).
-//
-// Filter-pass output per row:
-//   * rows with n_c <= kCandCap keep every candidate: entry b goes to slot b
-//     (no atomics; the threshold kernel already set the count to n_c);
-//   * other rows append (key, b) for key >= tau: hits are staged in LDS and
-//     each workgroup reserves its slots with one global atomic per row.
-template <int MT>
-struct ScoreStage {
-  static constexpr int kCap = MT == 1 ? 1024 : 128;   // staged hits per row
-};
+// ----------------------------------------------------- dense scores (decode)
+// Small tiles (at most 4 queries per sequence, i.e. decode and multi-token
+// decode): the score of every candidate is written out.  That costs 4 bytes
+// per block against the 256-byte block key the kernel must stream anyway, and
+// lets the select read scores instead of recomputing them; every 16th score
+// also goes to a contiguous sample row.  Workgroup = one
+// sequence's queries (m-tile rows 4*query + head) x kDenseChunk columns; wave
+// w takes the 16-column tiles w, w+4, ...  The tile loop is fully unrolled so
+// that kDenseDepth tiles of keys stay in flight with exact wait counts, and
+// the scores are stored after the last tile.
+constexpr int kDenseChunk = 1024;
+constexpr int kDenseTiles = kDenseChunk / 64;   // tiles per wave
+constexpr int kDenseDepth = 4;
 
-template <int MT, bool kSample>
-__global__ void __launch_bounds__(256, MT == 1 ? 4 : kScoreWaves)
-score_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
-             const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len, int n_seq,
-             int n_q, int tiles_per_seq, int max_blocks, const uint16_t* __restrict__ bk,
-             int64_t bk_stride, int chunk_cols, const uint32_t* __restrict__ thresh,
-             int32_t* __restrict__ cnt, u32x2* __restrict__ cand,
-             uint16_t* __restrict__ samples, int ns_stride) {
-  constexpr int QT = 4 * MT;
-  constexpr int stride = kSample ? kSampleStride : 1;
-  constexpr int kCapL = kSample ? 1 : ScoreStage<MT>::kCap;
-  __shared__ float s_w[QT][4];
-  __shared__ f32x4 s_wc[QT];      // w_h * (1/sqrt(128)) for the pre-filter
-  __shared__ float s_tlo[QT];     // pre-filter threshold, a little below tau
-  __shared__ int s_nc[QT];
-  __shared__ uint32_t s_th[QT];
-  __shared__ int s_cnt[QT];
-  __shared__ int s_base[QT];
-  __shared__ u32x2 s_buf[QT][kCapL];
-
+__global__ void __launch_bounds__(256, 4)
+score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
+                   const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
+                   int n_q, int max_blocks, const uint16_t* __restrict__ bk, int64_t bk_stride,
+                   uint32_t* __restrict__ dense, int64_t dense_stride,
+                   uint32_t* __restrict__ dsmp, int64_t dsmp_stride) {
+  __shared__ float s_w[4][4];
+  __shared__ int s_nc[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int s = blockIdx.x / tiles_per_seq, t = blockIdx.x % tiles_per_seq;
+  const int s = blockIdx.x;
   const int qb = cu_q[s], qe_raw = cu_q[s + 1];
-  const int qe = min(qe_raw, n_q);                    // rows past n_q are never touched
-  const int row0 = qb + t * QT;
-  if (row0 >= qe || row0 < 0) return;
-  const int pos0 = seq_len[s] - (qe_raw - qb) + t * QT;   // position of row0
-  const int n_rows = min(QT, qe - row0);
-  // candidates of the tile's last row bound every row's
-  const int nc_last = (pos0 + n_rows) >> 2;
-  if (nc_last > max_blocks) return;                   // reported by the final select
-  const int max_cols = kSample ? (nc_last + stride - 1) / stride : nc_last;
-  const int v0 = blockIdx.y * chunk_cols;
-  if (v0 >= max_cols) return;
-  if (kSample && nc_last <= kCandCap) return;          // no row of the tile samples
-  const int v1 = min(v0 + chunk_cols, max_cols);
-
-  if (threadIdx.x < QT) {
+  const int qe = min(qe_raw, n_q);
+  if (qb >= qe || qb < 0) return;
+  const int pos0 = seq_len[s] - (qe_raw - qb);
+  const int n_rows = min(4, qe - qb);
+  // rows with more than max_blocks candidates are reported by the select;
+  // the others still need every score
+  const int nc_last = min((pos0 + n_rows) >> 2, max_blocks);
+  const int v0 = blockIdx.y * kDenseChunk;
+  if (v0 >= nc_last) return;
+  const int v1 = min(v0 + kDenseChunk, nc_last);
+  if (threadIdx.x < 4) {
     const int j = threadIdx.x;
     const bool ok = j < n_rows;
-    const int rj = min(row0 + j, qe - 1);             // in-bounds address for padding rows
-    const int nc = ok ? (pos0 + j + 1) >> 2 : 0;
-    s_nc[j] = (kSample && nc <= kCandCap) ? 0 : nc;    // sample only rows that need it
-    const uint32_t th = kSample ? 0u : thresh[rj];
-    s_th[j] = ok && !kSample ? th : 0xFFFFFFFFu;
-    s_cnt[j] = 0;
+    const int rj = min(qb + j, qe - 1);
+    s_nc[j] = ok ? (pos0 + j + 1) >> 2 : 0;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const float wv = w[(int64_t)rj * 4 + h];
       s_w[j][h] = ok ? wv : 0.f;
-      s_wc[j][h] = ok ? wv * kScoreScale : 0.f;
     }
-    // Pre-filter bound.  The defined score and the fast one (fma chain with
-    // w*c folded in) both round non-negative terms a handful of times, so each
-    // lies within 2^-21 (relative) of c * sum_h w_h ReLU(t_h); a candidate
-    // with score >= tau therefore has fast score >= tau * (1 - 2^-19); the
-    // absolute 2^-100 covers rounding at subnormal scale.  Rows that keep
-    // every candidate pass everything (-1).
-    const float tau = __uint_as_float(s_th[j]);
-    s_tlo[j] = (!ok || kSample) ? INFINITY
-                                : (nc <= kCandCap ? -1.f : tau * (1.f - 0x1p-19f) - 0x1p-100f);
   }
-
-  // A fragments: m-tile mt, k-step ks -> row mt*16 + col (query mt*4 + col/4,
-  // head col%4), dims 32*ks + 8*grp .. +7.
-  u32x4 af[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int j = mt * 4 + (col >> 2);
-    const bool ok = j < n_rows;
-    const int rj = min(row0 + j, qe - 1);
+  // A fragment: row col = 4*query + head, dims 32*ks + 8*grp .. +7
+  u32x4 af[4];
+  {
+    const int j = col >> 2;
+    const int rj = min(qb + j, qe - 1);
     const uint16_t* src = idx_q + ((int64_t)rj * 4 + (col & 3)) * kIdxDim + 8 * grp;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const u32x4 v = ldg16(src + 32 * ks);
-      af[mt][ks] = ok ? v : u32x4{0, 0, 0, 0};
+      af[ks] = j < n_rows ? v : u32x4{0, 0, 0, 0};
     }
   }
-  __syncthreads();
-
-  const bool collect_all = !kSample && nc_last <= kCandCap;
   const uint16_t* bseq = bk + (int64_t)s * bk_stride;
-  // exact score of m-tile mt's row for this lane's block, and where it goes
-  auto emit_exact = [&](const f32x4& acc, int mt, int vcol, int b) {
-    const int j = mt * 4 + grp;
-    const int nc = s_nc[j];
-    if (!(vcol < v1 && b < nc)) return;
-    const uint32_t key = __float_as_uint(block_score(acc, s_w[j]));
-    const int64_t rbase = (int64_t)(row0 + j) * kCandCap;
-    if (kSample) {
-      samples[(int64_t)(row0 + j) * ns_stride + vcol] = (uint16_t)(key >> 16);
-    } else if (nc <= kCandCap) {
-      cand[rbase + b] = u32x2{key, (uint32_t)b};
-    } else if (key >= s_th[j]) {
-      const int slot = atomicAdd(&s_cnt[j], 1);
-      if (slot < kCapL) {
-        s_buf[j][slot] = u32x2{key, (uint32_t)b};
-      } else {                                          // rare: LDS stage full
-        const int g = atomicAdd(&cnt[row0 + j], 1);
-        if (g < kCandCap) cand[rbase + g] = u32x2{key, (uint32_t)b};
-      }
-    }
-  };
-  // B fragments of the 16-column tile starting at c0 (clamped: in bounds)
-  auto load_tile = [&](u32x4 (&bf)[4], int c0) {
-    const int b = min(c0 + col, v1 - 1) * stride;
+  const int c0 = v0 + wave * 16;
+  // B fragment of tile t: column c0 + 64t + col (clamped in bounds past v1)
+  auto load_tile = [&](u32x4 (&bf)[4], int t) {
+    const int b = min(c0 + 64 * t + col, v1 - 1);
     const uint16_t* src = bseq + (int64_t)b * kIdxDim + 8 * grp;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) bf[ks] = ldg16(src + 32 * ks);
   };
-  auto mfma_tile = [&](const u32x4 (&bf)[4], f32x4 (&acc)[MT]) {
+  u32x4 buf[kDenseDepth][4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < kDenseDepth; ++d) load_tile(buf[d], d);
+  __syncthreads();
+  // lane holds the 4 heads of query grp for block c0 + 64t + col
+  const int j = grp;
+  const float wr[4] = {s_w[j][0], s_w[j][1], s_w[j][2], s_w[j][3]};
+  const int nc_j = min(s_nc[j], v1);
+  float sc[kDenseTiles];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc[mt] = mfma_16x16x32(af[mt][ks], bf[ks], acc[mt]);
-    }
-  };
-  // pre-filter constants of this lane's rows, held in registers
-  f32x4 r_wc[MT];
-  float r_tlo[MT];
+  for (int t = 0; t < kDenseTiles; ++t) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    r_wc[mt] = s_wc[mt * 4 + grp];
-    r_tlo[mt] = s_tlo[mt * 4 + grp];
+    for (int ks = 0; ks < 4; ++ks) acc = mfma_16x16x32(af[ks], buf[t % kDenseDepth][ks], acc);
+    if (t + kDenseDepth < kDenseTiles) load_tile(buf[t % kDenseDepth], t + kDenseDepth);
+    sc[t] = block_score(acc, wr);
   }
-  auto epilogue = [&](const f32x4 (&acc)[MT], int c0) {
-    const int vcol = c0 + col;
-    const int b = vcol * stride;
-    if (kSample || collect_all) {
+  if (j < n_rows) {
+    uint32_t* drow = dense + (int64_t)(qb + j) * dense_stride;
+    uint32_t* srow = dsmp + (int64_t)(qb + j) * dsmp_stride;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) emit_exact(acc[mt], mt, vcol, b);
-    } else {
-      // branch-free conservative pre-filter for every m-tile (columns past
-      // the row's candidates may pass; emit_exact drops them)
-      uint32_t pass_bits = 0;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const f32x4 wc = r_wc[mt];
-        float fast = relu_bits(acc[mt][3]) * wc[3];
-        fast = fmaf(relu_bits(acc[mt][2]), wc[2], fast);
-        fast = fmaf(relu_bits(acc[mt][1]), wc[1], fast);
-        fast = fmaf(relu_bits(acc[mt][0]), wc[0], fast);
-        pass_bits |= (fast >= r_tlo[mt] ? 1u : 0u) << mt;
-      }
-      if (__ballot(pass_bits != 0)) {                   // rare: exact arithmetic
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          if (pass_bits & (1u << mt)) emit_exact(acc[mt], mt, vcol, b);
-      }
-    }
-  };
-
-  // Software pipeline over this wave's column tiles c, c+64, c+128, ...:
-  // the MFMAs of tile t+1 are issued before the epilogue of tile t, and the
-  // block keys of tile t+2 are in flight meanwhile.
-  {
-    u32x4 bX[4], bY[4];
-    f32x4 aX[MT], aY[MT];
-    int c = v0 + wave * 16;
-    if (c < v1) {
-      load_tile(bX, c);
-      load_tile(bY, c + 64);
-      mfma_tile(bX, aX);                 // aX: tile c
-      load_tile(bX, c + 128);
-      for (;;) {
-        // aX = tile c, bY = tile c+64, bX = tile c+128 (in flight)
-        const int c1 = c + 64;
-        if (c1 < v1) mfma_tile(bY, aY);  // aY: tile c+64
-        epilogue(aX, c);
-        if (c1 >= v1) break;
-        load_tile(bY, c1 + 128);         // bY: tile c+192
-        const int c2 = c1 + 64;
-        if (c2 < v1) mfma_tile(bX, aX);  // aX: tile c+128
-        epilogue(aY, c1);
-        if (c2 >= v1) break;
-        load_tile(bX, c2 + 128);         // bX: tile c+256
-        c = c2;
-      }
-    }
-  }
-
-  if (!kSample) {
-    // flush staged hits: one global reservation per row
-    __syncthreads();
-    if (threadIdx.x < QT) {
-      const int j = threadIdx.x;
-      const int n = min(s_cnt[j], kCapL);
-      s_base[j] = n > 0 ? atomicAdd(&cnt[row0 + j], n) : 0;
-      s_cnt[j] = n;
-    }
-    __syncthreads();
-    for (int j = 0; j < QT; ++j) {
-      const int n = s_cnt[j];
-      for (int i = threadIdx.x; i < n; i += 256) {
-        const int slot = s_base[j] + i;
-        if (slot < kCandCap) cand[(int64_t)(row0 + j) * kCandCap + slot] = s_buf[j][i];
+    for (int t = 0; t < kDenseTiles; ++t) {
+      const int b = c0 + 64 * t + col;
+      if (b < nc_j) {
+        drow[b] = __float_as_uint(sc[t]);
+        if ((b & (kSampleStride - 1)) == 0) srow[b / kSampleStride] = __float_as_uint(sc[t]);
       }
     }
   }
@@ -366,8 +240,8 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
   if (row0 >= qe || row0 < 0) return;
   const int pos0 = seq_len[s] - (qe_raw - qb) + t * QT;
   const int n_rows = min(QT, qe - row0);
-  const int nc_last = (pos0 + n_rows) >> 2;
-  if (nc_last > max_blocks) return;
+  // rows beyond max_blocks are reported by the select; the others proceed
+  const int nc_last = min((pos0 + n_rows) >> 2, max_blocks);
   const int max_cols = kSample ? (nc_last + stride - 1) / stride : nc_last;
   const int v0 = blockIdx.y * chunk_cols;
   if (v0 >= max_cols) return;
@@ -390,7 +264,12 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
       s_w[j][h] = ok ? wv : 0.f;
       s_wc[j][h] = ok ? wv * kScoreScale : 0.f;
     }
-    // same pre-filter bound as score_kernel
+    // Pre-filter bound.  The defined score and the fast one (fma chain with
+    // w*c folded in) both round non-negative terms a handful of times, so each
+    // lies within 2^-21 (relative) of c * sum_h w_h ReLU(t_h); a candidate
+    // with score >= tau therefore has fast score >= tau * (1 - 2^-19); the
+    // absolute 2^-100 covers rounding at subnormal scale.  Rows that keep
+    // every candidate pass everything (-1).
     const float tau = __uint_as_float(s_th[j]);
     s_tlo[j] = (!ok || kSample) ? INFINITY
                                 : (nc <= kCandCap ? -1.f : tau * (1.f - 0x1p-19f) - 0x1p-100f);
@@ -723,6 +602,112 @@ __device__ void exact_select_recompute(const uint16_t* __restrict__ q4, const fl
   for (int i = k + threadIdx.x; i < budget; i += 256) out[i] = -1;
 }
 
+// ------------------------------------------------------ list selection
+// Exact top-k (score desc, block asc) of an unordered list of c >= k
+// candidates held in LDS (key[], idx[]), written to out[0..k) in ascending
+// block order and -1 up to budget.  Radix select on the score key, then on
+// the block id among ties at the threshold; bitonic sort of the k ids.
+__device__ void select_from_list(const uint32_t* key, const int* idx, int c, int k, int* ids,
+                                 int* n_out, int* hist, int* tmp, int* res,
+                                 int32_t* __restrict__ out, int budget) {
+  uint32_t tau = 0, iota_cut = 0xFFFFFFFFu;
+  const bool all = c == k;
+  if (threadIdx.x == 0) *n_out = 0;
+  if (!all) {
+    tau = block_kth_largest([&](int i, bool& in) { in = true; return key[i]; }, c, k, 31, hist,
+                            tmp, res);
+    int above = 0, ties = 0;
+    for (int i = threadIdx.x; i < c; i += 256) {
+      above += key[i] > tau;
+      ties += key[i] == tau;
+    }
+    int tot_above, tot_ties;
+    block_excl_scan_256(above, tmp, tot_above);
+    block_excl_scan_256(ties, tmp, tot_ties);
+    const int need = k - tot_above;
+    if (need < tot_ties) {
+      // the `need` lowest block ids among the ties: k-th largest of (2^22-1-id)
+      const uint32_t v = block_kth_largest(
+          [&](int i, bool& in) { in = key[i] == tau; return 0x3FFFFFu - (uint32_t)idx[i]; }, c,
+          need, 22, hist, tmp, res);
+      iota_cut = 0x3FFFFFu - v;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < c; i += 256) {
+    const uint32_t kk = key[i];
+    const bool take = all || kk > tau || (kk == tau && (uint32_t)idx[i] <= iota_cut);
+    if (take) {
+      const int slot = atomicAdd(n_out, 1);
+      if (slot < kMaxBudget) ids[slot] = idx[i];
+    }
+  }
+  __syncthreads();
+  for (int i = k + threadIdx.x; i < kMaxBudget; i += 256) ids[i] = 0x7FFFFFFF;
+  __syncthreads();
+  bitonic_sort_512(ids);
+  for (int i = threadIdx.x; i < budget; i += 256) out[i] = i < k ? ids[i] : -1;
+}
+
+// Sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Exact top-k over keys get(0..n) of items id(0..n) listed in ascending
+// block order: threshold tau = k-th largest key, then every key > tau and the
+// first ties in list order, emitted in that order (so ids stay ascending).
+// The 4 waves take contiguous quarters; ranks come from wave ballots.
+template <class Get, class Id>
+__device__ void select_ordered(Get get, Id id, int n, int k, int* hist, int* tmp, int* res,
+                               int* wcnt, int32_t* __restrict__ out, int budget) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t tau =
+      k >= n ? 0u : block_kth_largest([&](int i, bool& in) { in = true; return get(i); }, n, k, 31,
+                                      hist, tmp, res);
+  const int per = (n + 3) / 4;
+  const int s0 = min(n, wave * per), s1 = min(n, s0 + per);
+  int a = 0, t = 0;
+  for (int i = s0 + lane; i < s1; i += 64) {
+    const uint32_t key = get(i);
+    a += key > tau;
+    t += key == tau;
+  }
+  a = wave_sum(a);
+  t = wave_sum(t);
+  if (lane == 0) { wcnt[2 * wave] = a; wcnt[2 * wave + 1] = t; }
+  __syncthreads();
+  int need = k;   // ties to take, in list order: k - #above overall
+  for (int w2 = 0; w2 < 4; ++w2) need -= wcnt[2 * w2];
+  int tie_base = 0, out_base = 0;
+  for (int w2 = 0; w2 < wave; ++w2) {
+    const int tw = wcnt[2 * w2 + 1];
+    out_base += wcnt[2 * w2] + min(max(need - tie_base, 0), tw);
+    tie_base += tw;
+  }
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int r0 = s0; r0 < s1; r0 += 64) {
+    const int i = r0 + lane;
+    const bool valid = i < s1;
+    const uint32_t key = valid ? get(i) : 0u;
+    const bool is_above = valid && key > tau;
+    const bool is_tie = valid && key == tau;
+    const unsigned long long mt = __ballot(is_tie);
+    const bool take = is_above || (is_tie && tie_base + __popcll(mt & below) < need);
+    const unsigned long long mk = __ballot(take);
+    if (take) {
+      const int slot = out_base + __popcll(mk & below);
+      if (slot < k) out[slot] = id(i);
+    }
+    tie_base += __popcll(mt);
+    out_base += __popcll(mk);
+  }
+  for (int i = k + threadIdx.x; i < budget; i += 256) out[i] = -1;
+  __syncthreads();
+}
+
 // --------------------------------------------------------- final select
 struct SelectShared {
   uint32_t key[kCandCap];
@@ -764,46 +749,288 @@ final_select_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict_
     sh.key[i] = e[0];
     sh.idx[i] = (int)e[1];
   }
-  if (threadIdx.x == 0) sh.n_out = 0;
   __syncthreads();
-
-  uint32_t tau = 0, iota_cut = 0xFFFFFFFFu;
-  bool all = c == k;
-  if (!all) {
-    tau = block_kth_largest([&](int i, bool& in) { in = true; return sh.key[i]; }, c, k, 31,
-                            sh.hist, sh.tmp, sh.res);
-    // how many strictly above tau, how many equal
-    int above = 0, ties = 0;
-    for (int i = threadIdx.x; i < c; i += 256) {
-      above += sh.key[i] > tau;
-      ties += sh.key[i] == tau;
-    }
-    int tot_above, tot_ties;
-    block_excl_scan_256(above, sh.tmp, tot_above);
-    block_excl_scan_256(ties, sh.tmp, tot_ties);
-    const int need = k - tot_above;
-    if (need < tot_ties) {
-      // the `need` lowest block ids among the ties: k-th largest of (2^22-1-id)
-      const uint32_t v = block_kth_largest(
-          [&](int i, bool& in) { in = sh.key[i] == tau; return 0x3FFFFFu - (uint32_t)sh.idx[i]; },
-          c, need, 22, sh.hist, sh.tmp, sh.res);
-      iota_cut = 0x3FFFFFu - v;
-    }
-  }
-  for (int i = threadIdx.x; i < c; i += 256) {
-    const uint32_t kk = sh.key[i];
-    const bool take = all || kk > tau || (kk == tau && (uint32_t)sh.idx[i] <= iota_cut);
-    if (take) {
-      const int slot = atomicAdd(&sh.n_out, 1);
-      if (slot < kMaxBudget) sh.ids[slot] = sh.idx[i];
-    }
-  }
-  __syncthreads();
-  for (int i = k + threadIdx.x; i < kMaxBudget; i += 256) sh.ids[i] = 0x7FFFFFFF;
-  __syncthreads();
-  bitonic_sort_512(sh.ids);
-  for (int i = threadIdx.x; i < budget; i += 256) out[i] = i < k ? sh.ids[i] : -1;
+  select_from_list(sh.key, sh.idx, c, k, sh.ids, &sh.n_out, sh.hist, sh.tmp, sh.res, out, budget);
   if (threadIdx.x == 0) sel_count[row] = k;
+}
+
+// ---------------------------------------------------- dense select (decode)
+// One workgroup per row over the dense scores of score_dense_kernel:
+//   1. tau_s = the r-th largest sample (every 16th score), r chosen so that
+//      about K + 768 scores reach it (the samples are loaded first, so this
+//      overlaps the loads of the row);
+//   2. the scores >= tau_s are compacted, in block order, into an LDS list:
+//      32768 scores per pass are staged in LDS so that each thread owns 128
+//      consecutive scores; a block scan of the per-thread hit counts gives
+//      each thread its list offset;
+//   3. if the list holds >= K entries it holds the true top K (all of them
+//      score >= the K-th score >= tau_s); they are found exactly and emitted
+//      in list order, i.e. ascending block order;
+//   4. a short or overflowing list falls back to an exact ordered select
+//      over all scores of the row.
+// The k-th largest values come from one 11-bit histogram pass plus an exact
+// finish inside the boundary bin (or the full radix select when that bin is
+// crowded).
+constexpr int kDenseList = 2560;
+constexpr int kDenseExtra = 768;
+constexpr int kDensePassQ = 8192;   // quads per pass (32768 scores; 32 per thread)
+constexpr int kFinishCap = 256;
+
+struct DenseShared {
+  u32x4 rowq[kDensePassQ];
+  union {
+    struct {
+      uint32_t key[kDenseList];
+      int pos[kDenseList];
+    } l;
+    uint32_t smp[2048];
+  } u;
+  int hist[kBins];
+  uint32_t bin[kFinishCap];
+  int tmp[8];
+  int res[2];
+  int wcnt[8];
+  int bin_n;
+};
+
+// Block-wide min and max of one value per thread (ends with a barrier).
+__device__ void block_min_max(uint32_t lo, uint32_t hi, int* tmp, uint32_t& out_lo,
+                              uint32_t& out_hi) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+  }
+  if (lane == 0) { tmp[wave] = (int)lo; tmp[4 + wave] = (int)hi; }
+  __syncthreads();
+  out_lo = min(min((uint32_t)tmp[0], (uint32_t)tmp[1]), min((uint32_t)tmp[2], (uint32_t)tmp[3]));
+  out_hi = max(max((uint32_t)tmp[4], (uint32_t)tmp[5]), max((uint32_t)tmp[6], (uint32_t)tmp[7]));
+  __syncthreads();
+}
+
+// k-th largest (1 <= k <= n) of get(0..n), keys < 2^31.  The keys' range
+// [lo, hi] is cut into at most 2048 bins of 2^s patterns (bin = (key-lo)>>s),
+// so that keys crowded in a narrow range still spread over many bins; one
+// histogram pass finds the boundary bin, whose keys are then ranked exactly
+// (each thread holds one and counts the others) when there are at most
+// kFinishCap of them, else the full radix select runs.  Ends with a barrier.
+template <class Get>
+__device__ uint32_t kth_largest_fast(Get get, int n, int k, DenseShared& sh) {
+  const int tid = threadIdx.x;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  for (int i = tid; i < n; i += 256) {
+    const uint32_t v = get(i);
+    lo = min(lo, v);
+    hi = max(hi, v);
+  }
+  for (int i = tid; i < kBins; i += 256) sh.hist[i] = 0;
+  if (tid == 0) sh.bin_n = 0;
+  block_min_max(lo, hi, sh.tmp, lo, hi);
+  const uint32_t span = hi - lo;
+  const int s = span < (uint32_t)kBins ? 0 : 32 - __clz((int)(span >> 11));   // span >> s < 2048
+  for (int i = tid; i < n; i += 256) atomicAdd(&sh.hist[(get(i) - lo) >> s], 1);
+  __syncthreads();
+  constexpr int per = kBins / 256;
+  const int b0 = tid * per;
+  int local = 0;
+#pragma unroll
+  for (int b = 0; b < per; ++b) local += sh.hist[b0 + b];
+  int total;
+  const int excl = block_excl_scan_256(local, sh.tmp, total);
+  int run = total - excl - local;   // keys in the bins above this thread's
+#pragma unroll
+  for (int b = per - 1; b >= 0; --b) {
+    const int h = sh.hist[b0 + b];
+    if (run < k && run + h >= k) { sh.res[0] = b0 + b; sh.res[1] = run; }
+    run += h;
+  }
+  __syncthreads();
+  const uint32_t B = (uint32_t)sh.res[0];
+  const int kk = k - sh.res[1];
+  const int hb = sh.hist[B];
+  __syncthreads();
+  if (hb > kFinishCap)
+    return block_kth_largest([&](int i, bool& in) { in = true; return get(i); }, n, k, 31,
+                             sh.hist, sh.tmp, sh.res);
+  for (int i = tid; i < n; i += 256) {
+    const uint32_t v = get(i);
+    if (((v - lo) >> s) == B) sh.bin[atomicAdd(&sh.bin_n, 1)] = v;
+  }
+  __syncthreads();
+  if (tid < hb) {
+    const uint32_t x = sh.bin[tid];
+    int gt = 0, ge = 0;
+    for (int j = 0; j < hb; ++j) {
+      const uint32_t y = sh.bin[j];
+      gt += y > x;
+      ge += y >= x;
+    }
+    if (gt < kk && kk <= ge) sh.res[0] = (int)x;   // every writer has the same x
+  }
+  __syncthreads();
+  const uint32_t T = (uint32_t)sh.res[0];
+  __syncthreads();
+  return T;
+}
+
+// Exact top-k of the LDS list (key, pos) of c entries in block order,
+// emitted in list order to out[0..k), -1 up to budget.
+__device__ void select_dense_list(int c, int k, DenseShared& sh, int32_t* __restrict__ out,
+                                  int budget) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t tau =
+      k >= c ? 0u : kth_largest_fast([&](int i) { return sh.u.l.key[i]; }, c, k, sh);
+  const int per = (c + 255) / 256 * 64;
+  const int s0 = min(c, wave * per), s1 = min(c, s0 + per);
+  int a = 0, t = 0;
+  for (int i = s0 + lane; i < s1; i += 64) {
+    const uint32_t v = sh.u.l.key[i];
+    a += v > tau;
+    t += v == tau;
+  }
+  a = wave_sum(a);
+  t = wave_sum(t);
+  if (lane == 0) { sh.wcnt[2 * wave] = a; sh.wcnt[2 * wave + 1] = t; }
+  __syncthreads();
+  int need = k;
+  for (int w2 = 0; w2 < 4; ++w2) need -= sh.wcnt[2 * w2];
+  int tie_base = 0, out_base = 0;
+  for (int w2 = 0; w2 < wave; ++w2) {
+    const int tw = sh.wcnt[2 * w2 + 1];
+    out_base += sh.wcnt[2 * w2] + min(max(need - tie_base, 0), tw);
+    tie_base += tw;
+  }
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int r0 = s0; r0 < s1; r0 += 64) {
+    const int i = r0 + lane;
+    const bool ok = i < s1;
+    const uint32_t v = ok ? sh.u.l.key[i] : 0u;
+    const bool is_tie = ok && v == tau;
+    const unsigned long long mt = __ballot(is_tie);
+    const bool take = (ok && v > tau) || (is_tie && tie_base + __popcll(mt & below) < need);
+    const unsigned long long mk = __ballot(take);
+    if (take) {
+      const int slot = out_base + __popcll(mk & below);
+      if (slot < k) out[slot] = sh.u.l.pos[i];
+    }
+    tie_base += __popcll(mt);
+    out_base += __popcll(mk);
+  }
+  for (int i = k + threadIdx.x; i < budget; i += 256) out[i] = -1;
+}
+
+__global__ void __launch_bounds__(256)
+select_dense_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
+                    int n_seq, int max_blocks, int budget, const uint32_t* __restrict__ dense,
+                    int64_t dense_stride, const uint32_t* __restrict__ dsmp,
+                    int64_t dsmp_stride, int32_t* __restrict__ sel,
+                    int32_t* __restrict__ sel_count) {
+  __shared__ DenseShared sh;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const RowGeom g = row_geom(cu_q, seq_len, n_seq, row, max_blocks);
+  int32_t* out = sel + (int64_t)row * budget;
+  if (!g.ok) {
+    for (int i = tid; i < budget; i += 256) out[i] = -1;
+    if (tid == 0) sel_count[row] = -1;
+    return;
+  }
+  const int n = g.n_c;
+  const int k = min(budget, n);
+  // 16-byte aligned; readable up to the row stride (a multiple of 64 >= n)
+  const uint32_t* drow = dense + (int64_t)row * dense_stride;
+  const u32x4* drow4 = reinterpret_cast<const u32x4*>(drow);
+  const uint32_t* srow = dsmp + (int64_t)row * dsmp_stride;
+  if (tid == 0) sel_count[row] = k;
+
+  if (n <= kDenseList) {   // short rows: the whole row is the list
+    for (int i = tid; i < n; i += 256) { sh.u.l.key[i] = drow[i]; sh.u.l.pos[i] = i; }
+    __syncthreads();
+    select_dense_list(n, k, sh, out, budget);
+    return;
+  }
+
+  const int nq = (n + 3) >> 2;
+  const int ns = (n + kSampleStride - 1) / kSampleStride;
+  const int r = min(ns, (k + kDenseExtra + kSampleStride - 1) / kSampleStride);
+  // samples first (the threshold waits only for them), then the row
+  uint32_t sv[8];
+  if (ns <= 2048) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sv[j] = srow[min(256 * j + tid, ns - 1)];
+  }
+  constexpr int kQ = kDensePassQ / 256;
+  u32x4 kv[kQ];
+  auto load_pass = [&](int q0) {
+#pragma unroll
+    for (int u = 0; u < kQ; ++u) kv[u] = drow4[min(q0 + 256 * u + tid, nq - 1)];
+  };
+  load_pass(0);
+  uint32_t tau_s;
+  if (ns <= 2048) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (256 * j + tid < ns) sh.u.smp[256 * j + tid] = sv[j];
+    __syncthreads();
+    tau_s = kth_largest_fast([&](int i) { return sh.u.smp[i]; }, ns, r, sh);
+  } else {
+    tau_s = kth_largest_fast([&](int i) { return srow[i]; }, ns, r, sh);
+  }
+
+  // compaction; tau_s = 0 would pass every score (more than the list holds)
+  int run = tau_s == 0 ? kDenseList + 1 : 0;
+  for (int q0 = 0; q0 < nq && tau_s != 0; q0 += kDensePassQ) {
+    if (q0 > 0) load_pass(q0);
+    // stage: quad ql of the pass goes to thread ql/32's run, slot swizzled by
+    // the owner so that both the writes here and the reads below are free of
+    // bank conflicts; scores past n become 0 (never >= tau_s >= 1)
+#pragma unroll
+    for (int u = 0; u < kQ; ++u) {
+      const int ql = 256 * u + tid;
+      u32x4 v = kv[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = 4 * (q0 + ql) + e < n ? v[e] : 0u;
+      const int seg = ql >> 5;
+      sh.rowq[(seg << 5) | ((ql & 31) ^ (seg & 31))] = v;
+    }
+    __syncthreads();
+    // this thread's 128 consecutive scores: hit mask and count
+    uint32_t hm[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const u32x4 v = sh.rowq[(tid << 5) | (j ^ (tid & 31))];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hm[j >> 3] |= (v[e] >= tau_s ? 1u : 0u) << (4 * (j & 7) + e);
+    }
+    const int c = __popc(hm[0]) + __popc(hm[1]) + __popc(hm[2]) + __popc(hm[3]);
+    int total;
+    int slot = run + block_excl_scan_256(c, sh.tmp, total);
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+      uint32_t m = hm[w4];
+      while (m) {
+        const int bit = __ffs(m) - 1;
+        m &= m - 1;
+        const int j = 8 * w4 + (bit >> 2), e = bit & 3;
+        if (slot < kDenseList) {
+          const uint32_t* qv = reinterpret_cast<const uint32_t*>(&sh.rowq[(tid << 5) | (j ^ (tid & 31))]);
+          sh.u.l.key[slot] = qv[e];
+          sh.u.l.pos[slot] = 4 * (q0 + 32 * tid + j) + e;
+        }
+        ++slot;
+      }
+    }
+    run += total;
+    __syncthreads();   // rowq is rewritten by the next pass
+  }
+
+  if (run >= k && run <= kDenseList) {
+    select_dense_list(run, k, sh, out, budget);
+  } else {
+    select_ordered([&](int i) { return drow[i]; }, [](int i) { return i; }, n, k, sh.hist, sh.tmp,
+                   sh.res, sh.wcnt, out, budget);
+  }
 }
 
 // ------------------------------------------------------------ workspace
@@ -812,23 +1039,39 @@ struct IndexWs {
   int32_t* cnt;
   u32x2* cand;
   uint16_t* samples;
+  uint32_t* dense;
+  uint32_t* dsmp;
   int ns_stride;
+  int64_t dense_stride, dsmp_stride;
   size_t bytes;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline IndexWs index_ws_layout(void* base, int n_q, int max_blocks) {
-  IndexWs ws;
+// Small tiles (<= 4 queries per sequence) use dense scores; otherwise the
+// sampled-threshold path with per-row candidate lists.
+inline bool use_dense(int max_q_len) { return max_q_len <= 4; }
+
+inline IndexWs index_ws_layout(void* base, int n_q, int max_q_len, int max_blocks) {
+  IndexWs ws = {};
   char* p = (char*)base;
   size_t off = 0;
   ws.ns_stride = (max_blocks + kSampleStride - 1) / kSampleStride;
-  ws.thresh = (uint32_t*)(p + off); off = align256(off + (size_t)n_q * 4);
-  ws.cnt = (int32_t*)(p + off); off = align256(off + (size_t)n_q * 4);
-  ws.cand = (u32x2*)(p + off); off = align256(off + (size_t)n_q * kCandCap * 8);
-  ws.samples = (uint16_t*)(p + off);
-  off = align256(off + (max_blocks > kCandCap ? (size_t)n_q * ws.ns_stride * 2 : 0));
-  ws.bytes = off;
+  ws.dense_stride = ((int64_t)max_blocks + 63) / 64 * 64;
+  ws.dsmp_stride = ((int64_t)ws.ns_stride + 63) / 64 * 64;
+  if (use_dense(max_q_len)) {
+    ws.dense = (uint32_t*)(p + off);
+    off = align256(off + (size_t)n_q * ws.dense_stride * 4);
+    ws.dsmp = (uint32_t*)(p + off);
+    off = align256(off + (size_t)n_q * ws.dsmp_stride * 4);
+  } else {
+    ws.thresh = (uint32_t*)(p + off); off = align256(off + (size_t)n_q * 4);
+    ws.cnt = (int32_t*)(p + off); off = align256(off + (size_t)n_q * 4);
+    ws.cand = (u32x2*)(p + off); off = align256(off + (size_t)n_q * kCandCap * 8);
+    ws.samples = (uint16_t*)(p + off);
+    off = align256(off + (max_blocks > kCandCap ? (size_t)n_q * ws.ns_stride * 2 : 0));
+  }
+  ws.bytes = off < 256 ? (size_t)256 : off;   // (HIP's host max() is int-only)
   return ws;
 }
 
@@ -836,9 +1079,9 @@ inline IndexWs index_ws_layout(void* base, int n_q, int max_blocks) {
 
 extern "C" {
 
-size_t qsa_index_select_workspace(int32_t n_q, int32_t max_blocks) {
-  if (n_q <= 0 || max_blocks < 0) return 0;
-  return qsa::index_ws_layout(nullptr, n_q, max_blocks).bytes;
+size_t qsa_index_select_workspace(int32_t n_q, int32_t max_q_len, int32_t max_blocks) {
+  if (n_q <= 0 || max_q_len <= 0 || max_blocks < 0) return 0;
+  return qsa::index_ws_layout(nullptr, n_q, max_q_len, max_blocks).bytes;
 }
 
 int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
@@ -858,31 +1101,38 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
     return QSA_ERR_INVALID_ARG;
   if (!stride_ok(bk_seq_stride)) return QSA_ERR_INVALID_ARG;
   if (max_blocks > QSA_MAX_TOKENS / QSA_BLOCK) return QSA_ERR_UNSUPPORTED;
-  const IndexWs ws = index_ws_layout(workspace, n_q, max_blocks);
+  if (n_seq > 0x7FFFFFFF / 8) return QSA_ERR_UNSUPPORTED;
+  const IndexWs ws = index_ws_layout(workspace, n_q, max_q_len, max_blocks);
   if (ws_bytes < ws.bytes) return QSA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = (hipStream_t)stream;
 
-  const bool small_tiles = max_q_len <= 4;
-  const int qt = small_tiles ? 4 : 16 * kPrefillMT;
+  if (use_dense(max_q_len)) {
+    // decode: dense scores, then one select per row
+    if (max_blocks > 0) {
+      dim3 grid((unsigned)n_seq, (max_blocks + kDenseChunk - 1) / kDenseChunk);
+      if (grid.y > 65535) return QSA_ERR_UNSUPPORTED;
+      hipLaunchKernelGGL(score_dense_kernel, grid, dim3(256), 0, st, (const uint16_t*)idx_q, w,
+                         cu_q, seq_len, n_q, max_blocks, (const uint16_t*)block_keys,
+                         bk_seq_stride, ws.dense, ws.dense_stride, ws.dsmp, ws.dsmp_stride);
+    }
+    hipLaunchKernelGGL(select_dense_kernel, dim3(n_q), dim3(256), 0, st, cu_q, seq_len, n_seq,
+                       max_blocks, budget, (const uint32_t*)ws.dense, ws.dense_stride,
+                       (const uint32_t*)ws.dsmp, ws.dsmp_stride, sel, sel_count);
+    return launch_status();
+  }
+
+  const int qt = 16 * kPrefillMT;
   const int64_t tiles_per_seq = (max_q_len + qt - 1) / qt;
   const int64_t gx = tiles_per_seq * n_seq;
   if (gx > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
-  const int chunk = small_tiles ? 512 : 1024;
-
+  constexpr int chunk = 1024;
   // 1. sample pass (only rows with more than kCandCap candidates need it)
   if (max_blocks > kCandCap) {
-    const int cols = ws.ns_stride;
-    dim3 grid((unsigned)gx, (cols + chunk - 1) / chunk);
-    if (small_tiles)
-      hipLaunchKernelGGL((score_kernel<1, true>), grid, dim3(256), 0, st, (const uint16_t*)idx_q,
-                         w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq, max_blocks,
-                         (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh, ws.cnt,
-                         ws.cand, ws.samples, ws.ns_stride);
-    else
-      hipLaunchKernelGGL((score_gemm_kernel<kPrefillMT, true>), grid, dim3(256), 0, st, (const uint16_t*)idx_q,
-                         w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq, max_blocks,
-                         (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh, ws.cnt,
-                         ws.cand, ws.samples, ws.ns_stride);
+    dim3 grid((unsigned)gx, (ws.ns_stride + chunk - 1) / chunk);
+    hipLaunchKernelGGL((score_gemm_kernel<kPrefillMT, true>), grid, dim3(256), 0, st,
+                       (const uint16_t*)idx_q, w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq,
+                       max_blocks, (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh,
+                       ws.cnt, ws.cand, ws.samples, ws.ns_stride);
   }
   // 2. thresholds (also preset the list counters)
   hipLaunchKernelGGL(threshold_kernel, dim3(n_q), dim3(256), 0, st, cu_q, seq_len, n_seq,
@@ -891,16 +1141,10 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
   if (max_blocks > 0) {
     dim3 grid((unsigned)gx, (max_blocks + chunk - 1) / chunk);
     if (grid.y > 65535) return QSA_ERR_UNSUPPORTED;
-    if (small_tiles)
-      hipLaunchKernelGGL((score_kernel<1, false>), grid, dim3(256), 0, st,
-                         (const uint16_t*)idx_q, w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq,
-                         max_blocks, (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh,
-                         ws.cnt, ws.cand, ws.samples, ws.ns_stride);
-    else
-      hipLaunchKernelGGL((score_gemm_kernel<kPrefillMT, false>), grid, dim3(256), 0, st,
-                         (const uint16_t*)idx_q, w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq,
-                         max_blocks, (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh,
-                         ws.cnt, ws.cand, ws.samples, ws.ns_stride);
+    hipLaunchKernelGGL((score_gemm_kernel<kPrefillMT, false>), grid, dim3(256), 0, st,
+                       (const uint16_t*)idx_q, w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq,
+                       max_blocks, (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh,
+                       ws.cnt, ws.cand, ws.samples, ws.ns_stride);
   }
   // 4. exact select per row (rows whose list came out short or overflowed
   //    are selected exactly by recomputing their scores)

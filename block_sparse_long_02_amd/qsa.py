@@ -31,7 +31,7 @@ SIGNATURES = {
     "qsa_pool_block_keys": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _c_void_p,
                                            _i32, _i32, _c_void_p]),
     "qsa_rope_apply": (ctypes.c_int, [_c_void_p, _i64, _i64, _i32, _c_void_p, _i32, _i32, _c_void_p]),
-    "qsa_index_select_workspace": (_size, [_i32, _i32]),
+    "qsa_index_select_workspace": (_size, [_i32, _i32, _i32]),
     "qsa_index_select": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                         _i32, _c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p,
                                         _size, _c_void_p]),
@@ -114,8 +114,8 @@ def rope_apply(x, row_stride, head_stride, n_heads, n_rows, pos=None, pos0=0, st
     _check("qsa_rope_apply", st)
 
 
-def index_select_workspace(n_q, max_blocks) -> int:
-    return int(lib().qsa_index_select_workspace(int(n_q), int(max_blocks)))
+def index_select_workspace(n_q, max_q_len, max_blocks) -> int:
+    return int(lib().qsa_index_select_workspace(int(n_q), int(max_q_len), int(max_blocks)))
 
 
 def index_select(idx_q, w, cu_q, seq_len, max_q_len, max_blocks, block_keys, budget, sel,

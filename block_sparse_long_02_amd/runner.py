@@ -51,7 +51,7 @@ class QSARunner:
         self.sel_count = torch.empty((self.n_q,), dtype=torch.int32, device=dev)
         self.out = torch.empty((self.n_q, 24, 256), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((self.n_q, 24), dtype=torch.float32, device=dev)
-        ws = qsa.index_select_workspace(self.n_q, self.max_blocks)
+        ws = qsa.index_select_workspace(self.n_q, self.max_q_len, self.max_blocks)
         self.ws_index = torch.empty((max(ws, 16),), dtype=torch.uint8, device=dev)
         wsd = qsa.attend_decode_workspace(self.n_seq) if self.decode else 16
         self.ws_decode = torch.empty((max(wsd, 16),), dtype=torch.uint8, device=dev)
@@ -82,3 +82,21 @@ class QSARunner:
         self.pool(stream)
         self.select(stream)
         self.attend(stream)
+
+    # HIP graphs ----------------------------------------------------------
+    def capture(self, parts=("pool", "select", "attend")) -> torch.cuda.CUDAGraph:
+        """Record the listed calls of a step as one HIP graph (the library
+        issues no allocations or memsets, so the calls capture as they are).
+        Replaying it redoes those calls on the runner's buffers."""
+        calls = [getattr(self, p) for p in parts]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in calls:
+                c()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        return g

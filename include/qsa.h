@@ -140,9 +140,12 @@ int qsa_rope_apply(void* x, int64_t row_stride, int64_t head_stride, int32_t n_h
  *                               sequence covers or whose n_c exceeds max_blocks
  * budget in 1..512.  The selection is exact with respect to the float32
  * scores the kernels compute (accumulation in MFMA order).  Needs workspace of
- * qsa_index_select_workspace(n_q, max_blocks) bytes.
+ * qsa_index_select_workspace(n_q, max_q_len, max_blocks) bytes, queried with
+ * the same n_q, max_q_len and max_blocks as the call (the method differs for
+ * max_q_len <= 4, where every score is kept); returns 0 for n_q <= 0,
+ * max_q_len <= 0 or max_blocks < 0.
  */
-size_t qsa_index_select_workspace(int32_t n_q, int32_t max_blocks);
+size_t qsa_index_select_workspace(int32_t n_q, int32_t max_q_len, int32_t max_blocks);
 int qsa_index_select(const void* idx_q, const float* w,
                      const int32_t* cu_q, const int32_t* seq_len,
                      int32_t n_seq, int32_t n_q, int32_t max_q_len, int32_t max_blocks,

@@ -45,10 +45,18 @@ def test_status_strings_and_version(L):
 
 
 def test_workspace_queries(L):
-    assert L.qsa_index_select_workspace(0, 100) == 0
-    small = L.qsa_index_select_workspace(10, 1000)
-    big = L.qsa_index_select_workspace(10, 1 << 18)
+    assert L.qsa_index_select_workspace(0, 64, 100) == 0
+    assert L.qsa_index_select_workspace(10, 0, 100) == 0
+    assert L.qsa_index_select_workspace(10, 64, -1) == 0
+    small = L.qsa_index_select_workspace(10, 64, 1000)
+    big = L.qsa_index_select_workspace(10, 64, 1 << 18)
     assert small > 10 * 4096 * 8 and big > small       # candidate lists, then samples
+    # 32768 query rows at 1M context: 1 GiB of lists plus 1 GiB of samples
+    # (sizes past 2^31 must not wrap)
+    assert L.qsa_index_select_workspace(32768, 32768, 1 << 18) >= 32768 * 4096 * 8 + 32768 * 16384 * 2
+    # up to 4 queries per sequence: every score is kept, one row per query
+    dense = L.qsa_index_select_workspace(32, 1, 1 << 15)
+    assert dense >= 32 * (1 << 15) * 4
     assert L.qsa_attend_decode_workspace(0) == 0
     assert L.qsa_attend_decode_workspace(32) >= 32 * 2 * 12 * 256 * 4
 

@@ -183,6 +183,40 @@ def test_index_select_exact_grid_decode():
     _select_and_check(b, exact=True)
 
 
+def test_index_select_exact_grid_decode_long_rows():
+    # n_c = 32768 (largest row selected inside LDS), 35000 and 65536 (sampled
+    # threshold, then the candidate list)
+    b = W.make_decode(seq_lens=[131075, 140001, 262147], budget=512, n_plant=32, seed=29,
+                      exact_grid=True)
+    _select_and_check(b, exact=True)
+
+
+def test_index_select_exact_grid_multi_token_tiles():
+    # 4 and 3 query rows per sequence (multi-token decode shapes): dense scores
+    for prefix, chunk in ((150000, 4), (20001, 3), (9, 4)):
+        b = W.make_prefill(prefix=prefix, chunk=chunk, budget=512, seg=4, n_plant=32,
+                           seed=30 + chunk, exact_grid=True)
+        assert b.max_q_len() <= 4
+        _select_and_check(b, exact=True)
+
+
+def test_index_select_long_row_fallbacks():
+    # all ties on a long row: the list overflows, the ordered select over
+    # global scores keeps the lowest 512 ids
+    b = W.make_decode(seq_lens=[200003], budget=512, n_plant=0, seed=31)
+    b.idx_k[:] = b.idx_k[0, 0].clone()
+    r, _, _ = _select_and_check(b, exact=True)
+    assert np.array_equal(r.sel.cpu().numpy()[0], np.arange(512))
+    # only sampled blocks (every 16th, below 8192) score high: the list is short
+    b = W.make_decode(seq_lens=[160001], budget=512, n_plant=0, seed=32)
+    u = b.idx_q[0].float().sum(0)
+    u = u / u.norm()
+    for blk in range(0, 8192, 16):
+        b.idx_k[0, 4 * blk:4 * blk + 4] = (math.sqrt(128) * (1 + blk / 1e4) * u).to(torch.bfloat16)
+    r, _, _ = _select_and_check(b, exact=True)
+    assert np.array_equal(r.sel.cpu().numpy()[0], np.arange(0, 8192, 16))
+
+
 def test_index_select_decode_rule():
     b = W.make_decode(seq_lens=[131073, 20001, 4100, 99999], budget=512, n_plant=32, seed=24)
     _, _, kinds = _select_and_check(b)
@@ -282,3 +316,29 @@ def test_end_to_end_ragged_decode_reduced():
     b = W.ragged_decode(n_seq=6, lo=4096, hi=200000)
     kinds, worst = _end_to_end(b, range(6))
     print("ragged decode:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+# ------------------------------------------------------------- HIP graphs
+
+def test_graph_replays_match_eager():
+    # decode (dense select path) and a small prefill (list path): the captured
+    # step, replayed several times with eager work in between, must give the
+    # eager results exactly (the kernels are deterministic)
+    for b in (W.make_decode(seq_lens=[40001, 150003, 9002], budget=512, n_plant=32, seed=41),
+              W.tiny_prefill(T=512)):
+        r = QSARunner(b.to("cuda"))
+        r.step()
+        _sync()
+        want = (r.sel.clone(), r.sel_count.clone(), r.out.clone(), r.lse.clone())
+        g = r.capture()
+        junk = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+        for rep in range(4):
+            for t in (r.sel, r.out, r.lse):
+                t.fill_(0)
+            junk.fill_(rep)            # eager work between replays
+            _sync()
+            g.replay()
+            _sync()
+            got = (r.sel, r.sel_count, r.out, r.lse)
+            for a, e in zip(got, want):
+                assert torch.equal(a, e), f"replay {rep} differs"

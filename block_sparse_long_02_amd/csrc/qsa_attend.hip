@@ -27,7 +27,16 @@ namespace qsa {
 #define QSA_ATTEND_XCD_REMAP 0
 #endif
 
-constexpr int kTileMB = 8;                    // micro-blocks per tile
+// micro-blocks per tile (4 or 8): a tile is 1 or 2 halves of 16 tokens
+#ifndef QSA_ATTEND_TILE
+#define QSA_ATTEND_TILE 8
+#endif
+// waves per SIMD the attention kernel is compiled for
+#ifndef QSA_ATTEND_OCC
+#define QSA_ATTEND_OCC 2
+#endif
+constexpr int kTileMB = QSA_ATTEND_TILE;
+constexpr int kHalves = kTileMB / 4;
 constexpr int kWaves = 4;
 constexpr int kMaxList = kMaxBudget + 1;      // selected blocks + tail block
 constexpr int kPartFloats = kGroup * kHeadDim + 2 * 16;  // O[12][256], m[16], l[16]
@@ -60,7 +69,7 @@ struct AttnShared {
 // mode kFinal: one workgroup per (row, KV head) writes out / lse.
 // otherwise: n_splits workgroups per (row, KV head) write partials.
 template <bool kFinal>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, QSA_ATTEND_OCC)
 attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
               const int32_t* __restrict__ seq_len, int n_seq, int n_rows,
               const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
@@ -176,58 +185,56 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
 
   for (int t = t_begin; t < t_end; ++t) {
     const int base = t * kTileMB;
-    // K rows: lane is token row `col` of each 16-token half
-    const int idk0 = sh.list[min(base + (col >> 2), n_mb - 1)];
-    const int idk1 = sh.list[min(base + 4 + (col >> 2), n_mb - 1)];
-    // V / P k-slices: micro-blocks base+grp and base+4+grp
-    const int sv0 = base + grp, sv1 = base + 4 + grp;
-    const int idv0 = sh.list[min(sv0, n_mb - 1)], idv1 = sh.list[min(sv1, n_mb - 1)];
-
-    const uint16_t* kp0 = kbase + ((int64_t)idk0 * kBlock + (col & 3)) * kHeadDim + 8 * grp;
-    const uint16_t* kp1 = kbase + ((int64_t)idk1 * kBlock + (col & 3)) * kHeadDim + 8 * grp;
-    const uint16_t* vp0 = vbase + (int64_t)idv0 * (kBlock * kHeadDim) + 8 * col;
-    const uint16_t* vp1 = vbase + (int64_t)idv1 * (kBlock * kHeadDim) + 8 * col;
-    u32x4 ka[8], kb[8], va[8], vb[8];
+    // Half hv covers micro-blocks base + 4hv .. +3.  K rows: lane is token
+    // row `col` of the half; V / P k-slices: micro-block base + 4hv + grp.
+    u32x4 kh[kHalves][8], vh[kHalves][8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) { ka[ks] = ldg16(kp0 + 32 * ks); kb[ks] = ldg16(kp1 + 32 * ks); }
+    for (int hv = 0; hv < kHalves; ++hv) {
+      const int idk = sh.list[min(base + 4 * hv + (col >> 2), n_mb - 1)];
+      const int idv = sh.list[min(base + 4 * hv + grp, n_mb - 1)];
+      const uint16_t* kp = kbase + ((int64_t)idk * kBlock + (col & 3)) * kHeadDim + 8 * grp;
+      const uint16_t* vp = vbase + (int64_t)idv * (kBlock * kHeadDim) + 8 * col;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) { va[c] = ldg16(vp0 + 128 * c); vb[c] = ldg16(vp1 + 128 * c); }
-
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < 8; ++ks) kh[hv][ks] = ldg16(kp + 32 * ks);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      s0 = mfma_16x16x32(ka[ks], qf[ks], s0);
-      s1 = mfma_16x16x32(kb[ks], qf[ks], s1);
+      for (int c = 0; c < 8; ++c) vh[hv][c] = ldg16(vp + 128 * c);
     }
-    // s0[i]: token i of micro-block slot sv0, head col; s1[i]: slot sv1.
-    float x[8];
+
+    // sc[hv][i]: token i of micro-block slot base + 4hv + grp, head col
+    f32x4 sc[kHalves];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { x[i] = s0[i] * scale; x[4 + i] = s1[i] * scale; }
+    for (int hv = 0; hv < kHalves; ++hv) {
+      sc[hv] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) sc[hv] = mfma_16x16x32(kh[hv][ks], qf[ks], sc[hv]);
+    }
+    float x[4 * kHalves];
+#pragma unroll
+    for (int hv = 0; hv < kHalves; ++hv)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * hv + i] = sc[hv][i] * scale;
     if (base + kTileMB > cnt) {
       // the tile holds the tail block and/or padding slots (uniform branch)
-      const bool v0 = sv0 < n_mb, v1 = sv1 < n_mb;
-      const int n0 = !v0 ? 0 : (sv0 == tail_slot ? tail_len : 4);
-      const int n1 = !v1 ? 0 : (sv1 == tail_slot ? tail_len : 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = i < n0 ? x[i] : -INFINITY;
-        x[4 + i] = i < n1 ? x[4 + i] : -INFINITY;
-      }
-      // Cache rows past the query inside the tail block (and padding slots)
-      // may hold anything: zero their V so that p = 0 cannot meet a NaN.
-      const uint32_t a01 = (n0 > 0 ? 0xFFFFu : 0u) | (n0 > 1 ? 0xFFFF0000u : 0u);
-      const uint32_t a23 = (n0 > 2 ? 0xFFFFu : 0u) | (n0 > 3 ? 0xFFFF0000u : 0u);
-      const uint32_t b01 = (n1 > 0 ? 0xFFFFu : 0u) | (n1 > 1 ? 0xFFFF0000u : 0u);
-      const uint32_t b23 = (n1 > 2 ? 0xFFFFu : 0u) | (n1 > 3 ? 0xFFFF0000u : 0u);
+      for (int hv = 0; hv < kHalves; ++hv) {
+        const int sv = base + 4 * hv + grp;
+        const int nv = sv >= n_mb ? 0 : (sv == tail_slot ? tail_len : 4);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        va[c][0] &= a01; va[c][1] &= a23; va[c][2] &= a01; va[c][3] &= a23;
-        vb[c][0] &= b01; vb[c][1] &= b23; vb[c][2] &= b01; vb[c][3] &= b23;
+        for (int i = 0; i < 4; ++i) x[4 * hv + i] = i < nv ? x[4 * hv + i] : -INFINITY;
+        // Cache rows past the query inside the tail block (and padding
+        // slots) may hold anything: zero their V so that p = 0 cannot meet a
+        // NaN.
+        const uint32_t m01 = (nv > 0 ? 0xFFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
+        const uint32_t m23 = (nv > 2 ? 0xFFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          vh[hv][c][0] &= m01; vh[hv][c][1] &= m23; vh[hv][c][2] &= m01; vh[hv][c][3] &= m23;
+        }
       }
     }
     float mt = x[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, x[i]);
+    for (int i = 1; i < 4 * kHalves; ++i) mt = fmaxf(mt, x[i]);
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     // Lazy rescale: the reference max m_run only moves when a head's tile max
@@ -247,25 +254,40 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
         for (int i = 0; i < 4; ++i) o[n][i] *= a_row[i];
       }
     }
-    float p[8], ps = 0.f;
+    float p[4 * kHalves], ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - m_run); ps += p[i]; }
+    for (int i = 0; i < 4 * kHalves; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - m_run); ps += p[i]; }
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
     l_run += ps;
 
-    u32x4 pa;
-    pa[0] = pack_bf16x2(p[0], p[1]);
-    pa[1] = pack_bf16x2(p[2], p[3]);
-    pa[2] = pack_bf16x2(p[4], p[5]);
-    pa[3] = pack_bf16x2(p[6], p[7]);
+    if constexpr (kHalves == 2) {
+      // P k-slice of 8 tokens (2 micro-blocks) per lane: MFMA 16x16x32
+      u32x4 pa;
+      pa[0] = pack_bf16x2(p[0], p[1]);
+      pa[1] = pack_bf16x2(p[2], p[3]);
+      pa[2] = pack_bf16x2(p[4], p[5]);
+      pa[3] = pack_bf16x2(p[6], p[7]);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      // dims 32c + 2*col (even tile) and 32c + 2*col + 1 (odd tile)
-      u32x4 be = {va[c][0], va[c][1], vb[c][0], vb[c][1]};
-      u32x4 bo = {va[c][2], va[c][3], vb[c][2], vb[c][3]};
-      o[2 * c] = mfma_16x16x32(pa, be, o[2 * c]);
-      o[2 * c + 1] = mfma_16x16x32(pa, bo, o[2 * c + 1]);
+      for (int c = 0; c < 8; ++c) {
+        // dims 32c + 2*col (even tile) and 32c + 2*col + 1 (odd tile)
+        u32x4 be = {vh[0][c][0], vh[0][c][1], vh[1][c][0], vh[1][c][1]};
+        u32x4 bo = {vh[0][c][2], vh[0][c][3], vh[1][c][2], vh[1][c][3]};
+        o[2 * c] = mfma_16x16x32(pa, be, o[2 * c]);
+        o[2 * c + 1] = mfma_16x16x32(pa, bo, o[2 * c + 1]);
+      }
+    } else {
+      // P k-slice of 4 tokens (1 micro-block) per lane: MFMA 16x16x16
+      u32x2 pa;
+      pa[0] = pack_bf16x2(p[0], p[1]);
+      pa[1] = pack_bf16x2(p[2], p[3]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        u32x2 be = {vh[0][c][0], vh[0][c][1]};
+        u32x2 bo = {vh[0][c][2], vh[0][c][3]};
+        o[2 * c] = mfma_16x16x16(pa, be, o[2 * c]);
+        o[2 * c + 1] = mfma_16x16x16(pa, bo, o[2 * c + 1]);
+      }
     }
   }
 

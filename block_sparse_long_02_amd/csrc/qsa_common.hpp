@@ -48,6 +48,15 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// D(16x16, f32) += A(16x16, bf16) * B(16x16, bf16).  Lane l supplies
+// A[l%16][4*(l/16) .. +3] and B[4*(l/16) .. +3][l%16]; it receives
+// D[4*(l/16) + i][l%16] for i = 0..3.
+__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
 // Rotary inverse frequency 1e7^(-j/32) of rotation pair j (float64).
 __device__ __forceinline__ double rope_inv_freq(int j) {
   return pow(1.0e7, -(double)j / (double)(kRopeDim / 2));

@@ -38,6 +38,10 @@ namespace qsa {
 #define QSA_PREFILL_MT 2
 #endif
 constexpr int kPrefillMT = QSA_PREFILL_MT;
+// workgroups per CU the prefill score GEMM is compiled for
+#ifndef QSA_SCORE_WGS
+#define QSA_SCORE_WGS 3
+#endif
 constexpr int kCandCap = 4096;      // list capacity per row
 constexpr int kSampleStride = 16;   // every 16th block is sampled
 constexpr int kSampleExtra = 1536;  // aimed-for surplus of list entries over K
@@ -211,7 +215,7 @@ constexpr int kStageCols = 64;
 constexpr int kPending = 16;        // pending pre-filter passes per row and workgroup
 
 template <int MT, bool kSample>
-__global__ void __launch_bounds__(256, 3)
+__global__ void __launch_bounds__(256, QSA_SCORE_WGS)
 score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
                   const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
                   int n_seq, int n_q, int tiles_per_seq, int max_blocks,
@@ -292,23 +296,42 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
   __syncthreads();
   f32x4 r_wc[MT];
   float r_tlo[MT];
+  int r_nc[MT];
+  // pending entries of this lane's row (uniform over its 16-lane group):
+  // each row belongs to exactly one wave, so the count needs no atomics
+  int r_pc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     r_wc[mt] = s_wc[(wave * MT + mt) * 4 + grp];
     r_tlo[mt] = s_tlo[(wave * MT + mt) * 4 + grp];
+    r_nc[mt] = min(s_nc[(wave * MT + mt) * 4 + grp], v1);
+    r_pc[mt] = 0;
   }
 
   const uint16_t* bseq = bk + (int64_t)s * bk_stride;
   const int n_stages = (v1 - v0 + kStageCols - 1) / kStageCols;
+  // The sequence's block keys as a buffer resource whose range ends after
+  // virtual column v1 - 1: loads past it return zeros (such columns are
+  // never emitted).  Offsets stay below 2^28 bytes (2^20 blocks x 256 B).
+  const int nrec = ((v1 - 1) * stride + 1) * kIdxDim * 2;
+  const __amdgpu_buffer_rsrc_t bk_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)bseq, (short)0, nrec, 0x00020000);
   // This thread carries 4 chunks of a stage: column c = 16*wave + 4*i +
-  // lane/16, chunk slot lane%16, which holds chunk (lane%16) ^ (c%16).
+  // lane/16, chunk slot lane%16, which holds chunk (lane%16) ^ (c%16); its
+  // byte offsets relative to the stage's first column are fixed.
+  int loff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 16 * wave + 4 * i + (lane >> 4);
+    const int q = (lane & 15) ^ (c & 15);
+    loff[i] = (c * stride * kIdxDim + q * 8) * 2;
+  }
   auto load_stage = [&](u32x4 (&r)[4], int st) {
+    const int base = (v0 + st * kStageCols) * stride * kIdxDim * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = 16 * wave + 4 * i + (lane >> 4);
-      const int q = (lane & 15) ^ (c & 15);
-      const int vcol = min(v0 + st * kStageCols + c, v1 - 1);
-      r[i] = ldg16(bseq + (int64_t)vcol * stride * kIdxDim + q * 8);
+      r[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(bk_rsrc, base + loff[i], 0, 0));
     }
   };
   auto store_stage = [&](const u32x4 (&r)[4], int st) {
@@ -367,10 +390,12 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
       fast = fmaf(relu_bits(acc[mt][2]), wc[2], fast);
       fast = fmaf(relu_bits(acc[mt][1]), wc[1], fast);
       fast = fmaf(relu_bits(acc[mt][0]), wc[0], fast);
-      const bool pass = fast >= r_tlo[mt];
-      if (__ballot(pass)) {                 // a few lanes: append raw accumulators
-        if (pass && vcol < v1 && vcol < s_nc[j]) {
-          const int slot = atomicAdd(&s_pcnt[j], 1);
+      if (__ballot(fast >= r_tlo[mt])) {    // a few lanes: append raw accumulators
+        const bool pass = fast >= r_tlo[mt] && vcol < r_nc[mt];
+        // this lane's 16-lane group is its row: rank among the group's passes
+        const uint32_t gm = (uint32_t)(__ballot(pass) >> (16 * grp)) & 0xFFFFu;
+        const int slot = r_pc[mt] + __popc(gm & ((1u << col) - 1u));
+        if (pass) {
           if (slot < kPend) {
             s_pacc[j][slot] = acc[mt];
             s_pidx[j][slot] = vcol;
@@ -378,6 +403,7 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
             emit_exact(acc[mt], j, vcol, vcol);   // rare: list full
           }
         }
+        r_pc[mt] += __popc(gm);
       }
     }
   };
@@ -413,6 +439,11 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
   else run(std::true_type{});
 
   if (!kSample && !collect_all) {
+    if (col == 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) s_pcnt[(wave * MT + mt) * 4 + grp] = r_pc[mt];
+    }
+    __syncthreads();
     // exact score of every pending entry; each wave takes rows wave, wave+4, ...
     for (int j = wave; j < QT; j += 4) {
       const int n = min(s_pcnt[j], kPend);

@@ -330,26 +330,36 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   }
 }
 
-// Combine the n_splits partials of every (row, KV head, head): one workgroup
-// per (row, query head), one output dim per thread.
+// Combine the NS partials of every (row, KV head, head): one workgroup per
+// (row, query head), one output dim per thread.  All NS (max, sum, output)
+// triples are loaded at once, then merged: one round trip to memory.
+template <int NS>
 __global__ void __launch_bounds__(256)
-combine_kernel(const float* __restrict__ part, int n_splits, int n_rows,
-               uint16_t* __restrict__ out, float* __restrict__ lse) {
+combine_kernel(const float* __restrict__ part, int n_rows, uint16_t* __restrict__ out,
+               float* __restrict__ lse) {
   const int h = blockIdx.x % kGroup;
   const int g = (blockIdx.x / kGroup) & 1;
   const int row = blockIdx.x / (2 * kGroup);
   if (row >= n_rows) return;
   const int d = threadIdx.x;
-  const float* base = part + (int64_t)(row * 2 + g) * n_splits * kPartFloats;
-  float mx = -INFINITY;
-  for (int sp = 0; sp < n_splits; ++sp) mx = fmaxf(mx, base[sp * kPartFloats + kGroup * kHeadDim + h]);
-  float lsum = 0.f, acc = 0.f;
-  for (int sp = 0; sp < n_splits; ++sp) {
+  const float* base = part + (int64_t)(row * 2 + g) * NS * kPartFloats;
+  float m[NS], l[NS], o[NS];
+#pragma unroll
+  for (int sp = 0; sp < NS; ++sp) {
     const float* pp = base + sp * kPartFloats;
-    const float l = pp[kGroup * kHeadDim + 16 + h];
-    const float f = l > 0.f ? exp2f(pp[kGroup * kHeadDim + h] - mx) : 0.f;
-    lsum += l * f;
-    acc += pp[h * kHeadDim + d] * f;
+    m[sp] = pp[kGroup * kHeadDim + h];
+    l[sp] = pp[kGroup * kHeadDim + 16 + h];
+    o[sp] = pp[h * kHeadDim + d];
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < NS; ++sp) mx = fmaxf(mx, m[sp]);
+  float lsum = 0.f, acc = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < NS; ++sp) {
+    const float f = l[sp] > 0.f ? exp2f(m[sp] - mx) : 0.f;
+    lsum += l[sp] * f;
+    acc += o[sp] * f;
   }
   out[((int64_t)row * kQHeads + g * kGroup + h) * kHeadDim + d] = (uint16_t)f32_to_bf16_bits(acc / lsum);
   if (lse && d == 0) lse[(int64_t)row * kQHeads + g * kGroup + h] = (mx + log2f(lsum)) * kLn2;
@@ -359,7 +369,11 @@ combine_kernel(const float* __restrict__ part, int n_splits, int n_rows,
 
 namespace {
 
-constexpr int kDecodeSplits = 8;
+// splits per (row, KV head) in decode
+#ifndef QSA_DECODE_SPLITS
+#define QSA_DECODE_SPLITS 8
+#endif
+constexpr int kDecodeSplits = QSA_DECODE_SPLITS;
 
 int check_attend_common(const void* q, const void* k_cache, const void* v_cache,
                         int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
@@ -421,9 +435,8 @@ int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq, cons
                      n_seq, n_seq, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
                      kv_seq_stride, kv_head_stride, sel, sel_count, budget, kDecodeSplits, 1,
                      (uint16_t*)nullptr, (float*)nullptr, part);
-  hipLaunchKernelGGL(qsa::combine_kernel, dim3(n_seq * 2 * qsa::kGroup), dim3(256), 0,
-                     (hipStream_t)stream, (const float*)part, kDecodeSplits, n_seq, (uint16_t*)out,
-                     lse);
+  hipLaunchKernelGGL(qsa::combine_kernel<kDecodeSplits>, dim3(n_seq * 2 * qsa::kGroup), dim3(256), 0,
+                     (hipStream_t)stream, (const float*)part, n_seq, (uint16_t*)out, lse);
   return launch_status();
 }
 

@@ -134,6 +134,14 @@ def test_attend_decode_on_oracle_selection():
     for row in range(b.n_q):
         ref_o, ref_l = view.attend(row, chosen[row])
         check_attention(r.out[row], r.lse[row], ref_o, ref_l, f"decode row {row}")
+    # the workspace's arrival counters stay valid across calls of different
+    # sizes: a call on the first 2 sequences, then all 5 again
+    out_all = r.out.clone()
+    qsa.attend_decode(r.b.q[:2], r.b.seq_len[:2], r.k_cache, r.v_cache, r.sel[:2],
+                      r.sel_count[:2], r.budget, r.out[:2], r.lse[:2], r.ws_decode)
+    r.attend()
+    _sync()
+    assert torch.equal(r.out, out_all)
     # split-K decode equals the one-workgroup prefill kernel on the same choices
     out_d, lse_d = r.out.clone(), r.lse.clone()
     qsa.attend_prefill(r.b.q, r.b.cu_q, r.b.seq_len, 1, r.k_cache, r.v_cache, r.sel, r.sel_count,

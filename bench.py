@@ -10,8 +10,10 @@ Inputs are seeded synthetic tensors generated directly in HBM; the timed
 region starts with everything resident.  Timing uses HIP events on the stream
 the kernels run on.  `roofline` is for the dominant kernel (the attention
 kernel of the prefill step): algorithmic bytes per launch / its mean
-duration, against 8 TB/s.  `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload.
+duration, against 8 TB/s, with the counted HBM-side bytes beside it
+(`traffic`, from profiles/traffic.json while the kernel source is unchanged).
+`rows` gives each hot-path row against its own roofline.  `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                     [--only prefill|decode]
@@ -53,7 +55,8 @@ def src_hash(path):
 
 
 def traffic_from_profiles(kernel_file, key):
-    """HBM bytes per launch from committed counter runs, if they were taken on
+    """HBM-side bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated against a
+    copy of known size) from the committed counter runs, if they were taken on
     the current source of the kernel's file; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
@@ -65,6 +68,18 @@ def traffic_from_profiles(kernel_file, key):
     if d.get("source_sha") != src_hash(kernel_file):
         return None
     return d.get("bytes_per_launch")
+
+
+def decode_traffic():
+    """HBM-side bytes of one decode step (sum over its kernels), or None."""
+    csrc = os.path.join(ROOT, "block_sparse_long_02_amd", "csrc")
+    # (131,073 tokens complete no new block: the step launches no pooling)
+    parts = [("qsa_index.hip", "score_dense_decode_128k"),
+             ("qsa_index.hip", "select_dense_decode_128k"),
+             ("qsa_attend.hip", "attend_decode_128k"),
+             ("qsa_attend.hip", "combine_decode_128k")]
+    vals = [traffic_from_profiles(os.path.join(csrc, f), k) for f, k in parts]
+    return None if any(v is None for v in vals) else int(sum(vals))
 
 
 def time_prefill(args):
@@ -101,12 +116,14 @@ def time_prefill(args):
     n_q = r.n_q
     attend_bytes = sum_s * TOKEN_GATHER_BYTES + n_q * (2 * Q_ROW_BYTES + 24 * 4 + r.budget * 4)
     attend_gbs = attend_bytes / (stage["attend"] * 1e-3) / 1e9
+    # core flops: per token of S and head, q.k and p.v over 256 dims
+    attend_flops = sum_s * 24 * 256 * 4
     index_flops = sum_nc * 1024 * (1 + 1 / 16)
     res = dict(
         n_q=n_q, ms_per_step=total_ms / args.steps, stages_ms=stage,
         value=n_q / (total_ms / args.steps * 1e-3),
         sum_set=sum_s, sum_candidates=sum_nc,
-        attend=dict(bytes=attend_bytes, gbs=attend_gbs),
+        attend=dict(bytes=attend_bytes, gbs=attend_gbs, flops=attend_flops),
         index=dict(flops=index_flops, tflops=index_flops / (stage["select"] * 1e-3) / 1e12),
         runner=r, batch=b)
     return res
@@ -245,14 +262,34 @@ def main():
             "workload": "chunked prefill: 32768-token chunk on a 1015808-token cached prefix "
                         "(1048576 total), batch 1, budget 512 blocks + tail",
             "global_batch": 1, "seq_len": 1048576, "query_tokens": pre["n_q"], "budget": 512}
+        traffic = traffic_from_profiles(attend_file, "attend_prefill_1m")
         out["roofline"] = {
             "kernel": "attend_kernel (sparse prefill attention)",
             "bound": "hbm", "achieved": round(pre["attend"]["gbs"], 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(pre["attend"]["gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profiles(attend_file, "attend_prefill_1m"),
+            "traffic": traffic,
             "algorithmic_bytes_per_launch": pre["attend"]["bytes"],
-            "mean_launch_ms": round(pre["stages_ms"]["attend"], 4)}
+            "mean_launch_ms": round(pre["stages_ms"]["attend"], 4),
+            # algorithmic bytes count every gathered token once per query (no
+            # reuse); the counters show what crossed the L2 boundary
+            "measured_gbs": (round(traffic / (pre["stages_ms"]["attend"] * 1e-3) / 1e9, 1)
+                             if traffic else None)}
         out["stages_ms"] = {k: round(v, 4) for k, v in pre["stages_ms"].items()}
+        pool_bytes = (pre["n_q"] // 4) * (4 * BLOCK_KEY_BYTES + BLOCK_KEY_BYTES)
+        out["rows"] = {
+            "a1_pool": {"ms": round(pre["stages_ms"]["pool"], 4), "bound": "hbm",
+                        "algorithmic_bytes": pool_bytes,
+                        "frac": round(pool_bytes / (pre["stages_ms"]["pool"] * 1e-3) / 1e9
+                                      / HBM_PEAK_GBS, 4)},
+            "a2_a3_index_select": {"ms": round(pre["stages_ms"]["select"], 4), "bound": "mfma",
+                                   "algorithmic_tflop": round(pre["index"]["flops"] / 1e12, 3),
+                                   "tflops": round(pre["index"]["tflops"], 1),
+                                   "frac": round(pre["index"]["tflops"] / MFMA_BF16_PEAK_TFS, 4)},
+            "a4_a5_a6_attend_prefill": {"ms": round(pre["stages_ms"]["attend"], 4),
+                                        "bound": "gather", "algorithmic_bytes": pre["attend"]["bytes"],
+                                        "frac_hbm_zero_reuse": round(pre["attend"]["gbs"] / HBM_PEAK_GBS, 4),
+                                        "core_tflops": round(pre["attend"]["flops"] / (pre["stages_ms"]["attend"] * 1e-3) / 1e12, 1),
+                                        "frac_mfma": round(pre["attend"]["flops"] / (pre["stages_ms"]["attend"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)}}
         out["index_select"] = {"algorithmic_tflop": round(pre["index"]["flops"] / 1e12, 3),
                                "tflops": round(pre["index"]["tflops"], 1),
                                "frac_of_bf16_mfma_peak": round(pre["index"]["tflops"] / MFMA_BF16_PEAK_TFS, 4)}
@@ -270,6 +307,7 @@ def main():
              "roofline": {"bound": "hbm", "scope": "whole step",
                           "achieved": round(dec["hbm"]["gbs"], 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(dec["hbm"]["gbs"] / HBM_PEAK_GBS, 4),
+                          "traffic": decode_traffic(),
                           "algorithmic_bytes": dec["hbm"]["bytes"]},
              "stages_ms": {k: round(v, 4) for k, v in dec["stages_ms"].items()}}
         if args.only == "decode":

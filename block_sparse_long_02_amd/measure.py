@@ -1,0 +1,133 @@
+"""HBM traffic of the hot-path kernels from rocprofv3 counters.
+
+Two counter runs of the same program give per-dispatch FETCH_SIZE and
+WRITE_SIZE (KiB moved between L2 and memory).  The program first runs a plain
+copy of known size (read 1 GiB, write 1 GiB) whose counters calibrate both:
+factor = known bytes / counted bytes.  Then one step of each workload:
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d D1 -o run -- \\
+        python3 -m block_sparse_long_02_amd.measure probe
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d D2 -o run -- \\
+        python3 -m block_sparse_long_02_amd.measure probe
+    python3 -m block_sparse_long_02_amd.measure summarize D1/run_counter_collection.csv \\
+        D2/run_counter_collection.csv profiles/traffic.json
+
+`summarize` writes, per kernel, the calibrated bytes per launch and the hash
+of the source file the kernel was built from, so that a reader (bench.py)
+uses the figures only while that source is unchanged.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import sys
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30
+
+# key -> (substring of the kernel name, source file, which dispatch of that
+# kernel: an index in dispatch order, or None for the mean of all).  Pooling
+# runs three times: the prefill runner pools its cached prefix, the prefill
+# step pools the chunk's new blocks, the decode runner pools its prefix (a
+# decode step of 131,073 tokens completes no new block).
+KERNELS = {
+    "pool_block_keys_prefill_1m": ("pool_block_keys_kernel", "qsa_pool.hip", 1),
+    "score_sample_prefill_1m": ("score_gemm_kernel<2, true>", "qsa_index.hip", None),
+    "threshold_prefill_1m": ("threshold_kernel", "qsa_index.hip", None),
+    "score_filter_prefill_1m": ("score_gemm_kernel<2, false>", "qsa_index.hip", None),
+    "final_select_prefill_1m": ("final_select_kernel", "qsa_index.hip", None),
+    "attend_prefill_1m": ("attend_kernel<true>", "qsa_attend.hip", None),
+    "score_dense_decode_128k": ("score_dense_kernel", "qsa_index.hip", None),
+    "select_dense_decode_128k": ("select_dense_kernel", "qsa_index.hip", None),
+    "attend_decode_128k": ("attend_kernel<false>", "qsa_attend.hip", None),
+    "combine_decode_128k": ("combine_kernel", "qsa_attend.hip", None),
+}
+
+
+def src_hash(name: str) -> str:
+    path = os.path.join(_PKG, "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def probe():
+    """The program the counter runs profile: copy, one prefill step, one decode step."""
+    import torch
+    from . import workloads as W
+    from .runner import QSARunner
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)          # the calibration copy: 1 GiB read, 1 GiB written
+    torch.cuda.synchronize()
+    del src, dst
+    print("MARK copy done", flush=True)
+
+    b = W.chunked_prefill_1m(device="cuda")
+    r = QSARunner(b)
+    torch.cuda.synchronize()
+    print("MARK prefill step", flush=True)
+    r.step()
+    torch.cuda.synchronize()
+    del r, b
+    torch.cuda.empty_cache()
+
+    b = W.decode_128k(device="cuda")
+    r = QSARunner(b)
+    torch.cuda.synchronize()
+    print("MARK decode step", flush=True)
+    r.step()
+    torch.cuda.synchronize()
+    print("MARK done", flush=True)
+
+
+def _dispatches(path: str, counter: str):
+    """[(dispatch id, kernel name, value in KiB)] in dispatch order."""
+    vals = {}
+    for row in csv.DictReader(open(path)):
+        if row.get("Counter_Name") != counter:
+            continue
+        key = (int(row["Dispatch_Id"]), row["Kernel_Name"])
+        vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    return [(d, k, v) for (d, k), v in sorted(vals.items())]
+
+
+def summarize(fetch_csv: str, write_csv: str, out_json: str):
+    fetch = _dispatches(fetch_csv, "FETCH_SIZE")
+    write = _dispatches(write_csv, "WRITE_SIZE")
+
+    def find(d, sub, index=None):
+        vs = [v for _, k, v in d if sub in k]
+        return vs if index is None else vs[index:index + 1]
+
+    copy_f = max(find(fetch, "neg_kernel"))       # the 1 GiB copy is the largest neg dispatch
+    copy_w = max(find(write, "neg_kernel"))
+    f_fac = COPY_BYTES / 1024.0 / copy_f
+    w_fac = COPY_BYTES / 1024.0 / copy_w
+    out = {"calibration": {"copy_bytes": COPY_BYTES, "fetch_kib_counted": copy_f,
+                           "write_kib_counted": copy_w, "fetch_factor": f_fac,
+                           "write_factor": w_fac}}
+    for key, (sub, src, index) in KERNELS.items():
+        fv, wv = find(fetch, sub, index), find(write, sub, index)
+        if not fv or not wv:
+            continue
+        fb = sum(fv) / len(fv) * 1024.0 * f_fac
+        wb = sum(wv) / len(wv) * 1024.0 * w_fac
+        out[key] = {"kernel": sub, "source": src, "source_sha": src_hash(src),
+                    "launches": len(fv), "fetch_bytes_per_launch": round(fb),
+                    "write_bytes_per_launch": round(wb), "bytes_per_launch": round(fb + wb)}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    for k, v in out.items():
+        print(k, v)
+
+
+if __name__ == "__main__":
+    if sys.argv[1:2] == ["probe"]:
+        probe()
+    elif sys.argv[1:2] == ["summarize"] and len(sys.argv) == 5:
+        summarize(*sys.argv[2:5])
+    else:
+        sys.exit("usage: measure.py probe | summarize FETCH_CSV WRITE_CSV OUT_JSON")

@@ -134,7 +134,10 @@ int qsa_rope_apply(void* x, int64_t row_stride, int64_t head_stride, int32_t n_h
  * order (score descending, block index ascending).
  *
  *   idx_q  bf16 [n_q][4][128]   indexer queries
- *   w      fp32 [n_q][4]        per-head weights
+ *   w      fp32 [n_q][4]        per-head weights, finite and >= 0 (scores are
+ *                               then >= 0 and the kernels order them by their
+ *                               float32 bit patterns; other weights give an
+ *                               unspecified selection)
  *   sel    int32 [n_q][budget]  OUT: B_i in ascending block order, then -1 padding
  *   count  int32 [n_q]          OUT: K = min(budget, n_c); -1 for a row that no
  *                               sequence covers or whose n_c exceeds max_blocks

@@ -44,8 +44,13 @@ constexpr int kPrefillMT = QSA_PREFILL_MT;
 #endif
 constexpr int kCandCap = 4096;      // list capacity per row
 constexpr int kSampleStride = 16;   // every 16th block is sampled
-constexpr int kSampleExtra = 1536;  // aimed-for surplus of list entries over K
-constexpr int kBins = 2048;         // 11-bit radix digits
+// aimed-for surplus of prefill list entries over K
+#ifndef QSA_SAMPLE_EXTRA
+#define QSA_SAMPLE_EXTRA 1024
+#endif
+constexpr int kSampleExtra = QSA_SAMPLE_EXTRA;
+constexpr int kBins = 2048;         // 11-bit radix digits / histogram bins
+constexpr int kFinishCap = 256;     // keys ranked one by one in a boundary bin
 // 1/sqrt(128) rounded once to float32
 constexpr float kScoreScale = 0x1.6a09e6p-4f;
 
@@ -154,9 +159,16 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
   }
   const uint16_t* bseq = bk + (int64_t)s * bk_stride;
   const int c0 = v0 + wave * 16;
-  // B fragment of tile t: column c0 + 64t + col (clamped in bounds past v1)
+#ifndef QSA_DENSE_SKEW
+#define QSA_DENSE_SKEW 1
+#endif
+  // Workgroups start at different tiles of their chunk (rotated order) so
+  // that the ones running together do not stream the same address offsets.
+  const int rot = QSA_DENSE_SKEW ? (int)((blockIdx.x * 7u + blockIdx.y * 3u) & (kDenseTiles - 1)) : 0;
+  auto tcol = [&](int t) { return c0 + 64 * ((t + rot) & (kDenseTiles - 1)); };
+  // B fragment of tile t: column tcol(t) + col (clamped in bounds past v1)
   auto load_tile = [&](u32x4 (&bf)[4], int t) {
-    const int b = min(c0 + 64 * t + col, v1 - 1);
+    const int b = min(tcol(t) + col, v1 - 1);
     const uint16_t* src = bseq + (int64_t)b * kIdxDim + 8 * grp;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) bf[ks] = ldg16(src + 32 * ks);
@@ -183,7 +195,7 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
     uint32_t* srow = dsmp + (int64_t)(qb + j) * dsmp_stride;
 #pragma unroll
     for (int t = 0; t < kDenseTiles; ++t) {
-      const int b = c0 + 64 * t + col;
+      const int b = tcol(t) + col;
       if (b < nc_j) {
         drow[b] = __float_as_uint(sc[t]);
         if ((b & (kSampleStride - 1)) == 0) srow[b / kSampleStride] = __float_as_uint(sc[t]);
@@ -268,15 +280,17 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
       s_w[j][h] = ok ? wv : 0.f;
       s_wc[j][h] = ok ? wv * kScoreScale : 0.f;
     }
-    // Pre-filter bound.  The defined score and the fast one (fma chain with
-    // w*c folded in) both round non-negative terms a handful of times, so each
-    // lies within 2^-21 (relative) of c * sum_h w_h ReLU(t_h); a candidate
-    // with score >= tau therefore has fast score >= tau * (1 - 2^-19); the
-    // absolute 2^-100 covers rounding at subnormal scale.  Rows that keep
-    // every candidate pass everything (-1).
+    // Pre-filter bound.  The defined score lies within 2^-21 (relative) of
+    // the real c * sum_h w_h ReLU(t_h).  The fast score rounds each ReLU(t_h)
+    // and each w_h*c to bf16 (RNE, relative error <= 2^-9 each; bf16 keeps
+    // float32's exponent range), multiplies exactly and sums in float32, so
+    // it is >= (1 - 2^-8) times the real value.  A candidate with score >=
+    // tau therefore has fast score >= tau * (1 - 2^-7); the absolute 2^-100
+    // covers rounding at subnormal scale.  Rows that keep every candidate
+    // pass everything (-1).
     const float tau = __uint_as_float(s_th[j]);
     s_tlo[j] = (!ok || kSample) ? INFINITY
-                                : (nc <= kCandCap ? -1.f : tau * (1.f - 0x1p-19f) - 0x1p-100f);
+                                : (nc <= kCandCap ? -1.f : tau * (1.f - 0x1p-7f) - 0x1p-100f);
   }
 
   // A fragments of this wave's m-tiles (rows (wave*MT + mt)*16 + col)
@@ -294,16 +308,18 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
     }
   }
   __syncthreads();
-  f32x4 r_wc[MT];
-  float r_tlo[MT];
+  bf16x2 r_wc01[MT], r_wc23[MT];   // w_h * c as packed bf16 pairs
+  float r_ntlo[MT];   // -tau_lo
   int r_nc[MT];
   // pending entries of this lane's row (uniform over its 16-lane group):
   // each row belongs to exactly one wave, so the count needs no atomics
   int r_pc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    r_wc[mt] = s_wc[(wave * MT + mt) * 4 + grp];
-    r_tlo[mt] = s_tlo[(wave * MT + mt) * 4 + grp];
+    const f32x4 wc = s_wc[(wave * MT + mt) * 4 + grp];
+    r_wc01[mt] = __builtin_convertvector((f32x2){wc[0], wc[1]}, bf16x2);
+    r_wc23[mt] = __builtin_convertvector((f32x2){wc[2], wc[3]}, bf16x2);
+    r_ntlo[mt] = -s_tlo[(wave * MT + mt) * 4 + grp];
     r_nc[mt] = min(s_nc[(wave * MT + mt) * 4 + grp], v1);
     r_pc[mt] = 0;
   }
@@ -385,13 +401,19 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
         emit_exact(acc[mt], j, vcol, vcol * stride);
         continue;
       }
-      const f32x4 wc = r_wc[mt];
-      float fast = relu_bits(acc[mt][3]) * wc[3];
-      fast = fmaf(relu_bits(acc[mt][2]), wc[2], fast);
-      fast = fmaf(relu_bits(acc[mt][1]), wc[1], fast);
-      fast = fmaf(relu_bits(acc[mt][0]), wc[0], fast);
-      if (__ballot(fast >= r_tlo[mt])) {    // a few lanes: append raw accumulators
-        const bool pass = fast >= r_tlo[mt] && vcol < r_nc[mt];
+      // fast score on packed bf16: ReLU as a 16-bit integer max (negative
+      // patterns, -0 included, become +0), then two bf16 dot2s into float32
+      const bf16x2 p01 = __builtin_convertvector((f32x2){acc[mt][0], acc[mt][1]}, bf16x2);
+      const bf16x2 p23 = __builtin_convertvector((f32x2){acc[mt][2], acc[mt][3]}, bf16x2);
+      const s16x2 z = {0, 0};
+      const bf16x2 r01 = __builtin_bit_cast(bf16x2, __builtin_elementwise_max(__builtin_bit_cast(s16x2, p01), z));
+      const bf16x2 r23 = __builtin_bit_cast(bf16x2, __builtin_elementwise_max(__builtin_bit_cast(s16x2, p23), z));
+      // margin = fast - tau_lo (the sum starts at -tau_lo; its float32
+      // rounding, ~2^-24 of tau, is far inside the 2^-7 slack)
+      float margin = __builtin_amdgcn_fdot2_f32_bf16(r23, r_wc23[mt], r_ntlo[mt], false);
+      margin = __builtin_amdgcn_fdot2_f32_bf16(r01, r_wc01[mt], margin, false);
+      if (__ballot(margin >= 0.f)) {         // a few lanes: append raw accumulators
+        const bool pass = margin >= 0.f && vcol < r_nc[mt];
         // this lane's 16-lane group is its row: rank among the group's passes
         const uint32_t gm = (uint32_t)(__ballot(pass) >> (16 * grp)) & 0xFFFFu;
         const int slot = r_pc[mt] + __popc(gm & ((1u << col) - 1u));
@@ -517,6 +539,107 @@ __device__ uint32_t block_kth_largest(Get get, int n, int k, int nbits, int* his
   return prefix;
 }
 
+// Block-wide min and max of one value per thread (ends with a barrier).
+__device__ void block_min_max(uint32_t lo, uint32_t hi, int* tmp, uint32_t& out_lo,
+                              uint32_t& out_hi) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+  }
+  if (lane == 0) { tmp[wave] = (int)lo; tmp[4 + wave] = (int)hi; }
+  __syncthreads();
+  out_lo = min(min((uint32_t)tmp[0], (uint32_t)tmp[1]), min((uint32_t)tmp[2], (uint32_t)tmp[3]));
+  out_hi = max(max((uint32_t)tmp[4], (uint32_t)tmp[5]), max((uint32_t)tmp[6], (uint32_t)tmp[7]));
+  __syncthreads();
+}
+
+// k-th largest (1 <= k <= n) of get(0..n), keys < 2^31.  Range-adaptive
+// histogram passes: the current key range [lo, hi] (first the keys' min and
+// max) is cut into at most 2048 bins of 2^s keys, bin = (key - lo) >> s, so
+// that keys crowded in a narrow range still spread over many bins.  Each pass
+// finds the bin holding the k-th largest and narrows the range to it; a bin
+// of single values (s = 0) is the answer, and a bin of at most kFinishCap
+// keys is ranked exactly (each thread holds one key and counts the others).
+// Ends with a barrier.
+struct KthLds {
+  int* hist;       // kBins
+  uint32_t* bin;   // kFinishCap
+  int* tmp;        // 8
+  int* res;        // 2
+  int* bin_n;      // 1
+};
+
+template <class Get>
+__device__ uint32_t kth_largest_fast(Get get, int n, int k, const KthLds& sh) {
+  const int tid = threadIdx.x;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  for (int i = tid; i < n; i += 256) {
+    const uint32_t v = get(i);
+    lo = min(lo, v);
+    hi = max(hi, v);
+  }
+  block_min_max(lo, hi, sh.tmp, lo, hi);
+  for (;;) {
+    const uint32_t span = hi - lo;
+    const int s = span < (uint32_t)kBins ? 0 : 32 - __clz((int)(span >> 11));   // span >> s < 2048
+    for (int i = tid; i < kBins; i += 256) sh.hist[i] = 0;
+    if (tid == 0) *sh.bin_n = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      const uint32_t v = get(i);
+      if (v >= lo && v <= hi) atomicAdd(&sh.hist[(v - lo) >> s], 1);
+    }
+    __syncthreads();
+    constexpr int per = kBins / 256;
+    const int b0 = tid * per;
+    int local = 0;
+#pragma unroll
+    for (int b = 0; b < per; ++b) local += sh.hist[b0 + b];
+    int total;
+    const int excl = block_excl_scan_256(local, sh.tmp, total);
+    int run = total - excl - local;   // keys in the bins above this thread's
+#pragma unroll
+    for (int b = per - 1; b >= 0; --b) {
+      const int h = sh.hist[b0 + b];
+      if (run < k && run + h >= k) { sh.res[0] = b0 + b; sh.res[1] = run; }
+      run += h;
+    }
+    __syncthreads();
+    const uint32_t B = (uint32_t)sh.res[0];
+    k -= sh.res[1];
+    const int hb = sh.hist[B];
+    __syncthreads();
+    const uint32_t blo = lo + (B << s);
+    if (s == 0) return blo;
+    if (hb <= kFinishCap) {
+      const uint32_t bhi = blo + ((1u << s) - 1u);
+      for (int i = tid; i < n; i += 256) {
+        const uint32_t v = get(i);
+        if (v >= blo && v <= bhi) sh.bin[atomicAdd(sh.bin_n, 1)] = v;
+      }
+      __syncthreads();
+      if (tid < hb) {
+        const uint32_t x = sh.bin[tid];
+        int gt = 0, ge = 0;
+        for (int j = 0; j < hb; ++j) {
+          const uint32_t y = sh.bin[j];
+          gt += y > x;
+          ge += y >= x;
+        }
+        if (gt < k && k <= ge) sh.res[0] = (int)x;   // every writer has the same x
+      }
+      __syncthreads();
+      const uint32_t T = (uint32_t)sh.res[0];
+      __syncthreads();
+      return T;
+    }
+    lo = blo;
+    hi = blo + ((1u << s) - 1u);
+  }
+}
+
 // Ascending bitonic sort of 512 ints in LDS by 256 threads.
 __device__ void bitonic_sort_512(int* a) {
   for (int k2 = 2; k2 <= 512; k2 <<= 1) {
@@ -567,6 +690,8 @@ threshold_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ s
   if (ns <= kLdsSamples) {
     for (int i = threadIdx.x; i < ns; i += 256) s_smp[i] = sp[i];
     __syncthreads();
+    // 16-bit keys: two radix passes (11 + 5 bits) beat the range-adaptive
+    // search here, whose extra min/max pass buys nothing on 16-bit samples
     t16 = block_kth_largest([&](int i, bool& in) { in = true; return (uint32_t)s_smp[i]; }, ns, r,
                             16, hist, tmp, res);
   } else {
@@ -639,14 +764,16 @@ __device__ void exact_select_recompute(const uint16_t* __restrict__ q4, const fl
 // block order and -1 up to budget.  Radix select on the score key, then on
 // the block id among ties at the threshold; bitonic sort of the k ids.
 __device__ void select_from_list(const uint32_t* key, const int* idx, int c, int k, int* ids,
-                                 int* n_out, int* hist, int* tmp, int* res,
-                                 int32_t* __restrict__ out, int budget) {
+                                 int* n_out, const KthLds& lds, int32_t* __restrict__ out,
+                                 int budget) {
+  int* hist = lds.hist;
+  int* tmp = lds.tmp;
+  int* res = lds.res;
   uint32_t tau = 0, iota_cut = 0xFFFFFFFFu;
   const bool all = c == k;
   if (threadIdx.x == 0) *n_out = 0;
   if (!all) {
-    tau = block_kth_largest([&](int i, bool& in) { in = true; return key[i]; }, c, k, 31, hist,
-                            tmp, res);
+    tau = kth_largest_fast([&](int i) { return key[i]; }, c, k, lds);
     int above = 0, ties = 0;
     for (int i = threadIdx.x; i < c; i += 256) {
       above += key[i] > tau;
@@ -744,10 +871,12 @@ struct SelectShared {
   uint32_t key[kCandCap];
   int idx[kCandCap];
   int hist[kBins];
+  uint32_t bin[kFinishCap];
   int ids[kMaxBudget];
   int tmp[8];
   int res[2];
   int n_out;
+  int bin_n;
 };
 
 __global__ void __launch_bounds__(256)
@@ -781,7 +910,8 @@ final_select_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict_
     sh.idx[i] = (int)e[1];
   }
   __syncthreads();
-  select_from_list(sh.key, sh.idx, c, k, sh.ids, &sh.n_out, sh.hist, sh.tmp, sh.res, out, budget);
+  select_from_list(sh.key, sh.idx, c, k, sh.ids, &sh.n_out,
+                   KthLds{sh.hist, sh.bin, sh.tmp, sh.res, &sh.bin_n}, out, budget);
   if (threadIdx.x == 0) sel_count[row] = k;
 }
 
@@ -805,7 +935,6 @@ final_select_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict_
 constexpr int kDenseList = 2560;
 constexpr int kDenseExtra = 768;
 constexpr int kDensePassQ = 8192;   // quads per pass (32768 scores; 32 per thread)
-constexpr int kFinishCap = 256;
 
 struct DenseShared {
   u32x4 rowq[kDensePassQ];
@@ -824,94 +953,14 @@ struct DenseShared {
   int bin_n;
 };
 
-// Block-wide min and max of one value per thread (ends with a barrier).
-__device__ void block_min_max(uint32_t lo, uint32_t hi, int* tmp, uint32_t& out_lo,
-                              uint32_t& out_hi) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
-  }
-  if (lane == 0) { tmp[wave] = (int)lo; tmp[4 + wave] = (int)hi; }
-  __syncthreads();
-  out_lo = min(min((uint32_t)tmp[0], (uint32_t)tmp[1]), min((uint32_t)tmp[2], (uint32_t)tmp[3]));
-  out_hi = max(max((uint32_t)tmp[4], (uint32_t)tmp[5]), max((uint32_t)tmp[6], (uint32_t)tmp[7]));
-  __syncthreads();
-}
-
-// k-th largest (1 <= k <= n) of get(0..n), keys < 2^31.  The keys' range
-// [lo, hi] is cut into at most 2048 bins of 2^s patterns (bin = (key-lo)>>s),
-// so that keys crowded in a narrow range still spread over many bins; one
-// histogram pass finds the boundary bin, whose keys are then ranked exactly
-// (each thread holds one and counts the others) when there are at most
-// kFinishCap of them, else the full radix select runs.  Ends with a barrier.
-template <class Get>
-__device__ uint32_t kth_largest_fast(Get get, int n, int k, DenseShared& sh) {
-  const int tid = threadIdx.x;
-  uint32_t lo = 0xFFFFFFFFu, hi = 0;
-  for (int i = tid; i < n; i += 256) {
-    const uint32_t v = get(i);
-    lo = min(lo, v);
-    hi = max(hi, v);
-  }
-  for (int i = tid; i < kBins; i += 256) sh.hist[i] = 0;
-  if (tid == 0) sh.bin_n = 0;
-  block_min_max(lo, hi, sh.tmp, lo, hi);
-  const uint32_t span = hi - lo;
-  const int s = span < (uint32_t)kBins ? 0 : 32 - __clz((int)(span >> 11));   // span >> s < 2048
-  for (int i = tid; i < n; i += 256) atomicAdd(&sh.hist[(get(i) - lo) >> s], 1);
-  __syncthreads();
-  constexpr int per = kBins / 256;
-  const int b0 = tid * per;
-  int local = 0;
-#pragma unroll
-  for (int b = 0; b < per; ++b) local += sh.hist[b0 + b];
-  int total;
-  const int excl = block_excl_scan_256(local, sh.tmp, total);
-  int run = total - excl - local;   // keys in the bins above this thread's
-#pragma unroll
-  for (int b = per - 1; b >= 0; --b) {
-    const int h = sh.hist[b0 + b];
-    if (run < k && run + h >= k) { sh.res[0] = b0 + b; sh.res[1] = run; }
-    run += h;
-  }
-  __syncthreads();
-  const uint32_t B = (uint32_t)sh.res[0];
-  const int kk = k - sh.res[1];
-  const int hb = sh.hist[B];
-  __syncthreads();
-  if (hb > kFinishCap)
-    return block_kth_largest([&](int i, bool& in) { in = true; return get(i); }, n, k, 31,
-                             sh.hist, sh.tmp, sh.res);
-  for (int i = tid; i < n; i += 256) {
-    const uint32_t v = get(i);
-    if (((v - lo) >> s) == B) sh.bin[atomicAdd(&sh.bin_n, 1)] = v;
-  }
-  __syncthreads();
-  if (tid < hb) {
-    const uint32_t x = sh.bin[tid];
-    int gt = 0, ge = 0;
-    for (int j = 0; j < hb; ++j) {
-      const uint32_t y = sh.bin[j];
-      gt += y > x;
-      ge += y >= x;
-    }
-    if (gt < kk && kk <= ge) sh.res[0] = (int)x;   // every writer has the same x
-  }
-  __syncthreads();
-  const uint32_t T = (uint32_t)sh.res[0];
-  __syncthreads();
-  return T;
-}
-
 // Exact top-k of the LDS list (key, pos) of c entries in block order,
 // emitted in list order to out[0..k), -1 up to budget.
 __device__ void select_dense_list(int c, int k, DenseShared& sh, int32_t* __restrict__ out,
                                   int budget) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t tau =
-      k >= c ? 0u : kth_largest_fast([&](int i) { return sh.u.l.key[i]; }, c, k, sh);
+      k >= c ? 0u : kth_largest_fast([&](int i) { return sh.u.l.key[i]; }, c, k,
+                                     KthLds{sh.hist, sh.bin, sh.tmp, sh.res, &sh.bin_n});
   const int per = (c + 255) / 256 * 64;
   const int s0 = min(c, wave * per), s1 = min(c, s0 + per);
   int a = 0, t = 0;
@@ -1004,9 +1053,11 @@ select_dense_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict_
     for (int j = 0; j < 8; ++j)
       if (256 * j + tid < ns) sh.u.smp[256 * j + tid] = sv[j];
     __syncthreads();
-    tau_s = kth_largest_fast([&](int i) { return sh.u.smp[i]; }, ns, r, sh);
+    tau_s = kth_largest_fast([&](int i) { return sh.u.smp[i]; }, ns, r,
+                             KthLds{sh.hist, sh.bin, sh.tmp, sh.res, &sh.bin_n});
   } else {
-    tau_s = kth_largest_fast([&](int i) { return srow[i]; }, ns, r, sh);
+    tau_s = kth_largest_fast([&](int i) { return srow[i]; }, ns, r,
+                             KthLds{sh.hist, sh.bin, sh.tmp, sh.res, &sh.bin_n});
   }
 
   // compaction; tau_s = 0 would pass every score (more than the list holds)

@@ -4,7 +4,8 @@ Headline (`value`): chunked prefill at 1M context -- a 32,768-token query
 chunk on a 1,015,808-token cached prefix (batch 1, budget 512 blocks + tail):
 query tokens per second for one step = pool the chunk's new blocks, select
 blocks for every query, sparse attention.  Alongside it (`decode`): a decode
-step for 32 sequences of 131,072 cached tokens + the new one.
+step for 32 sequences of 131,072 cached tokens + the new one; and
+(`mtp_decode`) a multi-token decode step with 4 query tokens per sequence.
 
 Inputs are seeded synthetic tensors generated directly in HBM; the timed
 region starts with everything resident.  Timing uses HIP events on the stream
@@ -16,7 +17,7 @@ duration, against 8 TB/s, with the counted HBM-side bytes beside it
 times the CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--only prefill|decode]
+                    [--only prefill|decode|mtp]
 """
 import argparse
 import hashlib
@@ -129,19 +130,21 @@ def time_prefill(args):
     return res
 
 
-def time_decode(args):
+def time_decode(args, mtp=False):
+    """Decode step (one query per sequence), or with mtp=True a multi-token
+    decode step (4 query tokens per sequence)."""
     import torch
     from block_sparse_long_02_amd import workloads as W
     from block_sparse_long_02_amd.runner import QSARunner
 
     t0 = time.time()
-    b = W.decode_128k(device="cuda")
+    b = W.mtp_decode_128k(device="cuda") if mtp else W.decode_128k(device="cuda")
     r = QSARunner(b)
     # 512 MB > MALL, swept by a read before each step so that the step starts
     # with none of its data cached and no dirty lines to write back
     flush = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
-    log(f"decode workload ready in {time.time() - t0:.1f}s")
+    log(f"{'mtp ' if mtp else ''}decode workload ready in {time.time() - t0:.1f}s")
     for _ in range(args.warmup):
         r.step()
     # a decode step is replayed from a HIP graph, as a serving loop would;
@@ -169,10 +172,13 @@ def time_decode(args):
     ms = timed([g_step])[0]
     sel_ms, att_ms = timed([g_sel, g_att])
     sum_s, sum_nc = set_sizes(r)
-    n_seq = r.n_seq
-    step_bytes = sum_nc * BLOCK_KEY_BYTES + sum_s * TOKEN_GATHER_BYTES + n_seq * (
+    n_seq, n_q = r.n_seq, r.n_q
+    # block keys once per sequence (its queries are scored together), each
+    # query row's own gather, queries in and out
+    blocks_read = sum(L // 4 for L in b.seq_lens_host())
+    step_bytes = blocks_read * BLOCK_KEY_BYTES + sum_s * TOKEN_GATHER_BYTES + n_q * (
         2 * Q_ROW_BYTES + 4 * 128 * 2 + 16)
-    return dict(value=n_seq / (ms * 1e-3), ms_per_step=ms,
+    return dict(value=n_q / (ms * 1e-3), ms_per_step=ms,
                 stages_ms=dict(select=sel_ms, attend=att_ms),
                 hbm=dict(bytes=step_bytes, gbs=step_bytes / (ms * 1e-3) / 1e9),
                 runner=r, batch=b)
@@ -237,7 +243,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "mtp"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the QSA path here is "
@@ -252,7 +258,7 @@ def main():
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic"}
-    if args.only != "decode":
+    if args.only in (None, "prefill"):
         pre = time_prefill(args)
         log(f"prefill: {pre['ms_per_step']:.3f} ms/step, stages {pre['stages_ms']}")
         attend_file = os.path.join(ROOT, "block_sparse_long_02_amd", "csrc", "qsa_attend.hip")
@@ -297,7 +303,7 @@ def main():
             out["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
         del pre
         torch.cuda.empty_cache()
-    if args.only != "prefill":
+    if args.only in (None, "decode"):
         dec = time_decode(args)
         log(f"decode: {dec['ms_per_step']:.4f} ms/step, stages {dec['stages_ms']}")
         d = {"value": round(dec["value"], 1), "unit": "tokens/s",
@@ -315,6 +321,26 @@ def main():
                        config=d["config"], roofline=d["roofline"])
         else:
             out["decode"] = d
+    dec = None
+    torch.cuda.empty_cache()
+    if args.only in (None, "mtp"):
+        mt = time_decode(args, mtp=True)
+        log(f"mtp decode: {mt['ms_per_step']:.4f} ms/step, stages {mt['stages_ms']}")
+        m = {"value": round(mt["value"], 1), "unit": "tokens/s",
+             "ms_per_step": round(mt["ms_per_step"], 4),
+             "config": {"workload": "multi-token decode: 32 sequences x (131072 cached + 4 new) "
+                                    "tokens, 4 query tokens each (a new token and 3 speculative), "
+                                    "budget 512 blocks + tail, MALL flushed before each step"},
+             "roofline": {"bound": "hbm", "scope": "whole step",
+                          "achieved": round(mt["hbm"]["gbs"], 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(mt["hbm"]["gbs"] / HBM_PEAK_GBS, 4),
+                          "algorithmic_bytes": mt["hbm"]["bytes"]},
+             "stages_ms": {k: round(v, 4) for k, v in mt["stages_ms"].items()}}
+        if args.only == "mtp":
+            out.update(value=m["value"], unit="tokens/s", ms_per_step=m["ms_per_step"],
+                       config=m["config"], roofline=m["roofline"])
+        else:
+            out["mtp_decode"] = m
     print(json.dumps(out), flush=True)
 
 

@@ -410,6 +410,37 @@ int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_le
   return qsa_host::launch_status();
 }
 
+size_t qsa_attend_decode_multi_workspace(int32_t n_q) {
+  if (n_q <= 0) return 0;
+  return (size_t)n_q * 2 * kDecodeSplits * qsa::kPartFloats * sizeof(float);
+}
+
+int qsa_attend_decode_multi(const void* q, const int32_t* cu_q, const int32_t* seq_len,
+                            int32_t n_seq, int32_t n_q, const void* k_cache, const void* v_cache,
+                            int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
+                            const int32_t* sel_count, int32_t budget, void* out, float* lse,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  using namespace qsa_host;
+  if (n_q < 0 || n_seq < 0) return QSA_ERR_INVALID_ARG;
+  if (n_q == 0) return QSA_OK;
+  if (n_seq == 0 || !cu_q || !seq_len) return QSA_ERR_INVALID_ARG;
+  int st = check_attend_common(q, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
+                               budget, out);
+  if (st != QSA_OK) return st;
+  if (!workspace || !aligned16(workspace)) return QSA_ERR_INVALID_ARG;
+  if (ws_bytes < qsa_attend_decode_multi_workspace(n_q)) return QSA_ERR_WORKSPACE_TOO_SMALL;
+  if ((int64_t)n_q * 2 * kDecodeSplits > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  float* part = (float*)workspace;
+  hipLaunchKernelGGL(qsa::attend_kernel<false>, dim3(n_q * 2 * kDecodeSplits), dim3(256), 0,
+                     (hipStream_t)stream, (const uint16_t*)q, cu_q, seq_len, n_seq, n_q,
+                     (const uint16_t*)k_cache, (const uint16_t*)v_cache, kv_seq_stride,
+                     kv_head_stride, sel, sel_count, budget, kDecodeSplits, 0,
+                     (uint16_t*)nullptr, (float*)nullptr, part);
+  hipLaunchKernelGGL(qsa::combine_kernel<kDecodeSplits>, dim3(n_q * 2 * qsa::kGroup), dim3(256), 0,
+                     (hipStream_t)stream, (const float*)part, n_q, (uint16_t*)out, lse);
+  return launch_status();
+}
+
 size_t qsa_attend_decode_workspace(int32_t n_seq) {
   if (n_seq <= 0) return 0;
   return (size_t)n_seq * 2 * kDecodeSplits * qsa::kPartFloats * sizeof(float);

@@ -42,6 +42,10 @@ SIGNATURES = {
     "qsa_attend_decode": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i64, _i64,
                                          _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p,
                                          _size, _c_void_p]),
+    "qsa_attend_decode_multi_workspace": (_size, [_i32]),
+    "qsa_attend_decode_multi": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
+                                               _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32,
+                                               _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
 }
 
 _lib = None
@@ -151,3 +155,19 @@ def attend_decode(q, seq_len, k_cache, v_cache, sel, sel_count, budget, out, lse
                                  int(budget), _p(out), _p(lse), _p(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream))
     _check("qsa_attend_decode", st)
+
+
+def attend_decode_multi_workspace(n_q) -> int:
+    return int(lib().qsa_attend_decode_multi_workspace(int(n_q)))
+
+
+def attend_decode_multi(q, cu_q, seq_len, k_cache, v_cache, sel, sel_count, budget, out, lse,
+                        workspace, stream=None):
+    _dev(q, cu_q, seq_len, k_cache, v_cache, sel, sel_count, out, lse, workspace)
+    st = lib().qsa_attend_decode_multi(_p(q), _p(cu_q), _p(seq_len), seq_len.numel(), q.shape[0],
+                                       _p(k_cache), _p(v_cache), k_cache.stride(0),
+                                       k_cache.stride(1), _p(sel), _p(sel_count), int(budget),
+                                       _p(out), _p(lse), _p(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream))
+    _check("qsa_attend_decode_multi", st)

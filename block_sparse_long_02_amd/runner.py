@@ -19,6 +19,8 @@ class QSARunner:
         assert b.idx_q.is_cuda, "batch must live on the GPU"
         self.b = b
         self.decode = (b.meta.get("kind") == "decode") if decode is None else decode
+        # several query tokens per sequence, attended with the split-K decode
+        self.mtp = b.meta.get("kind") == "mtp_decode" and not self.decode
         dev = b.idx_q.device
         lens = b.seq_lens_host()
         cu = b.cu_q_host()
@@ -53,7 +55,8 @@ class QSARunner:
         self.lse = torch.empty((self.n_q, 24), dtype=torch.float32, device=dev)
         ws = qsa.index_select_workspace(self.n_q, self.max_q_len, self.max_blocks)
         self.ws_index = torch.empty((max(ws, 16),), dtype=torch.uint8, device=dev)
-        wsd = qsa.attend_decode_workspace(self.n_seq) if self.decode else 16
+        wsd = (qsa.attend_decode_workspace(self.n_seq) if self.decode else
+               qsa.attend_decode_multi_workspace(self.n_q) if self.mtp else 16)
         self.ws_decode = torch.empty((max(wsd, 16),), dtype=torch.uint8, device=dev)
 
     # the three calls of a step ------------------------------------------
@@ -73,6 +76,10 @@ class QSARunner:
         if self.decode:
             qsa.attend_decode(b.q, b.seq_len, self.k_cache, self.v_cache, self.sel, self.sel_count,
                               self.budget, self.out, self.lse, self.ws_decode, stream=stream)
+        elif self.mtp:
+            qsa.attend_decode_multi(b.q, b.cu_q, b.seq_len, self.k_cache, self.v_cache, self.sel,
+                                    self.sel_count, self.budget, self.out, self.lse, self.ws_decode,
+                                    stream=stream)
         else:
             qsa.attend_prefill(b.q, b.cu_q, b.seq_len, self.max_q_len, self.k_cache, self.v_cache,
                                self.sel, self.sel_count, self.budget, self.out, self.lse,

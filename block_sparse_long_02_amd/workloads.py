@@ -294,6 +294,56 @@ def make_decode(*, seq_lens, budget: int, n_plant: int, seed: int, device="cpu",
                   exact_grid=exact_grid))
 
 
+def make_mtp_decode(*, seq_lens, q_len: int, budget: int, n_plant: int, seed: int,
+                    device="cpu", exact_grid: bool = False) -> QSABatch:
+    """Multi-token decode: q_len query tokens per sequence at its last positions
+    (a new token plus speculative ones).  The tokens of sequence s share a
+    random unit direction u_s: their indexer queries are N(0,1) + 8 u_s, and
+    n_plant blocks completed before the first of them get token keys
+    sqrt(128) u_s + 0.1 N(0,1)."""
+    device = torch.device(device)
+    gh = torch.Generator(device="cpu")
+    gh.manual_seed(seed)
+    gd = torch.Generator(device=device)
+    gd.manual_seed(seed + 7919)
+    lens = [int(x) for x in seq_lens]
+    assert all(L >= q_len for L in lens)
+    n_seq = len(lens)
+    n_q = n_seq * q_len
+    l_cap = _cap(max(lens))
+    idx_q_f = torch.randn((n_q, H_I, D_I), generator=gd, device=device, dtype=torch.float32)
+    idx_k = torch.empty((n_seq, l_cap, D_I), dtype=torch.bfloat16, device=device)
+    planted = []
+    for s in range(n_seq):
+        u = _unit(torch.randn((D_I,), generator=gh, dtype=torch.float64))
+        idx_q_f[s * q_len:(s + 1) * q_len] += 8.0 * u.to(device)[None, None, :]
+        kf = torch.zeros((l_cap, D_I), dtype=torch.float32, device=device)
+        for t0 in range(0, lens[s], _KV_CHUNK):
+            t1 = min(lens[s], t0 + _KV_CHUNK)
+            kf[t0:t1] = torch.randn((t1 - t0, D_I), generator=gd, device=device,
+                                    dtype=torch.float32)
+        n_avail = (lens[s] - q_len + 1) // R
+        n_p = min(n_plant, n_avail)
+        blocks = sorted(torch.randperm(n_avail, generator=gh)[:n_p].tolist()) if n_avail else []
+        _plant_tokens(kf, blocks, u, math.sqrt(D_I), 0.1, gd)
+        planted.append(blocks)
+        if exact_grid:
+            kf = _snap_grid(kf)
+        kf[lens[s]:] = 0.0
+        idx_k[s] = kf.to(torch.bfloat16)
+    if exact_grid:
+        idx_q_f = _snap_grid(idx_q_f)
+    w = _head_weights(n_q, gd, device, exact_grid)
+    q, k, v = _core_tensors(n_q, lens, l_cap, gd, device)
+    return QSABatch(
+        seq_len=torch.tensor(lens, dtype=torch.int32, device=device),
+        cu_q=torch.arange(0, n_q + 1, q_len, dtype=torch.int32, device=device),
+        idx_q=idx_q_f.to(torch.bfloat16).contiguous(), w=w, idx_k=idx_k.contiguous(), q=q, k=k,
+        v=v, budget=budget, planted=planted,
+        meta=dict(kind="mtp_decode", q_len=q_len, n_plant=n_plant, seed=seed,
+                  exact_grid=exact_grid))
+
+
 def ragged_lengths(n_seq: int, lo: int, hi: int, seed: int) -> list[int]:
     """Lengths 4*floor(X/4) + d, X log-uniform in [lo, hi], d in {1,2,3}."""
     g = torch.Generator(device="cpu")
@@ -331,6 +381,13 @@ def chunked_prefill_1m(device="cpu", seed=1003, prefix=1015808, chunk=32768, exa
     """Chunked prefill: a 32768-token chunk on a 1,015,808-token cached prefix."""
     return make_prefill(prefix=prefix, chunk=chunk, budget=512, seg=1024, n_plant=64,
                         seed=seed, device=device, distance="loguniform", exact_grid=exact_grid)
+
+
+def mtp_decode_128k(device="cpu", seed=1005, n_seq=32, ctx=131072, q_len=4, exact_grid=False):
+    """Multi-token decode: n_seq sequences of ctx cached tokens plus q_len new ones
+    (a new token and q_len - 1 speculative tokens), 32 planted blocks each."""
+    return make_mtp_decode(seq_lens=[ctx + q_len] * n_seq, q_len=q_len, budget=512, n_plant=32,
+                           seed=seed, device=device, exact_grid=exact_grid)
 
 
 def ragged_decode(device="cpu", seed=1004, n_seq=8, lo=4096, hi=1048572, exact_grid=False):

@@ -191,6 +191,24 @@ int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq,
                       const int32_t* sel, const int32_t* sel_count, int32_t budget,
                       void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * f1 (multi-token decode) -- the split-K decode of qsa_attend_decode for a
+ * varlen batch with a few query tokens per sequence, e.g. a new token plus
+ * speculative (MTP) tokens: [ailearn] performance box (decode measured with 3
+ * MTP steps).  Batch layout, mathematics and outputs as qsa_attend_prefill
+ * (rows cu_q[s] .. cu_q[s+1]-1 at the last positions of sequence s); each
+ * row's selected set is split across workgroups and combined as in
+ * qsa_attend_decode.  Needs qsa_attend_decode_multi_workspace(n_q) bytes.
+ */
+size_t qsa_attend_decode_multi_workspace(int32_t n_q);
+int qsa_attend_decode_multi(const void* q, const int32_t* cu_q, const int32_t* seq_len,
+                            int32_t n_seq, int32_t n_q,
+                            const void* k_cache, const void* v_cache,
+                            int64_t kv_seq_stride, int64_t kv_head_stride,
+                            const int32_t* sel, const int32_t* sel_count, int32_t budget,
+                            void* out, float* lse, void* workspace, size_t ws_bytes,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
         assert n in qsa.SIGNATURES, n
@@ -59,6 +59,8 @@ def test_workspace_queries(L):
     assert dense >= 32 * (1 << 15) * 4
     assert L.qsa_attend_decode_workspace(0) == 0
     assert L.qsa_attend_decode_workspace(32) >= 32 * 2 * 12 * 256 * 4
+    assert L.qsa_attend_decode_multi_workspace(0) == 0
+    assert L.qsa_attend_decode_multi_workspace(128) >= 128 * 2 * 12 * 256 * 4
 
 
 def _select(L, **kw):
@@ -96,6 +98,10 @@ def test_attention_and_pool_reject_bad_arguments(L):
     assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 100, None) == 3
     assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 600, A, A, A, 1 << 30, None) == 1
     assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, MISALIGNED, 1 << 30, None) == 1
+    # multi-token decode: cu_q required, workspace sized by n_q
+    assert L.qsa_attend_decode_multi(A, None, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, None) == 1
+    assert L.qsa_attend_decode_multi(A, A, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 100, None) == 3
+    assert L.qsa_attend_decode_multi(A, A, A, 2, 0, A, A, 1024, 512, A, A, 16, A, A, A, 0, None) == 0
     # pooling and rope
     assert L.qsa_pool_block_keys(None, 128, A, 128, A, A, 1, 4, None) == 1
     assert L.qsa_pool_block_keys(A, 129, A, 128, A, A, 1, 4, None) == 1

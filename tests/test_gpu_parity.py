@@ -326,6 +326,37 @@ def test_end_to_end_ragged_decode_reduced():
     print("ragged decode:", kinds, f"worst rel-L2 {worst:.2e}")
 
 
+# ------------------------------------------------------- multi-token decode
+
+def test_mtp_decode_selection_exact_grid():
+    # 4 query tokens per sequence; the last one completes a new block for the
+    # first sequence (position 4k+3) and not for the others
+    b = W.make_mtp_decode(seq_lens=[4 * 10000 + 4, 70003, 130005], q_len=4, budget=512,
+                          n_plant=32, seed=51, exact_grid=True)
+    _select_and_check(b, exact=True)
+
+
+def test_end_to_end_mtp_decode_reduced():
+    b = W.mtp_decode_128k(n_seq=5, ctx=20000)
+    kinds, worst = _end_to_end(b, range(b.n_q))
+    print("mtp decode:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_attend_decode_multi_matches_prefill_kernel():
+    # split-K over a varlen batch equals the one-workgroup prefill kernel on
+    # the same selections (also 1 and 3 tokens per sequence)
+    b = W.make_mtp_decode(seq_lens=[9001, 40003, 7], q_len=3, budget=512, n_plant=16, seed=52)
+    r = QSARunner(b.to("cuda"))
+    r.step()
+    _sync()
+    out_m, lse_m = r.out.clone(), r.lse.clone()
+    qsa.attend_prefill(r.b.q, r.b.cu_q, r.b.seq_len, r.max_q_len, r.k_cache, r.v_cache, r.sel,
+                       r.sel_count, r.budget, r.out, r.lse)
+    _sync()
+    assert (r.out.float() - out_m.float()).abs().max().item() <= 2e-3
+    assert (r.lse - lse_m).abs().max().item() <= 1e-4
+
+
 # ------------------------------------------------------------- HIP graphs
 
 def test_graph_replays_match_eager():

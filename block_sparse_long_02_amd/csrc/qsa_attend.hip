@@ -23,19 +23,7 @@
 
 namespace qsa {
 
-#ifndef QSA_ATTEND_XCD_REMAP
-#define QSA_ATTEND_XCD_REMAP 0
-#endif
-
-// micro-blocks per tile (4 or 8): a tile is 1 or 2 halves of 16 tokens
-#ifndef QSA_ATTEND_TILE
-#define QSA_ATTEND_TILE 8
-#endif
-// waves per SIMD the attention kernel is compiled for
-#ifndef QSA_ATTEND_OCC
-#define QSA_ATTEND_OCC 2
-#endif
-constexpr int kTileMB = QSA_ATTEND_TILE;
+constexpr int kTileMB = 8;                    // micro-blocks per tile (two 16-token halves)
 constexpr int kHalves = kTileMB / 4;
 constexpr int kWaves = 4;
 constexpr int kMaxList = kMaxBudget + 1;      // selected blocks + tail block
@@ -69,7 +57,7 @@ struct AttnShared {
 // mode kFinal: one workgroup per (row, KV head) writes out / lse.
 // otherwise: n_splits workgroups per (row, KV head) write partials.
 template <bool kFinal>
-__global__ void __launch_bounds__(256, QSA_ATTEND_OCC)
+__global__ void __launch_bounds__(256, 2)
 attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
               const int32_t* __restrict__ seq_len, int n_seq, int n_rows,
               const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
@@ -81,15 +69,7 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
 
-  // Optionally remap workgroup ids so that each of the 8 XCDs (dispatched
-  // round-robin, each with its own L2) works on a contiguous range of rows.
-  // Off by default: measured slower, since most reuse of the gathered blocks
-  // comes from the shared MALL, which favours all XCDs working on nearby rows.
-#if QSA_ATTEND_XCD_REMAP
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-#else
   const int wg = blockIdx.x;
-#endif
   const int split = wg % n_splits;
   const int g = (wg / n_splits) & 1;
   const int row = wg / (2 * n_splits);
@@ -183,22 +163,32 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   for (int n = 0; n < 16; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int base = t * kTileMB;
-    // Half hv covers micro-blocks base + 4hv .. +3.  K rows: lane is token
-    // row `col` of the half; V / P k-slices: micro-block base + 4hv + grp.
-    u32x4 kh[kHalves][8], vh[kHalves][8];
+  // Half hv of tile t covers micro-blocks t*kTileMB + 4hv .. +3.  K rows:
+  // lane is token row `col` of the half; V / P k-slices: micro-block
+  // t*kTileMB + 4hv + grp.
+  u32x4 kh[kHalves][8], vh[kHalves][8];
+  auto load_k = [&](int t) {
 #pragma unroll
     for (int hv = 0; hv < kHalves; ++hv) {
-      const int idk = sh.list[min(base + 4 * hv + (col >> 2), n_mb - 1)];
-      const int idv = sh.list[min(base + 4 * hv + grp, n_mb - 1)];
+      const int idk = sh.list[min(t * kTileMB + 4 * hv + (col >> 2), n_mb - 1)];
       const uint16_t* kp = kbase + ((int64_t)idk * kBlock + (col & 3)) * kHeadDim + 8 * grp;
-      const uint16_t* vp = vbase + (int64_t)idv * (kBlock * kHeadDim) + 8 * col;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) kh[hv][ks] = ldg16(kp + 32 * ks);
+    }
+  };
+  auto load_v = [&](int t) {
+#pragma unroll
+    for (int hv = 0; hv < kHalves; ++hv) {
+      const int idv = sh.list[min(t * kTileMB + 4 * hv + grp, n_mb - 1)];
+      const uint16_t* vp = vbase + (int64_t)idv * (kBlock * kHeadDim) + 8 * col;
 #pragma unroll
       for (int c = 0; c < 8; ++c) vh[hv][c] = ldg16(vp + 128 * c);
     }
+  };
+  for (int t = t_begin; t < t_end; ++t) {
+    const int base = t * kTileMB;
+    load_k(t);
+    load_v(t);
 
     // sc[hv][i]: token i of micro-block slot base + 4hv + grp, head col
     f32x4 sc[kHalves];
@@ -206,7 +196,8 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     for (int hv = 0; hv < kHalves; ++hv) {
       sc[hv] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) sc[hv] = mfma_16x16x32(kh[hv][ks], qf[ks], sc[hv]);
+      for (int ks = 0; ks < 8; ++ks)
+        sc[hv] = mfma_16x16x32(kh[hv][ks], qf[ks], sc[hv]);
     }
     float x[4 * kHalves];
 #pragma unroll
@@ -261,7 +252,7 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     ps += __shfl_xor(ps, 32, 64);
     l_run += ps;
 
-    if constexpr (kHalves == 2) {
+    {
       // P k-slice of 8 tokens (2 micro-blocks) per lane: MFMA 16x16x32
       u32x4 pa;
       pa[0] = pack_bf16x2(p[0], p[1]);
@@ -275,18 +266,6 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
         u32x4 bo = {vh[0][c][2], vh[0][c][3], vh[1][c][2], vh[1][c][3]};
         o[2 * c] = mfma_16x16x32(pa, be, o[2 * c]);
         o[2 * c + 1] = mfma_16x16x32(pa, bo, o[2 * c + 1]);
-      }
-    } else {
-      // P k-slice of 4 tokens (1 micro-block) per lane: MFMA 16x16x16
-      u32x2 pa;
-      pa[0] = pack_bf16x2(p[0], p[1]);
-      pa[1] = pack_bf16x2(p[2], p[3]);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        u32x2 be = {vh[0][c][0], vh[0][c][1]};
-        u32x2 bo = {vh[0][c][2], vh[0][c][3]};
-        o[2 * c] = mfma_16x16x16(pa, be, o[2 * c]);
-        o[2 * c + 1] = mfma_16x16x16(pa, bo, o[2 * c + 1]);
       }
     }
   }

@@ -51,31 +51,12 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// D(16x16, f32) += A(16x16, bf16) * B(16x16, bf16).  Lane l supplies
-// A[l%16][4*(l/16) .. +3] and B[4*(l/16) .. +3][l%16]; it receives
-// D[4*(l/16) + i][l%16] for i = 0..3.
-__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
-
 // Rotary inverse frequency 1e7^(-j/32) of rotation pair j (float64).
 __device__ __forceinline__ double rope_inv_freq(int j) {
   return pow(1.0e7, -(double)j / (double)(kRopeDim / 2));
 }
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
-
-// Map a hardware workgroup id (dispatched round-robin over the 8 XCDs of an
-// MI355X) to a logical id such that each XCD receives a contiguous range of
-// logical ids.  A bijection on [0, n): the first (n % 8) XCDs take one extra.
-__device__ __forceinline__ int xcd_remap(int hw, int n) {
-  constexpr int kXcds = 8;
-  const int xcd = hw % kXcds, k = hw / kXcds;
-  const int q = n / kXcds, r = n % kXcds;
-  return xcd * q + min(xcd, r) + k;
-}
 
 // --------------------------------------------------------- block helpers
 // Exclusive prefix sum over a 256-thread workgroup.  `tmp` holds >= 4 ints of

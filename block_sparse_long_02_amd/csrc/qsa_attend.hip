@@ -99,6 +99,46 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   }
   const int n_mb = cnt + (tail_len > 0 ? 1 : 0);
 
+  // ---- this wave's tiles
+  const int n_tiles = (n_mb + kTileMB - 1) / kTileMB;
+  const int parts = n_splits * kWaves;
+  const int my_part = split * kWaves + wave;
+  // even split: part p takes tiles [p*n/parts, (p+1)*n/parts)
+  const int t_begin = (int)((int64_t)my_part * n_tiles / parts);
+  const int t_end = (int)((int64_t)(my_part + 1) * n_tiles / parts);
+  const int tail_slot = tail_len > 0 ? cnt : -1;
+
+  const uint16_t* kbase = kc + (int64_t)s * seq_stride + (int64_t)g * head_stride;
+  const uint16_t* vbase = vc + (int64_t)s * seq_stride + (int64_t)g * head_stride;
+  const float scale = kLog2e / 16.0f;
+
+  f32x4 o[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Half hv of tile t covers micro-blocks t*kTileMB + 4hv .. +3.  K rows:
+  // lane is token row `col` of the half; V / P k-slices: micro-block
+  // t*kTileMB + 4hv + grp.
+  u32x4 kh[kHalves][8], vh[kHalves][8];
+  auto load_k = [&](int t) {
+#pragma unroll
+    for (int hv = 0; hv < kHalves; ++hv) {
+      const int idk = sh.list[min(t * kTileMB + 4 * hv + (col >> 2), n_mb - 1)];
+      const uint16_t* kp = kbase + ((int64_t)idk * kBlock + (col & 3)) * kHeadDim + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kh[hv][ks] = ldg16(kp + 32 * ks);
+    }
+  };
+  auto load_v = [&](int t) {
+#pragma unroll
+    for (int hv = 0; hv < kHalves; ++hv) {
+      const int idv = sh.list[min(t * kTileMB + 4 * hv + grp, n_mb - 1)];
+      const uint16_t* vp = vbase + (int64_t)idv * (kBlock * kHeadDim) + 8 * col;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) vh[hv][c] = ldg16(vp + 128 * c);
+    }
+  };
   // ---- block list and the query's rotary angles into LDS
   for (int i = threadIdx.x; i < cnt; i += 256) {
     int id = sel[(int64_t)row * budget + i];
@@ -145,46 +185,6 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     if (col < kGroup) { qf[0] = r0; qf[1] = r1; }
   }
 
-  // ---- this wave's tiles
-  const int n_tiles = (n_mb + kTileMB - 1) / kTileMB;
-  const int parts = n_splits * kWaves;
-  const int my_part = split * kWaves + wave;
-  const int per = (n_tiles + parts - 1) / parts;
-  const int t_begin = my_part * per;
-  const int t_end = min(n_tiles, t_begin + per);
-  const int tail_slot = tail_len > 0 ? cnt : -1;
-
-  const uint16_t* kbase = kc + (int64_t)s * seq_stride + (int64_t)g * head_stride;
-  const uint16_t* vbase = vc + (int64_t)s * seq_stride + (int64_t)g * head_stride;
-  const float scale = kLog2e / 16.0f;
-
-  f32x4 o[16];
-#pragma unroll
-  for (int n = 0; n < 16; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // Half hv of tile t covers micro-blocks t*kTileMB + 4hv .. +3.  K rows:
-  // lane is token row `col` of the half; V / P k-slices: micro-block
-  // t*kTileMB + 4hv + grp.
-  u32x4 kh[kHalves][8], vh[kHalves][8];
-  auto load_k = [&](int t) {
-#pragma unroll
-    for (int hv = 0; hv < kHalves; ++hv) {
-      const int idk = sh.list[min(t * kTileMB + 4 * hv + (col >> 2), n_mb - 1)];
-      const uint16_t* kp = kbase + ((int64_t)idk * kBlock + (col & 3)) * kHeadDim + 8 * grp;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) kh[hv][ks] = ldg16(kp + 32 * ks);
-    }
-  };
-  auto load_v = [&](int t) {
-#pragma unroll
-    for (int hv = 0; hv < kHalves; ++hv) {
-      const int idv = sh.list[min(t * kTileMB + 4 * hv + grp, n_mb - 1)];
-      const uint16_t* vp = vbase + (int64_t)idv * (kBlock * kHeadDim) + 8 * col;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) vh[hv][c] = ldg16(vp + 128 * c);
-    }
-  };
   for (int t = t_begin; t < t_end; ++t) {
     const int base = t * kTileMB;
     load_k(t);

@@ -1207,7 +1207,10 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
   const int64_t tiles_per_seq = (max_q_len + qt - 1) / qt;
   const int64_t gx = tiles_per_seq * n_seq;
   if (gx > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
-  constexpr int chunk = 1024;
+#ifndef QSA_PREFILL_CHUNK
+#define QSA_PREFILL_CHUNK 2048
+#endif
+  constexpr int chunk = QSA_PREFILL_CHUNK;   // candidate blocks per workgroup
   // 1. sample pass (only rows with more than kCandCap candidates need it)
   if (max_blocks > kCandCap) {
     dim3 grid((unsigned)gx, (ws.ns_stride + chunk - 1) / chunk);

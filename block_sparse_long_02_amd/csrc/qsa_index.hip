@@ -13,7 +13,7 @@
 //   1. sample pass   -- the score GEMM over every 16th block writes those
 //                       scores (1/16 of the work) for rows with > 4096 candidates;
 //   2. threshold     -- per row, tau = the r-th largest sampled score, with r
-//                       chosen so that about K + 1536 candidates score >= tau;
+//                       chosen so that about K + 768 candidates score >= tau;
 //   3. filter pass   -- the full score GEMM (bf16 MFMA 16x16x32, indexer query
 //                       rows in registers, block keys streamed) appends every
 //                       (score, block) with score >= tau to a per-row list
@@ -46,7 +46,7 @@ constexpr int kCandCap = 4096;      // list capacity per row
 constexpr int kSampleStride = 16;   // every 16th block is sampled
 // aimed-for surplus of prefill list entries over K
 #ifndef QSA_SAMPLE_EXTRA
-#define QSA_SAMPLE_EXTRA 1024
+#define QSA_SAMPLE_EXTRA 768
 #endif
 constexpr int kSampleExtra = QSA_SAMPLE_EXTRA;
 constexpr int kBins = 2048;         // 11-bit radix digits / histogram bins
@@ -224,7 +224,10 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
 // the exact tau test run once per workgroup over the pending lists, one entry
 // per lane.
 constexpr int kStageCols = 64;
-constexpr int kPending = 16;        // pending pre-filter passes per row and workgroup
+#ifndef QSA_PENDING
+#define QSA_PENDING 24
+#endif
+constexpr int kPending = QSA_PENDING;   // pending pre-filter passes per row and workgroup
 
 template <int MT, bool kSample>
 __global__ void __launch_bounds__(256, QSA_SCORE_WGS)

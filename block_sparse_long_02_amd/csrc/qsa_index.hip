@@ -10,10 +10,10 @@
 // Design (gfx950).  Scores are never materialised for all candidates: at 1M
 // tokens that would be 1 MB per query, and writing then re-reading them costs
 // more HBM time than the score GEMM itself.  Instead:
-//   1. sample pass   -- the score GEMM over every 16th block writes those
-//                       scores (1/16 of the work) for rows with > 4096 candidates;
+//   1. sample pass   -- the score GEMM over every 32nd block writes those
+//                       scores (1/32 of the work) for rows with > 4096 candidates;
 //   2. threshold     -- per row, tau = the r-th largest sampled score, with r
-//                       chosen so that about K + 768 candidates score >= tau;
+//                       chosen so that about K + 1280 candidates score >= tau;
 //   3. filter pass   -- the full score GEMM (bf16 MFMA 16x16x32, indexer query
 //                       rows in registers, block keys streamed) appends every
 //                       (score, block) with score >= tau to a per-row list
@@ -43,10 +43,15 @@ constexpr int kPrefillMT = QSA_PREFILL_MT;
 #define QSA_SCORE_WGS 3
 #endif
 constexpr int kCandCap = 4096;      // list capacity per row
-constexpr int kSampleStride = 16;   // every 16th block is sampled
+constexpr int kSampleStride = 16;   // decode (dense) path: every 16th score is a sample
+// prefill sample pass: every kPrefillSampleStride-th block is scored
+#ifndef QSA_PREFILL_SAMPLE_STRIDE
+#define QSA_PREFILL_SAMPLE_STRIDE 32
+#endif
+constexpr int kPrefillSampleStride = QSA_PREFILL_SAMPLE_STRIDE;
 // aimed-for surplus of prefill list entries over K
 #ifndef QSA_SAMPLE_EXTRA
-#define QSA_SAMPLE_EXTRA 768
+#define QSA_SAMPLE_EXTRA 1280
 #endif
 constexpr int kSampleExtra = QSA_SAMPLE_EXTRA;
 constexpr int kBins = 2048;         // 11-bit radix digits / histogram bins
@@ -238,7 +243,7 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
                   const uint32_t* __restrict__ thresh, int32_t* __restrict__ cnt,
                   u32x2* __restrict__ cand, uint16_t* __restrict__ samples, int ns_stride) {
   constexpr int QT = 16 * MT;
-  constexpr int stride = kSample ? kSampleStride : 1;
+  constexpr int stride = kSample ? kPrefillSampleStride : 1;
   constexpr int kPend = kSample ? 1 : kPending;
   __shared__ __attribute__((aligned(16))) uint16_t s_b[2][kStageCols * kIdxDim];
   __shared__ float s_w[QT][4];
@@ -686,8 +691,8 @@ threshold_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ s
   }
   if (threadIdx.x == 0) cnt[row] = 0;
   const int k = min(budget, g.n_c);
-  const int ns = (g.n_c + kSampleStride - 1) / kSampleStride;
-  const int r = min(ns, (k + kSampleExtra + kSampleStride - 1) / kSampleStride);
+  const int ns = (g.n_c + kPrefillSampleStride - 1) / kPrefillSampleStride;
+  const int r = min(ns, (k + kSampleExtra + kPrefillSampleStride - 1) / kPrefillSampleStride);
   const uint16_t* sp = samples + (int64_t)row * ns_stride;
   uint32_t t16;
   if (ns <= kLdsSamples) {
@@ -1141,9 +1146,9 @@ inline IndexWs index_ws_layout(void* base, int n_q, int max_q_len, int max_block
   IndexWs ws = {};
   char* p = (char*)base;
   size_t off = 0;
-  ws.ns_stride = (max_blocks + kSampleStride - 1) / kSampleStride;
+  ws.ns_stride = (max_blocks + kPrefillSampleStride - 1) / kPrefillSampleStride;
   ws.dense_stride = ((int64_t)max_blocks + 63) / 64 * 64;
-  ws.dsmp_stride = ((int64_t)ws.ns_stride + 63) / 64 * 64;
+  ws.dsmp_stride = ((int64_t)((max_blocks + kSampleStride - 1) / kSampleStride) + 63) / 64 * 64;
   if (use_dense(max_q_len)) {
     ws.dense = (uint32_t*)(p + off);
     off = align256(off + (size_t)n_q * ws.dense_stride * 4);

@@ -1230,13 +1230,25 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
   // 2. thresholds (also preset the list counters)
   hipLaunchKernelGGL(threshold_kernel, dim3(n_q), dim3(256), 0, st, cu_q, seq_len, n_seq,
                      max_blocks, budget, ws.samples, ws.ns_stride, ws.thresh, ws.cnt);
-  // 3. filter pass
+  // 3. filter pass.  About K + kSampleExtra of a row's n_c candidates pass
+  //    the pre-filter, spread over its n_c / chunk workgroups; the chunk is
+  //    halved (down to one stage) until the longest row expects at most
+  //    kPassTarget passes per workgroup, so that short rows (a larger share
+  //    passes) rarely fill their kPending-entry lists.
   if (max_blocks > 0) {
-    dim3 grid((unsigned)gx, (max_blocks + chunk - 1) / chunk);
+#ifndef QSA_PASS_TARGET
+#define QSA_PASS_TARGET 24
+#endif
+    constexpr int kPassTarget = QSA_PASS_TARGET;
+    int fchunk = chunk;
+    while (fchunk > kStageCols &&
+           (int64_t)fchunk * (budget + kSampleExtra) > (int64_t)kPassTarget * max_blocks)
+      fchunk >>= 1;
+    dim3 grid((unsigned)gx, (max_blocks + fchunk - 1) / fchunk);
     if (grid.y > 65535) return QSA_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((score_gemm_kernel<kPrefillMT, false>), grid, dim3(256), 0, st,
                        (const uint16_t*)idx_q, w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq,
-                       max_blocks, (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh,
+                       max_blocks, (const uint16_t*)block_keys, bk_seq_stride, fchunk, ws.thresh,
                        ws.cnt, ws.cand, ws.samples, ws.ns_stride);
   }
   // 4. exact select per row (rows whose list came out short or overflowed

@@ -185,6 +185,16 @@ def test_index_select_exact_grid_sampled_path():
     _select_and_check(b, exact=True)
 
 
+def test_index_select_exact_grid_mid_rows():
+    # rows from 3,750 to 6,250 candidates: a tile that mixes rows keeping
+    # every candidate with filtered rows, and filtered rows where a fifth to
+    # a third of the blocks pass the pre-filter (pending lists drain often)
+    b = W.make_prefill(prefix=15000, chunk=10000, budget=512, seg=64, n_plant=32, seed=27,
+                       exact_grid=True)
+    rows = sorted(set(range(0, 10000, 53)) | set(range(1340, 1420)) | set(range(9968, 10000)))
+    _select_and_check(b, exact=True, rows=rows)
+
+
 def test_index_select_exact_grid_decode():
     b = W.make_decode(seq_lens=[20001, 37002, 70003, 5000, 3], budget=512, n_plant=32, seed=23,
                       exact_grid=True)

@@ -28,6 +28,18 @@ Readings where the pages leave a step open (each also stated where it is used):
     float64;
   * softmax scale 1/sqrt(256) = 1/16; Q head h reads KV head floor(h/12).
 
+Readings for the pages' full indexer transforms (transform_block_keys,
+transform_queries), which the plain path above leaves out:
+  * RMSNorm over the 128 dims: x / sqrt(mean(x^2) + eps) * gamma, eps = 1e-6
+    unless given, gamma = 1 unless given; on the query side per head;
+  * the pooled mean enters the norm as the float32 sum-and-scale of the plain
+    block key, before its bf16 rounding;
+  * indexer RoPE: rotate-half on dims 0..63 of 128, pairs (j, j+32), the core's
+    frequencies 1e7^(-j/32); keys at the block position p_b = 4b, queries at
+    their token position;
+  * everything after the float32 mean is float64; the result goes to float32
+    (RNE), then to bf16 (RNE).
+
 Arrays holding bf16 data are passed as float64 arrays whose values are exactly
 representable in bf16 (the caller decodes bf16 losslessly).
 
@@ -166,6 +178,97 @@ def sparse_token_set(blocks: np.ndarray, i: int) -> np.ndarray:
     expanded = (R * b[:, None] + np.arange(R)[None, :]).reshape(-1)
     tail = np.arange(R * completed_blocks(i), i + 1, dtype=np.int64)
     return np.concatenate([expanded, tail])
+
+
+# ----------------------------------------- indexer: the pages' transforms
+
+RMS_EPS = 1.0e-6      # reading: the pages give no epsilon
+D_I_ROPE = 64         # [ailearn] §03 second QSA step: the indexer rotates 64 of its 128 dims
+
+
+def index_inv_freq() -> np.ndarray:
+    """The 32 rotary frequencies 1e7^(-j/32) of the indexer's 64 rotated dims.
+
+    [ailearn] §03 second QSA step (partial RoPE, 64 of 128 indexer dims).
+    Reading: the same base and spacing as the core heads' rotary dims.
+    """
+    j = np.arange(D_I_ROPE // 2, dtype=np.float64)
+    return ROPE_BASE ** (-2.0 * j / D_I_ROPE)
+
+
+def rms_norm(x: np.ndarray, gamma=None, eps: float = RMS_EPS) -> np.ndarray:
+    """RMS normalisation over the last axis, in float64.
+
+    [ailearn] indexer figure caption and its note on the order of operations
+    (the pooled key, and each projected query, are RMS-normalised).
+    y = (x * (mean(x^2) + eps)^(-1/2)) * gamma.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    g = np.ones(x.shape[-1]) if gamma is None else np.asarray(gamma, dtype=np.float64)
+    return (x * r) * g
+
+
+def index_rope(x: np.ndarray, pos, inv_freq=None) -> np.ndarray:
+    """Partial rotary embedding on the first 64 of the 128 indexer dims, float64.
+
+    [ailearn] §03 second QSA step.  Rotate-half with pairs (j, j+32):
+      y_j = x_j cos(theta_j) - x_{j+32} sin(theta_j)
+      y_{j+32} = x_{j+32} cos(theta_j) + x_j sin(theta_j),  theta_j = pos * f_j;
+    dims 64..127 pass through.  x: [..., 128]; pos broadcasts against x[..., 0].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    f = index_inv_freq() if inv_freq is None else np.asarray(inv_freq, dtype=np.float64)
+    theta = np.asarray(pos, dtype=np.float64)[..., None] * f
+    c, s = np.cos(theta), np.sin(theta)
+    h = D_I_ROPE // 2
+    y = x.copy()
+    y[..., :h] = x[..., :h] * c - x[..., h:D_I_ROPE] * s
+    y[..., h:D_I_ROPE] = x[..., h:D_I_ROPE] * c + x[..., :h] * s
+    return y
+
+
+def _to_bf16_via_f32(y: np.ndarray) -> np.ndarray:
+    return round_to_bf16(np.asarray(y, dtype=np.float64).astype(np.float32))
+
+
+def transform_block_keys(idx_k: np.ndarray, n_blocks: int, gamma=None, eps: float = RMS_EPS,
+                         inv_freq=None, rounded: bool = True) -> np.ndarray:
+    """The pages' block key: pool, then RMSNorm, then block-position partial RoPE.
+
+    [ailearn] indexer figure caption and its note on the order (key side:
+    average-pool each 4 tokens, then RMSNorm and block-level partial RoPE);
+    §03 first and second QSA steps.  Block b is rotated at p_b = 4b, the
+    block's first token (the p_b of the BLOCK SCORE condition).
+
+    The mean is the float32 ((k0 + k1) + k2) + k3, times 0.25, as for the plain
+    block key but not rounded to bf16; the rest is float64, then float32, then
+    bf16 (skipped with rounded=False, which returns the float64 values).
+    idx_k: [L][128] token keys (bf16 values).  Returns [n_blocks][128].
+    """
+    k = np.asarray(idx_k, dtype=np.float64)
+    assert k.shape[0] >= R * n_blocks
+    t = k[:R * n_blocks].reshape(n_blocks, R, D_I).astype(np.float32)
+    m = ((t[:, 0] + t[:, 1]) + t[:, 2]) + t[:, 3]
+    m = (m * np.float32(0.25)).astype(np.float64)
+    y = index_rope(rms_norm(m, gamma, eps), R * np.arange(n_blocks), inv_freq)
+    return _to_bf16_via_f32(y) if rounded else y
+
+
+def transform_queries(q_raw: np.ndarray, pos, gamma=None, eps: float = RMS_EPS,
+                      inv_freq=None, rounded: bool = True) -> np.ndarray:
+    """The pages' indexer query: per-head RMSNorm, then token-position RoPE.
+
+    [ailearn] indexer figure caption and its note on the order (query side:
+    independent projections, normalisation, then the current position's
+    rotary embedding).  q_raw: [..., 4, 128] projected queries (bf16 values);
+    pos: the token position of each row, broadcast against q_raw[..., 0, 0].
+    float64, then float32, then bf16 (skipped with rounded=False).
+    """
+    q = np.asarray(q_raw, dtype=np.float64)
+    p = np.asarray(pos, dtype=np.float64)[..., None]      # one position per row, all heads
+    y = index_rope(rms_norm(q, gamma, eps), p, inv_freq)
+    return _to_bf16_via_f32(y) if rounded else y
 
 
 # ------------------------------------------------------------ core attention

@@ -361,3 +361,117 @@ def test_oracle_query_pipeline_on_generated_prefill():
         if O.completed_blocks(i) <= b.budget:
             o2, l2 = O.dense_causal_gqa(bf16_vals(b.q[i]), k_raw, v, i)
             assert np.allclose(out, o2, atol=1e-12)
+
+
+# ------------------------------------------------- indexer transforms (pages)
+
+def _hadamard_rows():
+    # two orthogonal +-1 vectors of length 128 (rows of a Sylvester Hadamard matrix)
+    h = np.array([[1.0]])
+    while h.shape[0] < 128:
+        h = np.block([[h, h], [h, -h]])
+    return h[1], h[2]
+
+
+def test_oracle_rms_norm_closed_forms():
+    x, y = _hadamard_rows()
+    assert np.array_equal(O.rms_norm(x, eps=0.0), x)                 # mean square 1
+    v = np.zeros(128)
+    v[0], v[1] = 3.0, 4.0                                             # mean square 25/128
+    want = np.zeros(128)
+    want[0], want[1] = 3.0 * math.sqrt(128) / 5, 4.0 * math.sqrt(128) / 5
+    assert np.allclose(O.rms_norm(v, eps=0.0), want, rtol=1e-15, atol=0)
+    assert np.allclose(O.rms_norm(7.5 * v, eps=0.0), want, rtol=1e-15, atol=0)
+    g = np.linspace(0.5, 2.0, 128)
+    assert np.allclose(O.rms_norm(v, g, eps=0.0), want * g, rtol=1e-15, atol=0)
+    # the default epsilon: 1e-6 inside the root
+    assert np.allclose(O.rms_norm(x), x / math.sqrt(1.0 + 1e-6), rtol=1e-15, atol=0)
+    assert np.array_equal(O.rms_norm(np.zeros(128)), np.zeros(128))
+    # over the last axis only: rows are normalised independently
+    both = O.rms_norm(np.stack([v, 100.0 * x]), eps=0.0)
+    assert np.allclose(both[0], want, rtol=1e-15) and np.allclose(both[1], x, rtol=1e-15)
+
+
+def test_oracle_index_rope_basis_vectors():
+    assert np.allclose(O.index_inv_freq(), 10.0 ** (-7.0 * np.arange(32) / 32.0), rtol=1e-15)
+    for p in (0, 1, 5, 4096, 1048572):
+        for j in (0, 1, 13, 31):
+            th = p * 10.0 ** (-7.0 * j / 32.0)
+            e = np.zeros(128)
+            e[j] = 1.0
+            y = O.index_rope(e, p)
+            assert abs(y[j] - math.cos(th)) < 1e-12 and abs(y[j + 32] - math.sin(th)) < 1e-12
+            assert np.count_nonzero(np.delete(y, [j, j + 32])) == 0
+            e = np.zeros(128)
+            e[j + 32] = 1.0
+            y = O.index_rope(e, p)
+            assert abs(y[j] + math.sin(th)) < 1e-12 and abs(y[j + 32] - math.cos(th)) < 1e-12
+    x = np.random.default_rng(40).standard_normal(128)
+    assert np.array_equal(O.index_rope(x, 0), x)
+    assert np.array_equal(O.index_rope(x, 777)[64:], x[64:])
+
+
+def test_oracle_index_rope_relative_position():
+    rng = np.random.default_rng(41)
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
+    for i, j, t in [(100, 8, 4096), (1048575, 4, 12), (3, 0, 1)]:
+        a = O.index_rope(q, i) @ O.index_rope(k, j)
+        b = O.index_rope(q, i + t) @ O.index_rope(k, j + t)
+        assert abs(a - b) < 1e-9 * (1 + abs(a))
+
+
+def test_oracle_transform_block_keys_pools_before_the_norm():
+    # tokens x, x, x, 10y with x, y orthogonal and mean square 1: the mean
+    # (3x + 10y)/4 has mean square 109/16, so the key is (3x + 10y)/sqrt(109)
+    # (normalising each token first would give (3x + y)/4)
+    x, y = _hadamard_rows()
+    toks = np.stack([x, x, x, 10.0 * y])
+    got = O.transform_block_keys(toks, 1, eps=0.0, rounded=False)[0]
+    want = (3.0 * x + 10.0 * y) / math.sqrt(109.0)
+    assert np.allclose(got, want, rtol=1e-14, atol=0)
+    got_r = O.transform_block_keys(toks, 1, eps=0.0)[0]
+    assert np.array_equal(got_r, O.round_to_bf16(want.astype(np.float32)))
+
+
+def test_oracle_transform_block_keys_block_position():
+    # block b of four tokens 16 e_0: mean square 2, normalised 8 sqrt(2) e_0,
+    # rotated at p_b = 4b with f_0 = 1 into the plane (0, 32)
+    toks = np.zeros((4 * 6, 128))
+    toks[:, 0] = 16.0
+    got = O.transform_block_keys(toks, 6, eps=0.0, rounded=False)
+    for b in range(6):
+        assert abs(got[b, 0] - 8 * math.sqrt(2) * math.cos(4 * b)) < 1e-12
+        assert abs(got[b, 32] - 8 * math.sqrt(2) * math.sin(4 * b)) < 1e-12
+    # scores depend on the token distance between query and block only:
+    # moving the block by t blocks and the query by 4t tokens keeps q . kbar
+    rng = np.random.default_rng(42)
+    k = O.round_to_bf16(rng.standard_normal((4, 128)))
+    q = O.round_to_bf16(rng.standard_normal((4, 128)))
+    keys = np.zeros((4 * 40, 128))
+    keys[4 * 3:4 * 4] = k
+    keys[4 * 37:4 * 38] = k
+    kb = O.transform_block_keys(keys, 40, rounded=False)
+    d1 = O.transform_queries(q, 100, rounded=False) @ kb[3]
+    d2 = O.transform_queries(q, 100 + 4 * 34, rounded=False) @ kb[37]
+    assert np.allclose(d1, d2, rtol=1e-9, atol=1e-9)
+
+
+def test_oracle_transform_queries_norm_then_rope_per_head():
+    # head 0 = 16 e_0 with gamma_0 = 2: normalised 16 sqrt(2) e_0, then rotated
+    # at the token position (rotating first would scale only the cos part)
+    q = np.zeros((4, 128))
+    q[0, 0] = 16.0
+    q[1] = 3.0 * _hadamard_rows()[0]        # per head: each head has its own mean square
+    g = np.ones(128)
+    g[0] = 2.0
+    for p in (0, 9, 262143):
+        y = O.transform_queries(q, p, gamma=g, eps=0.0, rounded=False)
+        assert abs(y[0, 0] - 16 * math.sqrt(2) * math.cos(p)) < 1e-12
+        assert abs(y[0, 32] - 16 * math.sqrt(2) * math.sin(p)) < 1e-12
+        h = O.index_rope(_hadamard_rows()[0] * g, p)
+        assert np.allclose(y[1], h, rtol=1e-13, atol=1e-13)
+        assert np.array_equal(O.transform_queries(q, p, gamma=g)[2], np.zeros(128))   # eps > 0
+    # rows take their own positions
+    y = O.transform_queries(np.stack([q, q]), np.array([0, 9]), gamma=g, rounded=False)
+    assert np.array_equal(y[1], O.transform_queries(q, 9, gamma=g, rounded=False))
+    assert np.array_equal(y[0], O.transform_queries(q, 0, gamma=g, rounded=False))

@@ -13,8 +13,10 @@ the kernels run on.  `roofline` is for the dominant kernel (the attention
 kernel of the prefill step): algorithmic bytes per launch / its mean
 duration, against 8 TB/s, with the counted HBM-side bytes beside it
 (`traffic`, from profiles/traffic.json while the kernel source is unchanged).
-`rows` gives each hot-path row against its own roofline.  `cpu_baseline`
-times the CPU oracle on a bounded sample of the same workload.
+`rows` gives each hot-path row against its own roofline.  `index_transforms`
+repeats the prefill step with the pages' indexer transforms (RMSNorm and
+partial RoPE of block keys and queries) and times each transform kernel.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                     [--only prefill|decode|mtp]
@@ -83,14 +85,16 @@ def decode_traffic():
     return None if any(v is None for v in vals) else int(sum(vals))
 
 
-def time_prefill(args):
+def time_prefill(args, transforms=False, batch=None):
+    """The chunked-prefill step; transforms=True runs it with the pages'
+    indexer transforms (normalised, rotated block keys and queries)."""
     import torch
     from block_sparse_long_02_amd import workloads as W
     from block_sparse_long_02_amd.runner import QSARunner
 
     t0 = time.time()
-    b = W.chunked_prefill_1m(device="cuda")
-    r = QSARunner(b)
+    b = W.chunked_prefill_1m(device="cuda") if batch is None else batch
+    r = QSARunner(b, transforms=transforms)
     torch.cuda.synchronize()
     log(f"prefill workload ready in {time.time() - t0:.1f}s")
     for _ in range(args.warmup):
@@ -129,6 +133,46 @@ def time_prefill(args):
         index=dict(flops=index_flops, tflops=index_flops / (stage["select"] * 1e-3) / 1e12),
         runner=r, batch=b)
     return res
+
+
+def time_calls(fn, steps):
+    """Mean duration (ms) of fn() over `steps` calls, HIP events on the current stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_transforms(args, pre):
+    """The pages' indexer transforms on the prefill workload: the whole step
+    with them, and each transform kernel on its own against HBM."""
+    from block_sparse_long_02_amd import qsa
+    b = pre["batch"]
+    tr = time_prefill(args, transforms=True, batch=b)
+    r = tr["runner"]
+    steps = max(args.steps, 10)
+    q_ms = time_calls(lambda: qsa.index_query_transform(b.idx_q, r.idx_q_t, b.cu_q, b.seq_len,
+                                                        r.max_q_len), steps)
+    k_ms = time_calls(lambda: r.pool(), steps)
+    q_bytes = 2 * b.idx_q.numel() * 2                       # read raw, write transformed
+    n_new = int((r.pool_end - r.pool_begin).sum().item())
+    k_bytes = n_new * (4 * BLOCK_KEY_BYTES + BLOCK_KEY_BYTES)
+    return {
+        "ms_per_step": round(tr["ms_per_step"], 4), "value": round(tr["value"], 1),
+        "unit": "tokens/s", "stages_ms": {k: round(v, 4) for k, v in tr["stages_ms"].items()},
+        "index_tflops": round(tr["index"]["tflops"], 1),
+        "query_transform": {"kernel": "index_query_transform_kernel", "ms": round(q_ms, 4),
+                            "bound": "hbm", "algorithmic_bytes": q_bytes,
+                            "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "key_transform": {"kernel": "pool_block_keys_normed_kernel", "ms": round(k_ms, 4),
+                          "blocks": n_new, "bound": "hbm", "algorithmic_bytes": k_bytes,
+                          "frac": round(k_bytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
 def time_decode(args, mtp=False):
@@ -302,6 +346,10 @@ def main():
                                "frac_of_bf16_mfma_peak": round(pre["index"]["tflops"] / MFMA_BF16_PEAK_TFS, 4)}
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
+        del pre["runner"]
+        torch.cuda.empty_cache()
+        out["index_transforms"] = time_transforms(args, pre)
+        log(f"prefill with indexer transforms: {out['index_transforms']}")
         del pre
         torch.cuda.empty_cache()
     if args.only in (None, "decode"):

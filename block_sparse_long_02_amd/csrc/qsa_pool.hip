@@ -86,7 +86,7 @@ const char* qsa_status_string(int status) {
   }
 }
 
-int qsa_abi_version(void) { return 1; }
+int qsa_abi_version(void) { return 2; }
 
 int qsa_pool_block_keys(const void* idx_k, int64_t ik_seq_stride, void* block_keys,
                         int64_t bk_seq_stride, const int32_t* blk_begin, const int32_t* blk_end,

@@ -31,7 +31,8 @@ COPY_BYTES = 1 << 30
 # kernel: an index in dispatch order, or None for the mean of all).  Pooling
 # runs three times: the prefill runner pools its cached prefix, the prefill
 # step pools the chunk's new blocks, the decode runner pools its prefix (a
-# decode step of 131,073 tokens completes no new block).
+# decode step of 131,073 tokens completes no new block).  The transformed
+# pooling runs twice (prefix, then the step's new blocks).
 KERNELS = {
     "pool_block_keys_prefill_1m": ("pool_block_keys_kernel", "qsa_pool.hip", 1),
     "score_sample_prefill_1m": ("score_gemm_kernel<2, true>", "qsa_index.hip", None),
@@ -41,6 +42,8 @@ KERNELS = {
     "attend_prefill_1m": ("attend_kernel<true>", "qsa_attend.hip", None),
     "score_dense_decode_128k": ("score_dense_kernel", "qsa_index.hip", None),
     "select_dense_decode_128k": ("select_dense_kernel", "qsa_index.hip", None),
+    "key_transform_prefill_1m": ("pool_block_keys_normed_kernel", "qsa_index_transform.hip", 1),
+    "query_transform_prefill_1m": ("index_query_transform_kernel", "qsa_index_transform.hip", None),
     "attend_decode_128k": ("attend_kernel<false>", "qsa_attend.hip", None),
     "combine_decode_128k": ("combine_kernel", "qsa_attend.hip", None),
 }
@@ -52,7 +55,8 @@ def src_hash(name: str) -> str:
 
 
 def probe():
-    """The program the counter runs profile: copy, one prefill step, one decode step."""
+    """The program the counter runs profile: copy, one prefill step (plain, then
+    with the indexer transforms), one decode step."""
     import torch
     from . import workloads as W
     from .runner import QSARunner
@@ -68,6 +72,13 @@ def probe():
     r = QSARunner(b)
     torch.cuda.synchronize()
     print("MARK prefill step", flush=True)
+    r.step()
+    torch.cuda.synchronize()
+    del r
+    torch.cuda.empty_cache()
+    r = QSARunner(b, transforms=True)
+    torch.cuda.synchronize()
+    print("MARK prefill step with indexer transforms", flush=True)
     r.step()
     torch.cuda.synchronize()
     del r, b

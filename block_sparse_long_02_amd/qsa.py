@@ -31,6 +31,12 @@ SIGNATURES = {
     "qsa_pool_block_keys": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _c_void_p,
                                            _i32, _i32, _c_void_p]),
     "qsa_rope_apply": (ctypes.c_int, [_c_void_p, _i64, _i64, _i32, _c_void_p, _i32, _i32, _c_void_p]),
+    "qsa_pool_block_keys_normed": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _i64, _c_void_p,
+                                                  _c_void_p, _i32, _i32, _c_void_p, ctypes.c_double,
+                                                  _c_void_p, _c_void_p]),
+    "qsa_index_query_transform": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
+                                                 _i32, _i32, _c_void_p, ctypes.c_double, _c_void_p,
+                                                 _c_void_p]),
     "qsa_index_select_workspace": (_size, [_i32, _i32, _i32]),
     "qsa_index_select": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                         _i32, _c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p,
@@ -116,6 +122,39 @@ def rope_apply(x, row_stride, head_stride, n_heads, n_rows, pos=None, pos0=0, st
     st = lib().qsa_rope_apply(_p(x), int(row_stride), int(head_stride), int(n_heads), _p(pos),
                               int(pos0), int(n_rows), _stream(stream))
     _check("qsa_rope_apply", st)
+
+
+def _host_f64(a):
+    """(pointer, keep-alive) for an optional host float64 array of 32 frequencies."""
+    if a is None:
+        return None, None
+    if len(a) != 32:
+        raise ValueError("inv_freq holds 32 float64 frequencies")
+    buf = (ctypes.c_double * 32)(*[float(v) for v in a])
+    return ctypes.cast(buf, ctypes.c_void_p), buf
+
+
+def pool_block_keys_normed(idx_k, block_keys, blk_begin, blk_end, max_span, gamma=None, eps=1e-6,
+                           inv_freq=None, stream=None):
+    """Pool, RMS-normalise and rotate blocks blk_begin..blk_end (the pages' indexer keys)."""
+    _dev(idx_k, block_keys, blk_begin, blk_end, gamma)
+    fp, _keep = _host_f64(inv_freq)
+    st = lib().qsa_pool_block_keys_normed(_p(idx_k), idx_k.stride(0), _p(block_keys),
+                                          block_keys.stride(0), _p(blk_begin), _p(blk_end),
+                                          blk_begin.numel(), int(max_span), _p(gamma), float(eps),
+                                          fp, _stream(stream))
+    _check("qsa_pool_block_keys_normed", st)
+
+
+def index_query_transform(q_raw, q_out, cu_q, seq_len, max_q_len, gamma=None, eps=1e-6,
+                          inv_freq=None, stream=None):
+    """RMS-normalise and rotate the indexer query heads (bf16 [n_q][4][128]) at their positions."""
+    _dev(q_raw, q_out, cu_q, seq_len, gamma)
+    fp, _keep = _host_f64(inv_freq)
+    st = lib().qsa_index_query_transform(_p(q_raw), _p(q_out), _p(cu_q), _p(seq_len),
+                                         seq_len.numel(), q_raw.shape[0], int(max_q_len),
+                                         _p(gamma), float(eps), fp, _stream(stream))
+    _check("qsa_index_query_transform", st)
 
 
 def index_select_workspace(n_q, max_q_len, max_blocks) -> int:

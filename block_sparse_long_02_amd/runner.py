@@ -14,7 +14,11 @@ from .workloads import QSABatch, R, v_cache_layout
 
 
 class QSARunner:
-    def __init__(self, batch: QSABatch, decode: bool | None = None):
+    def __init__(self, batch: QSABatch, decode: bool | None = None, transforms: bool = False,
+                 gamma_k=None, gamma_q=None, eps: float = 1e-6):
+        """transforms=True applies the pages' indexer transforms: block keys are
+        pooled, RMS-normalised and rotated; each step first normalises and
+        rotates the indexer queries into a buffer of its own."""
         b = batch
         assert b.idx_q.is_cuda, "batch must live on the GPU"
         self.b = b
@@ -29,6 +33,8 @@ class QSARunner:
         self.max_blocks = b.max_blocks()
         self.budget = b.budget
         cap = b.l_cap
+        self.transforms, self.gamma_k, self.gamma_q, self.eps = transforms, gamma_k, gamma_q, eps
+        self.idx_q_t = torch.empty_like(b.idx_q) if transforms else None
 
         # caches: K rotated once at its positions (cache-write time), V re-laid out
         self.k_cache = b.k.clone()
@@ -44,7 +50,7 @@ class QSARunner:
         zero = torch.zeros(self.n_seq, dtype=torch.int32, device=dev)
         t_before = torch.tensor(before, dtype=torch.int32, device=dev)
         if max(before) > 0:
-            qsa.pool_block_keys(b.idx_k, self.block_keys, zero, t_before, max(before))
+            self._pool(zero, t_before, max(before))
         self.pool_begin = t_before
         self.pool_end = torch.tensor(after, dtype=torch.int32, device=dev)
         self.pool_span = max(a - c for a, c in zip(after, before))
@@ -59,15 +65,26 @@ class QSARunner:
                qsa.attend_decode_multi_workspace(self.n_q) if self.mtp else 16)
         self.ws_decode = torch.empty((max(wsd, 16),), dtype=torch.uint8, device=dev)
 
+    def _pool(self, begin, end, span, stream=None):
+        if self.transforms:
+            qsa.pool_block_keys_normed(self.b.idx_k, self.block_keys, begin, end, span,
+                                       gamma=self.gamma_k, eps=self.eps, stream=stream)
+        else:
+            qsa.pool_block_keys(self.b.idx_k, self.block_keys, begin, end, span, stream=stream)
+
     # the three calls of a step ------------------------------------------
     def pool(self, stream=None):
         if self.pool_span > 0:
-            qsa.pool_block_keys(self.b.idx_k, self.block_keys, self.pool_begin, self.pool_end,
-                                self.pool_span, stream=stream)
+            self._pool(self.pool_begin, self.pool_end, self.pool_span, stream)
 
     def select(self, stream=None):
         b = self.b
-        qsa.index_select(b.idx_q, b.w, b.cu_q, b.seq_len, self.max_q_len, self.max_blocks,
+        idx_q = b.idx_q
+        if self.transforms:
+            qsa.index_query_transform(b.idx_q, self.idx_q_t, b.cu_q, b.seq_len, self.max_q_len,
+                                      gamma=self.gamma_q, eps=self.eps, stream=stream)
+            idx_q = self.idx_q_t
+        qsa.index_select(idx_q, b.w, b.cu_q, b.seq_len, self.max_q_len, self.max_blocks,
                          self.block_keys, self.budget, self.sel, self.sel_count, self.ws_index,
                          stream=stream)
 

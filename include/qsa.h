@@ -124,6 +124,58 @@ int qsa_rope_apply(void* x, int64_t row_stride, int64_t head_stride, int32_t n_h
                    const int32_t* pos, int32_t pos0, int32_t n_rows, void* stream);
 
 /*
+ * The pages' indexer transforms (optional; the plain path above omits them).
+ * [ailearn] indexer figure caption and its note on the order of operations,
+ * and §03 second QSA step: the key side average-pools each 4-token block,
+ * then RMS-normalises it and rotates it at the block's position (partial
+ * RoPE on 64 of the 128 dims); the query side RMS-normalises each projected
+ * head and rotates it at the query's token position.  Feed the results to
+ * qsa_index_select in place of the plain block keys and queries.
+ *
+ * Arithmetic, identical for both calls (x = one 128-dim vector):
+ *   keys:    x[d] = float32 ((k0[d] + k1[d]) + k2[d]) + k3[d], times 0.25
+ *            (the plain block key before its bf16 rounding);
+ *   queries: x[d] = the bf16 input;
+ *   then in float64: n[d] = (x[d] * (sum_d' x[d']^2 / 128 + eps)^(-1/2)) * gamma[d];
+ *   for j < 32, with theta_j = pos * f_j:
+ *            y[j]    = n[j] cos(theta_j) - n[j+32] sin(theta_j)
+ *            y[j+32] = n[j+32] cos(theta_j) + n[j] sin(theta_j);
+ *            y[d] = n[d] for d >= 64;
+ *   out[d] = bf16_rne(float32_rne(y[d])).
+ * pos = 4b for block b (the block's first token); the token position for a
+ * query row (see the varlen convention).  Readings where the pages are
+ * silent: eps (1e-6 is the usual choice), gamma (NULL = all ones; trained
+ * weights replace it), f_j (NULL = 1e7^(-j/32), the core heads' frequencies).
+ *
+ *   gamma     float32 [128] device, or NULL
+ *   eps       finite, >= 0 (eps = 0 turns an all-zero vector into NaN)
+ *   inv_freq  float64 [32] HOST array of f_j, copied at the call, or NULL
+ * Errors: QSA_ERR_INVALID_ARG for a negative count, a bad eps or a
+ * non-finite f_j, and as for the plain calls.
+ */
+
+/* Key side: pools and transforms blocks blk_begin[s] <= b < blk_end[s] of
+ * every sequence s exactly like qsa_pool_block_keys (same arguments, same
+ * launch sizing); other blocks are untouched. */
+int qsa_pool_block_keys_normed(const void* idx_k, int64_t ik_seq_stride,
+                               void* block_keys, int64_t bk_seq_stride,
+                               const int32_t* blk_begin, const int32_t* blk_end,
+                               int32_t n_seq, int32_t max_span,
+                               const float* gamma, double eps, const double* inv_freq,
+                               void* stream);
+
+/* Query side: q_raw and q_out are bf16 [n_q][4][128] (q_out may equal q_raw;
+ * other overlaps are not allowed).  Row cu_q[s] + j of sequence s is
+ * transformed at its position; rows that no sequence covers, or whose
+ * position would be negative, are not written.  max_q_len as for
+ * qsa_index_select. */
+int qsa_index_query_transform(const void* q_raw, void* q_out,
+                              const int32_t* cu_q, const int32_t* seq_len,
+                              int32_t n_seq, int32_t n_q, int32_t max_q_len,
+                              const float* gamma, double eps, const double* inv_freq,
+                              void* stream);
+
+/*
  * a2 + a3 -- indexer block scores and deterministic top-K_B block selection.
  * [ailearn] §03 BLOCK SCORE and CAUSAL SPARSE SET equations, third and fourth
  * QSA steps.  For query row i at position p (batch layout above), the

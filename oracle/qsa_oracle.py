@@ -233,7 +233,7 @@ def _to_bf16_via_f32(y: np.ndarray) -> np.ndarray:
 
 
 def transform_block_keys(idx_k: np.ndarray, n_blocks: int, gamma=None, eps: float = RMS_EPS,
-                         inv_freq=None, rounded: bool = True) -> np.ndarray:
+                         inv_freq=None, rounded: bool = True, first_block: int = 0) -> np.ndarray:
     """The pages' block key: pool, then RMSNorm, then block-position partial RoPE.
 
     [ailearn] indexer figure caption and its note on the order (key side:
@@ -244,14 +244,15 @@ def transform_block_keys(idx_k: np.ndarray, n_blocks: int, gamma=None, eps: floa
     The mean is the float32 ((k0 + k1) + k2) + k3, times 0.25, as for the plain
     block key but not rounded to bf16; the rest is float64, then float32, then
     bf16 (skipped with rounded=False, which returns the float64 values).
-    idx_k: [L][128] token keys (bf16 values).  Returns [n_blocks][128].
+    idx_k: [L][128] token keys (bf16 values), token 0 being the first token of
+    block first_block.  Returns [n_blocks][128].
     """
     k = np.asarray(idx_k, dtype=np.float64)
     assert k.shape[0] >= R * n_blocks
     t = k[:R * n_blocks].reshape(n_blocks, R, D_I).astype(np.float32)
     m = ((t[:, 0] + t[:, 1]) + t[:, 2]) + t[:, 3]
     m = (m * np.float32(0.25)).astype(np.float64)
-    y = index_rope(rms_norm(m, gamma, eps), R * np.arange(n_blocks), inv_freq)
+    y = index_rope(rms_norm(m, gamma, eps), R * (first_block + np.arange(n_blocks)), inv_freq)
     return _to_bf16_via_f32(y) if rounded else y
 
 

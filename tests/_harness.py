@@ -19,18 +19,30 @@ def np64(t: torch.Tensor) -> np.ndarray:
 class OracleView:
     """Oracle-side view of one QSABatch (float64 arrays, per sequence)."""
 
-    def __init__(self, b):
+    def __init__(self, b, transforms=False, gamma_k=None, gamma_q=None, eps=O.RMS_EPS):
+        """transforms=True: block keys and indexer queries as the pages'
+        transforms make them (gamma_* are numpy arrays or None)."""
         self.b = b
         self.lens = b.seq_lens_host()
         self.cu = b.cu_q_host()
         self.pos = b.q_pos_host()
         self.seq = b.q_seq_host()
+        self.transforms, self.gamma_k, self.gamma_q, self.eps = transforms, gamma_k, gamma_q, eps
         self._kb = {}
 
     def kbar(self, s):
         if s not in self._kb:
-            self._kb[s] = O.pool_block_keys(np64(self.b.idx_k[s]), self.lens[s] // O.R)
+            k, n = np64(self.b.idx_k[s]), self.lens[s] // O.R
+            self._kb[s] = (O.transform_block_keys(k, n, self.gamma_k, self.eps) if self.transforms
+                           else O.pool_block_keys(k, n))
         return self._kb[s]
+
+    def query(self, row):
+        """The indexer query heads [4][128] of a row, as scored."""
+        q = np64(self.b.idx_q[row])
+        if self.transforms:
+            q = O.transform_queries(q, self.pos[row], self.gamma_q, self.eps)
+        return q
 
     def rows(self, s, tokens):
         """Raw K and V rows [n][2][256] of the listed tokens of sequence s."""
@@ -42,8 +54,7 @@ class OracleView:
     def scores(self, row):
         s, p = self.seq[row], self.pos[row]
         n_c = O.completed_blocks(p)
-        return O.block_scores(np64(self.b.idx_q[row]), self.b.w[row].cpu().numpy(),
-                              self.kbar(s)[:n_c])
+        return O.block_scores(self.query(row), self.b.w[row].cpu().numpy(), self.kbar(s)[:n_c])
 
     def select(self, row):
         return O.select_blocks(self.scores(row), self.b.budget)
@@ -77,7 +88,7 @@ def check_selection(view: OracleView, row: int, gpu_ids, gpu_count: int, exact: 
     assert k_eff == 0 or (ids[0] >= 0 and ids[-1] < n_c), row
     sc = view.scores(row)
     want = O.select_blocks(sc, b.budget)
-    gap, delta, s_k = O.selection_gap(sc, np64(b.idx_q[row]), b.w[row].cpu().numpy(),
+    gap, delta, s_k = O.selection_gap(sc, view.query(row), b.w[row].cpu().numpy(),
                                       view.kbar(s)[:n_c], b.budget)
     if exact or gap > delta:
         assert np.array_equal(ids, want), (row, np.setdiff1d(ids, want)[:8], np.setdiff1d(want, ids)[:8])

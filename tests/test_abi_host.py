@@ -31,7 +31,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
         assert n in qsa.SIGNATURES, n
@@ -41,7 +41,7 @@ def test_status_strings_and_version(L):
     for code, name in qsa.STATUS.items():
         assert qsa.status_string(code) == name
     assert qsa.status_string(99) == "QSA_ERR_UNKNOWN"
-    assert qsa.abi_version() == 1
+    assert qsa.abi_version() == 2
 
 
 def test_workspace_queries(L):
@@ -51,9 +51,10 @@ def test_workspace_queries(L):
     small = L.qsa_index_select_workspace(10, 64, 1000)
     big = L.qsa_index_select_workspace(10, 64, 1 << 18)
     assert small > 10 * 4096 * 8 and big > small       # candidate lists, then samples
-    # 32768 query rows at 1M context: 1 GiB of lists plus 1 GiB of samples
-    # (sizes past 2^31 must not wrap)
-    assert L.qsa_index_select_workspace(32768, 32768, 1 << 18) >= 32768 * 4096 * 8 + 32768 * 16384 * 2
+    # 32768 query rows at 1M context: 1 GiB of lists plus 0.5 GiB of 16-bit
+    # samples of every 32nd block; twice the rows pass 2^31 bytes, which must not wrap
+    assert L.qsa_index_select_workspace(32768, 32768, 1 << 18) >= 32768 * 4096 * 8 + 32768 * 8192 * 2
+    assert L.qsa_index_select_workspace(65536, 65536, 1 << 18) >= 65536 * 4096 * 8 + 65536 * 8192 * 2
     # up to 4 queries per sequence: every score is kept, one row per query
     dense = L.qsa_index_select_workspace(32, 1, 1 << 15)
     assert dense >= 32 * (1 << 15) * 4
@@ -110,3 +111,27 @@ def test_attention_and_pool_reject_bad_arguments(L):
     assert L.qsa_rope_apply(MISALIGNED, 256, 256, 2, None, 0, 10, None) == 1
     assert L.qsa_rope_apply(A, 256, 256, 2, None, 0, 0, None) == 0
     assert L.qsa_rope_apply(A, 256, 256, 2, None, (1 << 22), 10, None) == 2
+
+
+def test_indexer_transforms_reject_bad_arguments(L):
+    freq = (ctypes.c_double * 32)(*[1.0] * 32)
+    bad = (ctypes.c_double * 32)(*([1.0] * 31 + [float("inf")]))
+    pool = lambda **kw: L.qsa_pool_block_keys_normed(
+        kw.get("ik", ALIGNED), 128 * 64, kw.get("bk", ALIGNED), 128 * 16, ALIGNED, ALIGNED,
+        kw.get("n_seq", 1), kw.get("span", 16), None, kw.get("eps", 1e-6),
+        kw.get("freq", None), None)
+    query = lambda **kw: L.qsa_index_query_transform(
+        kw.get("q", ALIGNED), kw.get("o", ALIGNED), ALIGNED, ALIGNED, kw.get("n_seq", 1),
+        kw.get("n_q", 4), kw.get("mq", 4), None, kw.get("eps", 1e-6), kw.get("freq", None), None)
+    for f in (pool, query):
+        assert f(eps=-1.0) == 1
+        assert f(eps=float("nan")) == 1
+        assert f(eps=float("inf")) == 1
+        assert f(freq=ctypes.cast(bad, ctypes.c_void_p)) == 1
+        assert f(n_seq=-1) == 1
+        assert f(n_seq=0) == 0                     # nothing to do, nothing enqueued
+        assert f(n_seq=0, freq=ctypes.cast(freq, ctypes.c_void_p)) == 0
+    assert pool(ik=None) == 1 and pool(bk=MISALIGNED) == 1
+    assert pool(span=0) == 0 and pool(span=-1) == 1
+    assert query(q=None) == 1 and query(o=MISALIGNED) == 1
+    assert query(n_q=0) == 0 and query(mq=0) == 0 and query(n_q=-1) == 1

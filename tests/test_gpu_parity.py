@@ -279,6 +279,115 @@ def test_index_select_fallback_short_list():
     assert np.array_equal(r.sel.cpu().numpy()[0], np.arange(0, 8192, 16))
 
 
+# ------------------------------------------------- indexer transforms (pages)
+
+def _rand_bf16(g, shape):
+    # N(0,1) rows, each scaled by 10^u, u uniform in [-3, 3]
+    x = torch.randn(*shape, generator=g, dtype=torch.float64)
+    sc = 10.0 ** (torch.rand(*shape[:-1], 1, generator=g, dtype=torch.float64) * 6 - 3)
+    return (x * sc).to(torch.bfloat16)
+
+
+_FREQ_1E4 = [1.0e4 ** (-j / 32.0) for j in range(32)]    # a caller-given frequency table
+
+
+def _transform_cases(g):
+    gamma = (torch.rand(128, generator=g) + 0.5).float()
+    return [(None, None), (gamma, None), (None, _FREQ_1E4), (gamma, _FREQ_1E4)]
+
+
+def test_index_key_transform_bit_exact():
+    g = torch.Generator().manual_seed(60)
+    cap = 1 << 20
+    # sequence 0: blocks 0..516 (block 10 all zero); sequence 1: the last
+    # 1,144 blocks of a 1M-token cache (positions up to 1,048,572)
+    ranges = [(0, 517), (261000, 262144)]
+    idx_k = torch.zeros(2, cap, 128, dtype=torch.bfloat16)
+    for s, (b0, b1) in enumerate(ranges):
+        idx_k[s, 4 * b0:4 * b1] = _rand_bf16(g, (4 * (b1 - b0), 128))
+    idx_k[0, 40:44] = 0
+    ik = idx_k.cuda()
+    begin = torch.tensor([r[0] for r in ranges], dtype=torch.int32).cuda()
+    end = torch.tensor([r[1] for r in ranges], dtype=torch.int32).cuda()
+    sentinel = torch.full((2, cap // 4, 128), 0x1234, dtype=torch.int16).cuda()
+    for ci, (gamma, freq) in enumerate(_transform_cases(g)):
+        for max_span in (1144, 16):
+            bk = sentinel.clone().view(torch.bfloat16)
+            print(f"key transform case {ci} max_span {max_span}", flush=True)
+            qsa.pool_block_keys_normed(ik, bk, begin, end, max_span,
+                                       gamma=None if gamma is None else gamma.cuda(),
+                                       eps=1e-6, inv_freq=freq)
+            _sync()
+            got = _bits(bk)
+            for s, (b0, b1) in enumerate(ranges):
+                ref = O.transform_block_keys(np64(idx_k[s, 4 * b0:4 * b1]), b1 - b0,
+                                             None if gamma is None else gamma.double().numpy(),
+                                             1e-6, freq, first_block=b0)
+                ref_bits = torch.tensor(ref, dtype=torch.float32).to(torch.bfloat16)
+                ref_bits = ref_bits.view(torch.int16).numpy()
+                assert np.array_equal(got[s, b0:b1], ref_bits), (ci, s, max_span)
+                assert np.all(got[s, :b0] == 0x1234) and np.all(got[s, b1:] == 0x1234)
+            assert np.all(got[0, 10] & 0x7FFF == 0)   # the all-zero block stays (+-)0
+
+
+def test_index_query_transform_bit_exact():
+    g = torch.Generator().manual_seed(61)
+    lens, nq = [1 << 20, 5000, 37, 3], [40, 7, 37, 5]   # the last: 2 rows before position 0
+    cu = np.concatenate([[0], np.cumsum(nq)]).tolist()
+    n_rows = cu[-1] + 6                                 # 6 rows no sequence covers
+    q_raw = _rand_bf16(g, (n_rows, 4, 128))
+    q_raw[3] = 0
+    cu_q = torch.tensor(cu, dtype=torch.int32).cuda()
+    seq_len = torch.tensor(lens, dtype=torch.int32).cuda()
+    pos = np.concatenate([np.arange(L - n, L) for L, n in zip(lens, nq)])
+    valid = pos >= 0
+    for ci, (gamma, freq) in enumerate(_transform_cases(g)):
+        print(f"query transform case {ci}", flush=True)
+        gd = None if gamma is None else gamma.cuda()
+        out = torch.full((n_rows, 4, 128), 0x1234, dtype=torch.int16).cuda().view(torch.bfloat16)
+        qsa.index_query_transform(q_raw.cuda(), out, cu_q, seq_len, max(nq), gamma=gd, eps=1e-6,
+                                  inv_freq=freq)
+        inplace = q_raw.cuda()
+        qsa.index_query_transform(inplace, inplace, cu_q, seq_len, max(nq), gamma=gd, eps=1e-6,
+                                  inv_freq=freq)
+        _sync()
+        got = _bits(out)
+        ref = O.transform_queries(np64(q_raw[:cu[-1]][valid]), pos[valid],
+                                  None if gamma is None else gamma.double().numpy(), 1e-6, freq)
+        ref_bits = torch.tensor(ref, dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+        assert np.array_equal(got[:cu[-1]][valid], ref_bits.numpy()), ci
+        assert np.all(got[:cu[-1]][~valid] == 0x1234) and np.all(got[cu[-1]:] == 0x1234)
+        assert np.array_equal(_bits(inplace)[:cu[-1]][valid], got[:cu[-1]][valid])
+        assert np.all(got[3] & 0x7FFF == 0)
+
+
+def test_index_select_with_transforms():
+    # the select on the pages' transformed keys and queries, both methods:
+    # the sampled prefill path (n_c > 4096) and the dense decode path
+    g = torch.Generator().manual_seed(62)
+    gk, gq = (torch.rand(128, generator=g) + 0.5).float(), (torch.rand(128, generator=g) + 0.5).float()
+    batches = [W.make_prefill(prefix=40000, chunk=77, budget=512, seg=32, n_plant=32, seed=63),
+               W.make_decode(seq_lens=[20001, 131073, 70003, 5], budget=512, n_plant=32, seed=64),
+               W.tiny_prefill(T=512)]
+    for bi, b in enumerate(batches):
+        print(f"transformed select batch {bi}", flush=True)
+        view = OracleView(b, transforms=True, gamma_k=gk.double().numpy(),
+                          gamma_q=gq.double().numpy())
+        r = QSARunner(b.to("cuda"), transforms=True, gamma_k=gk.cuda(), gamma_q=gq.cuda())
+        r.pool()
+        r.select()
+        _sync()
+        for s in range(b.n_seq):                 # the keys the select saw, bit-exact
+            n = view.lens[s] // 4
+            ref = torch.tensor(view.kbar(s), dtype=torch.float32).to(torch.bfloat16)
+            assert torch.equal(r.block_keys[s, :n].cpu().view(torch.int16), ref.view(torch.int16))
+        sel, cnt = r.sel.cpu().numpy(), r.sel_count.cpu().numpy()
+        kinds = {"exact": 0, "near": 0}
+        for row in range(b.n_q):
+            kinds[check_selection(view, row, sel[row], int(cnt[row]))] += 1
+        print("transformed select:", bi, kinds)
+
+
 # ------------------------------------------------------------- end to end
 
 def _end_to_end(b, rows, dense=False):

@@ -28,6 +28,11 @@ Readings where the pages leave a step open (each also stated where it is used):
     float64;
   * softmax scale 1/sqrt(256) = 1/16; Q head h reads KV head floor(h/12).
 
+Readings for YaRN (yarn_inv_freq, yarn_softmax_scale), which the pages name
+without constants: the YaRN paper's published ramp with alpha = 1, beta = 32,
+s = 4 over the native 262,144 tokens, and its temperature applied to the whole
+logit; the indexer rotation takes the same table.
+
 Readings for the pages' full indexer transforms (transform_block_keys,
 transform_queries), which the plain path above leaves out:
   * RMSNorm over the 128 dims: x / sqrt(mean(x^2) + eps) * gamma, eps = 1e-6
@@ -272,22 +277,59 @@ def transform_queries(q_raw: np.ndarray, pos, gamma=None, eps: float = RMS_EPS,
     return _to_bf16_via_f32(y) if rounded else y
 
 
+# -------------------------------------------------- YaRN context extension
+
+NATIVE_CTX = 262144      # [card]; [ailearn] §07: native context, extended to 1M with YaRN
+YARN_FACTOR = 4.0        # reading: s = 4 makes 4 * 262144 = 1,048,576 positions
+YARN_ALPHA, YARN_BETA = 1.0, 32.0   # reading: the YaRN paper's ramp bounds
+
+
+def yarn_inv_freq(factor: float = YARN_FACTOR, orig_ctx: int = NATIVE_CTX, base: float = ROPE_BASE,
+                  alpha: float = YARN_ALPHA, beta: float = YARN_BETA) -> np.ndarray:
+    """YaRN-scaled frequencies of the 32 rotary pairs (64 rotated dims).
+
+    [ailearn] headline figures (262K -> 1M, YaRN) and §07 Deployment, [card]
+    structure paragraph: the native 262,144-token window is extended
+    statically to 1M with YaRN.  The pages give no
+    constants, so this follows the YaRN paper (Peng et al., 2023) as
+    published: for the pair with frequency theta (wavelength 2 pi / theta),
+    r = orig_ctx / wavelength counts the rotations over the native window;
+    gamma(r) = 0 below alpha, 1 above beta, linear in between; the new
+    frequency is (1 - gamma) theta / s + gamma theta.  float64.
+    """
+    j = np.arange(D_ROPE // 2, dtype=np.float64)
+    theta = base ** (-2.0 * j / D_ROPE)
+    wavelength = 2.0 * np.pi / theta
+    r = orig_ctx / wavelength
+    gamma = np.clip((r - alpha) / (beta - alpha), 0.0, 1.0)
+    return (1.0 - gamma) * theta / factor + gamma * theta
+
+
+def yarn_softmax_scale(factor: float = YARN_FACTOR) -> float:
+    """Softmax scale of the core attention under YaRN: the logits q.k / 16 are
+    divided by the paper's temperature t, with sqrt(1/t) = 0.1 ln(s) + 1.
+    Reading: the whole logit is scaled (the paper's form for full RoPE)."""
+    return SOFTMAX_SCALE * (0.1 * np.log(factor) + 1.0) ** 2
+
+
 # ------------------------------------------------------------ core attention
 
-def rope(x: np.ndarray, pos) -> np.ndarray:
+def rope(x: np.ndarray, pos, inv_freq=None) -> np.ndarray:
     """Partial rotary embedding on the first 64 of 256 dims.
 
     [card] structure paragraph and [ailearn] config table (rotary dim 64) and
     second QSA step (the core uses 64 of 256 dims).  Reading: rotate-half with
-    pairs (j, j+32), angle theta_j = pos * 1e7^(-j/32), everything in float64;
-    dims 64..255 pass through.
+    pairs (j, j+32), angle theta_j = pos * f_j with f_j = 1e7^(-j/32) unless a
+    table is given (yarn_inv_freq), everything in float64; dims 64..255 pass
+    through.
 
     x: [..., 256]; pos: scalar or array broadcast against x[..., 0].
     """
     x = np.asarray(x, dtype=np.float64)
     p = np.asarray(pos, dtype=np.float64)[..., None]
     j = np.arange(D_ROPE // 2, dtype=np.float64)
-    theta = p * ROPE_BASE ** (-2.0 * j / D_ROPE)
+    f = ROPE_BASE ** (-2.0 * j / D_ROPE) if inv_freq is None else np.asarray(inv_freq, np.float64)
+    theta = p * f
     c, s = np.cos(theta), np.sin(theta)
     y = x.copy()
     x1, x2 = x[..., :D_ROPE // 2], x[..., D_ROPE // 2:D_ROPE]
@@ -297,12 +339,13 @@ def rope(x: np.ndarray, pos) -> np.ndarray:
 
 
 def attend(q_i: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, tokens: np.ndarray,
-           i: int):
+           i: int, inv_freq=None, scale=None):
     """Exact GQA softmax attention of query i over the token set S_i.
 
     [ailearn] §03 fifth QSA step: the 24-query / 2-KV core attends exactly over
-    the original tokens of S_i.  Q and K are rotated at their own positions;
-    logits are scaled by 1/16; head h reads KV head floor(h/12).
+    the original tokens of S_i.  Q and K are rotated at their own positions
+    (with the frequency table inv_freq, default 1e7^(-j/32)); logits are
+    scaled by `scale` (default 1/16); head h reads KV head floor(h/12).
 
     q_i: [24][256] raw query; tokens: the positions of S_i; k_rows, v_rows:
     [len(tokens)][2][256] the raw cache rows of those tokens (K not rotated).
@@ -310,15 +353,16 @@ def attend(q_i: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, tokens: np.n
     scaled logits.
     """
     S = np.asarray(tokens, dtype=np.int64)
-    qr = rope(np.asarray(q_i, dtype=np.float64), i)
-    kr = rope(np.asarray(k_rows, dtype=np.float64), S[:, None])     # [n][2][256]
+    qr = rope(np.asarray(q_i, dtype=np.float64), i, inv_freq)
+    kr = rope(np.asarray(k_rows, dtype=np.float64), S[:, None], inv_freq)     # [n][2][256]
+    sm = SOFTMAX_SCALE if scale is None else float(scale)
     vs = np.asarray(v_rows, dtype=np.float64)                       # [n][2][256]
     assert kr.shape[0] == S.shape[0] and vs.shape[0] == S.shape[0]
     out = np.empty((H_Q, D), dtype=np.float64)
     lse = np.empty(H_Q, dtype=np.float64)
     for h in range(H_Q):
         g = h // GROUP
-        logits = (kr[:, g, :] @ qr[h]) * SOFTMAX_SCALE
+        logits = (kr[:, g, :] @ qr[h]) * sm
         m = logits.max()
         p = np.exp(logits - m)
         l = p.sum()

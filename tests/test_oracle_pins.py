@@ -475,3 +475,71 @@ def test_oracle_transform_queries_norm_then_rope_per_head():
     y = O.transform_queries(np.stack([q, q]), np.array([0, 9]), gamma=g, rounded=False)
     assert np.array_equal(y[1], O.transform_queries(q, 9, gamma=g, rounded=False))
     assert np.array_equal(y[0], O.transform_queries(q, 0, gamma=g, rounded=False))
+
+
+# -------------------------------------------------------------------- YaRN
+
+def test_oracle_yarn_frequencies_closed_forms():
+    base = 10.0 ** (-7.0 * np.arange(32) / 32.0)              # the unscaled 1e7^(-j/32)
+    # s = 1 changes nothing; the temperature is then 1
+    assert np.allclose(O.yarn_inv_freq(factor=1.0), base, rtol=1e-15, atol=0)
+    assert O.yarn_softmax_scale(1.0) == 1.0 / 16.0
+    f = O.yarn_inv_freq()                                      # s = 4 over 262,144 tokens
+    L = 262144
+    for j in range(32):
+        wavelength = 2 * math.pi / base[j]
+        if wavelength * 32 <= L:            # >= 32 rotations in the native window: kept
+            assert abs(f[j] - base[j]) <= 1e-15 * base[j], j
+        if wavelength >= L:                 # < 1 rotation: plain interpolation by s
+            assert abs(f[j] - base[j] / 4) <= 1e-15 * base[j], j
+    assert f[0] == 1.0 and abs(f[31] - base[31] / 4) <= 1e-15 * base[31]
+    ratio = f / base
+    assert np.all(np.diff(ratio) <= 1e-15) and ratio[0] == 1.0 and abs(ratio[-1] - 0.25) < 1e-15
+    # inside the ramp: a window of 2 pi * 8.75 tokens gives pair 0 (frequency 1)
+    # r = 8.75 rotations, gamma = (8.75 - 1) / 31 = 1/4: f = (3/4) / 4 + 1/4
+    g = O.yarn_inv_freq(factor=4.0, orig_ctx=2 * math.pi * 8.75)
+    assert abs(g[0] - 0.4375) < 1e-15
+    # r = 24.25: gamma = 3/4, f = (1/4) / 2 + 3/4 with s = 2
+    g = O.yarn_inv_freq(factor=2.0, orig_ctx=2 * math.pi * 24.25)
+    assert abs(g[0] - 0.875) < 1e-15
+
+
+def test_oracle_yarn_temperature_and_interpolation():
+    # sqrt(1/t) = 0.1 ln s + 1: s = 4 multiplies the logits by 1.1386...^2
+    assert abs(O.yarn_softmax_scale(4.0) * 16 - (1 + 0.1 * math.log(4.0)) ** 2) < 1e-15
+    assert abs(O.yarn_softmax_scale(4.0) * 16 - 1.2964769927807) < 1e-12
+    # interpolated pairs at position s*m rotate like the original ones at m
+    f = O.yarn_inv_freq()
+    e = np.zeros(256)
+    e[31] = 1.0
+    for m in (1, 1000, 262143):
+        a = O.rope(e, 4 * m, inv_freq=f)
+        b = O.rope(e, m)
+        assert np.allclose(a, b, rtol=0, atol=1e-12)
+    # a kept pair is unchanged at every position
+    e = np.zeros(256)
+    e[0] = 1.0
+    assert np.allclose(O.rope(e, 777, inv_freq=f), O.rope(e, 777), rtol=0, atol=0)
+
+
+def test_oracle_attend_scale_is_a_logit_multiplier():
+    rng = np.random.default_rng(43)
+    q, k, v = rng.standard_normal((24, 256)), rng.standard_normal((9, 2, 256)), rng.standard_normal((9, 2, 256))
+    S = np.array([0, 1, 2, 3, 8, 9, 10, 11, 12])
+    o1, l1 = O.attend(2.0 * q, k, v, S, 12)                    # logits doubled through q
+    o2, l2 = O.attend(q, k, v, S, 12, scale=2.0 / 16.0)        # ... or through the scale
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-12) and np.allclose(l1, l2, rtol=1e-12)
+    o0, l0 = O.attend(q, k, v, S, 12, scale=0.0)               # no logits: the plain mean
+    for h in range(24):
+        assert np.allclose(o0[h], v[:, h // 12, :].mean(0), atol=1e-12)
+    assert np.allclose(l0, math.log(9.0))
+    f = O.yarn_inv_freq()
+    o3, _ = O.attend(q, k, v, S, 12, inv_freq=O.yarn_inv_freq(factor=1.0))
+    o4, _ = O.attend(q, k, v, S, 12)
+    assert np.allclose(o3, o4, rtol=1e-12, atol=1e-12)
+    o5, _ = O.attend(q, k, v, S, 12, inv_freq=f)
+    assert not np.allclose(o5, o4, atol=1e-6)                  # the table is used
+    # Q and K take the same table: moving the query and its keys together
+    # (by a multiple of 4, so the block structure is unchanged) keeps the output
+    o6, _ = O.attend(q, k, v, S + 4000, 12 + 4000, inv_freq=f)
+    assert np.allclose(o5, o6, rtol=1e-9, atol=1e-9)

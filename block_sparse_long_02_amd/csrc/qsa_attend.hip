@@ -64,7 +64,7 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
               int64_t seq_stride, int64_t head_stride,
               const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int budget,
               int n_splits, int one_per_seq, uint16_t* __restrict__ out,
-              float* __restrict__ lse, float* __restrict__ part) {
+              float* __restrict__ lse, float* __restrict__ part, RopeFreq fr, float sm_scale) {
   __shared__ AttnShared sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -110,7 +110,7 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
 
   const uint16_t* kbase = kc + (int64_t)s * seq_stride + (int64_t)g * head_stride;
   const uint16_t* vbase = vc + (int64_t)s * seq_stride + (int64_t)g * head_stride;
-  const float scale = kLog2e / 16.0f;
+  const float scale = kLog2e * sm_scale;   // logits in log2 units
 
   f32x4 o[16];
 #pragma unroll
@@ -147,7 +147,7 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   if (threadIdx.x == 0 && tail_len > 0) sh.list[cnt] = n_c;
   if (threadIdx.x < kRopeDim / 2) {
     double sd, cd;
-    sincos((double)pos * rope_inv_freq(threadIdx.x), &sd, &cd);
+    sincos((double)pos * freq_at(fr, threadIdx.x), &sd, &cd);
     sh.cs[threadIdx.x][0] = (float)cd;
     sh.cs[threadIdx.x][1] = (float)sd;
   }
@@ -374,8 +374,11 @@ int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_le
                        int32_t n_q, int32_t max_q_len, const void* k_cache, const void* v_cache,
                        int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
                        const int32_t* sel_count, int32_t budget, void* out, float* lse,
-                       void* stream) {
+                       const double* inv_freq, float softmax_scale, void* stream) {
   if (n_q < 0 || n_seq < 0 || max_q_len < 0) return QSA_ERR_INVALID_ARG;
+  qsa::RopeFreq fr;
+  if (!qsa_host::make_rope_freq(inv_freq, fr) || !qsa_host::softmax_scale_ok(softmax_scale))
+    return QSA_ERR_INVALID_ARG;
   if (n_q == 0) return QSA_OK;
   if (n_seq == 0 || !cu_q || !seq_len) return QSA_ERR_INVALID_ARG;
   int st = check_attend_common(q, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
@@ -385,7 +388,7 @@ int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_le
   hipLaunchKernelGGL(qsa::attend_kernel<true>, dim3(n_q * 2), dim3(256), 0, (hipStream_t)stream,
                      (const uint16_t*)q, cu_q, seq_len, n_seq, n_q, (const uint16_t*)k_cache,
                      (const uint16_t*)v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
-                     budget, 1, 0, (uint16_t*)out, lse, (float*)nullptr);
+                     budget, 1, 0, (uint16_t*)out, lse, (float*)nullptr, fr, softmax_scale);
   return qsa_host::launch_status();
 }
 
@@ -398,9 +401,12 @@ int qsa_attend_decode_multi(const void* q, const int32_t* cu_q, const int32_t* s
                             int32_t n_seq, int32_t n_q, const void* k_cache, const void* v_cache,
                             int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
                             const int32_t* sel_count, int32_t budget, void* out, float* lse,
-                            void* workspace, size_t ws_bytes, void* stream) {
+                            void* workspace, size_t ws_bytes, const double* inv_freq,
+                            float softmax_scale, void* stream) {
   using namespace qsa_host;
   if (n_q < 0 || n_seq < 0) return QSA_ERR_INVALID_ARG;
+  qsa::RopeFreq fr;
+  if (!make_rope_freq(inv_freq, fr) || !softmax_scale_ok(softmax_scale)) return QSA_ERR_INVALID_ARG;
   if (n_q == 0) return QSA_OK;
   if (n_seq == 0 || !cu_q || !seq_len) return QSA_ERR_INVALID_ARG;
   int st = check_attend_common(q, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
@@ -414,7 +420,7 @@ int qsa_attend_decode_multi(const void* q, const int32_t* cu_q, const int32_t* s
                      (hipStream_t)stream, (const uint16_t*)q, cu_q, seq_len, n_seq, n_q,
                      (const uint16_t*)k_cache, (const uint16_t*)v_cache, kv_seq_stride,
                      kv_head_stride, sel, sel_count, budget, kDecodeSplits, 0,
-                     (uint16_t*)nullptr, (float*)nullptr, part);
+                     (uint16_t*)nullptr, (float*)nullptr, part, fr, softmax_scale);
   hipLaunchKernelGGL(qsa::combine_kernel<kDecodeSplits>, dim3(n_q * 2 * qsa::kGroup), dim3(256), 0,
                      (hipStream_t)stream, (const float*)part, n_q, (uint16_t*)out, lse);
   return launch_status();
@@ -428,9 +434,12 @@ size_t qsa_attend_decode_workspace(int32_t n_seq) {
 int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq, const void* k_cache,
                       const void* v_cache, int64_t kv_seq_stride, int64_t kv_head_stride,
                       const int32_t* sel, const int32_t* sel_count, int32_t budget, void* out,
-                      float* lse, void* workspace, size_t ws_bytes, void* stream) {
+                      float* lse, void* workspace, size_t ws_bytes, const double* inv_freq,
+                      float softmax_scale, void* stream) {
   using namespace qsa_host;
   if (n_seq < 0) return QSA_ERR_INVALID_ARG;
+  qsa::RopeFreq fr;
+  if (!make_rope_freq(inv_freq, fr) || !softmax_scale_ok(softmax_scale)) return QSA_ERR_INVALID_ARG;
   if (n_seq == 0) return QSA_OK;
   if (!seq_len) return QSA_ERR_INVALID_ARG;
   int st = check_attend_common(q, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
@@ -444,7 +453,7 @@ int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq, cons
                      (hipStream_t)stream, (const uint16_t*)q, (const int32_t*)nullptr, seq_len,
                      n_seq, n_seq, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
                      kv_seq_stride, kv_head_stride, sel, sel_count, budget, kDecodeSplits, 1,
-                     (uint16_t*)nullptr, (float*)nullptr, part);
+                     (uint16_t*)nullptr, (float*)nullptr, part, fr, softmax_scale);
   hipLaunchKernelGGL(qsa::combine_kernel<kDecodeSplits>, dim3(n_seq * 2 * qsa::kGroup), dim3(256), 0,
                      (hipStream_t)stream, (const float*)part, n_seq, (uint16_t*)out, lse);
   return launch_status();

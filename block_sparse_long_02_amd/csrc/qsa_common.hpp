@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "qsa.h"
 
 namespace qsa {
@@ -51,9 +53,20 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Rotary inverse frequency 1e7^(-j/32) of rotation pair j (float64).
-__device__ __forceinline__ double rope_inv_freq(int j) {
-  return pow(1.0e7, -(double)j / (double)(kRopeDim / 2));
+// The 32 rotary frequencies f_j of the rotate-half pairs (j, j+32), passed to
+// kernels by value (256 bytes of kernel arguments).
+constexpr int kRopePairs = kRopeDim / 2;
+struct RopeFreq {
+  double f[kRopePairs];
+};
+
+// f_k for a lane-dependent k < 32, from the uniform table (a select chain,
+// no indexed load of a kernel argument)
+__device__ __forceinline__ double freq_at(const RopeFreq& fr, int k) {
+  double f = 0.0;
+#pragma unroll
+  for (int t = 0; t < kRopePairs; ++t) f = (k == t) ? fr.f[t] : f;
+  return f;
 }
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
@@ -95,5 +108,17 @@ inline int launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH_FAILED;
 }
+
+// The caller's host table of 32 frequencies, or by default the core heads'
+// 1e7^(-j/32) (float64).  False if an entry is not finite.
+inline bool make_rope_freq(const double* inv_freq, qsa::RopeFreq& fr) {
+  for (int j = 0; j < qsa::kRopePairs; ++j) {
+    fr.f[j] = inv_freq ? inv_freq[j] : std::pow(1.0e7, -(double)j / (double)qsa::kRopePairs);
+    if (!std::isfinite(fr.f[j])) return false;
+  }
+  return true;
+}
+
+inline bool softmax_scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
 }  // namespace qsa_host

@@ -28,25 +28,12 @@
 
 namespace qsa {
 
-constexpr int kIdxRopeHalf = 32;   // pairs (j, j + 32) over dims 0..63
-
-struct InvFreq {
-  double f[kIdxRopeHalf];
-};
+constexpr int kIdxRopeHalf = kRopePairs;   // pairs (j, j + 32) over dims 0..63
 
 __device__ __forceinline__ double sum16(double v) {
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m, 16);
   return v;
-}
-
-// f_k for a lane-dependent k < 32, from the uniform table (no indexed load of
-// a kernel argument)
-__device__ __forceinline__ double freq_at(const InvFreq& fr, int k) {
-  double f = 0.0;
-#pragma unroll
-  for (int t = 0; t < kIdxRopeHalf; ++t) f = (k == t) ? fr.f[t] : f;
-  return f;
 }
 
 // x[0..7]: this lane's 8 dims (part = lane % 16 holds dims 8*part..8*part+7),
@@ -97,7 +84,7 @@ pool_block_keys_normed_kernel(const uint16_t* __restrict__ idx_k, int64_t ik_str
                               uint16_t* __restrict__ bk, int64_t bk_stride,
                               const int32_t* __restrict__ blk_begin,
                               const int32_t* __restrict__ blk_end,
-                              const float* __restrict__ gamma, double eps, InvFreq fr) {
+                              const float* __restrict__ gamma, double eps, RopeFreq fr) {
   const int s = blockIdx.y;
   const int64_t b0 = blk_begin[s], b1 = blk_end[s];
   const int part = threadIdx.x & 15;
@@ -150,7 +137,7 @@ pool_block_keys_normed_kernel(const uint16_t* __restrict__ idx_k, int64_t ik_str
 __global__ void __launch_bounds__(256)
 index_query_transform_kernel(const uint16_t* q_raw, uint16_t* q_out,
                              const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
-                             int n_q, const float* __restrict__ gamma, double eps, InvFreq fr) {
+                             int n_q, const float* __restrict__ gamma, double eps, RopeFreq fr) {
   const int s = blockIdx.y;
   const int qb = cu_q[s], qe_raw = cu_q[s + 1];
   const int qe = min(qe_raw, n_q);
@@ -191,15 +178,6 @@ index_query_transform_kernel(const uint16_t* q_raw, uint16_t* q_out,
 
 namespace {
 
-bool make_freq(const double* inv_freq, qsa::InvFreq& fr) {
-  for (int j = 0; j < qsa::kIdxRopeHalf; ++j) {
-    // default: the core heads' frequencies 1e7^(-j/32)
-    fr.f[j] = inv_freq ? inv_freq[j] : std::pow(1.0e7, -(double)j / (double)qsa::kIdxRopeHalf);
-    if (!std::isfinite(fr.f[j])) return false;
-  }
-  return true;
-}
-
 bool eps_ok(double eps) { return std::isfinite(eps) && eps >= 0.0; }
 
 }  // namespace
@@ -213,8 +191,8 @@ int qsa_pool_block_keys_normed(const void* idx_k, int64_t ik_seq_stride, void* b
                                void* stream) {
   using namespace qsa_host;
   if (n_seq < 0 || max_span < 0 || !eps_ok(eps)) return QSA_ERR_INVALID_ARG;
-  qsa::InvFreq fr;
-  if (!make_freq(inv_freq, fr)) return QSA_ERR_INVALID_ARG;
+  qsa::RopeFreq fr;
+  if (!make_rope_freq(inv_freq, fr)) return QSA_ERR_INVALID_ARG;
   if (n_seq == 0 || max_span == 0) return QSA_OK;
   if (!idx_k || !block_keys || !blk_begin || !blk_end) return QSA_ERR_INVALID_ARG;
   if (!aligned16(idx_k) || !aligned16(block_keys)) return QSA_ERR_INVALID_ARG;
@@ -234,8 +212,8 @@ int qsa_index_query_transform(const void* q_raw, void* q_out, const int32_t* cu_
                               const double* inv_freq, void* stream) {
   using namespace qsa_host;
   if (n_seq < 0 || n_q < 0 || max_q_len < 0 || !eps_ok(eps)) return QSA_ERR_INVALID_ARG;
-  qsa::InvFreq fr;
-  if (!make_freq(inv_freq, fr)) return QSA_ERR_INVALID_ARG;
+  qsa::RopeFreq fr;
+  if (!make_rope_freq(inv_freq, fr)) return QSA_ERR_INVALID_ARG;
   if (n_seq == 0 || n_q == 0 || max_q_len == 0) return QSA_OK;
   if (!q_raw || !q_out || !cu_q || !seq_len) return QSA_ERR_INVALID_ARG;
   if (!aligned16(q_raw) || !aligned16(q_out)) return QSA_ERR_INVALID_ARG;

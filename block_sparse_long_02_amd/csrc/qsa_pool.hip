@@ -48,14 +48,15 @@ pool_block_keys_kernel(const uint16_t* __restrict__ idx_k, int64_t ik_stride,
 __global__ void __launch_bounds__(256)
 rope_apply_kernel(uint16_t* __restrict__ x, int64_t row_stride, int64_t head_stride,
                   int32_t n_heads, const int32_t* __restrict__ pos, int32_t pos0,
-                  int64_t n_pairs) {
+                  int64_t n_pairs, RopeFreq fr) {
   const int j = threadIdx.x & 31;
+  const double fj = freq_at(fr, j);
   for (int64_t rh = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5); rh < n_pairs;
        rh += (int64_t)gridDim.x * 8) {
     const int64_t r = rh / n_heads;
     const int h = (int)(rh - r * n_heads);
     const int32_t p = pos ? pos[r] : pos0 + (int32_t)r;
-    double theta = (double)p * rope_inv_freq(j);
+    double theta = (double)p * fj;
     double sd, cd;
     sincos(theta, &sd, &cd);
     const float c = (float)cd, s = (float)sd;
@@ -86,7 +87,7 @@ const char* qsa_status_string(int status) {
   }
 }
 
-int qsa_abi_version(void) { return 2; }
+int qsa_abi_version(void) { return 3; }
 
 int qsa_pool_block_keys(const void* idx_k, int64_t ik_seq_stride, void* block_keys,
                         int64_t bk_seq_stride, const int32_t* blk_begin, const int32_t* blk_end,
@@ -109,9 +110,12 @@ int qsa_pool_block_keys(const void* idx_k, int64_t ik_seq_stride, void* block_ke
 }
 
 int qsa_rope_apply(void* x, int64_t row_stride, int64_t head_stride, int32_t n_heads,
-                   const int32_t* pos, int32_t pos0, int32_t n_rows, void* stream) {
+                   const int32_t* pos, int32_t pos0, int32_t n_rows, const double* inv_freq,
+                   void* stream) {
   using namespace qsa_host;
   if (n_rows < 0 || n_heads < 0) return QSA_ERR_INVALID_ARG;
+  qsa::RopeFreq fr;
+  if (!make_rope_freq(inv_freq, fr)) return QSA_ERR_INVALID_ARG;
   if (n_rows == 0 || n_heads == 0) return QSA_OK;
   if (!x || !aligned16(x)) return QSA_ERR_INVALID_ARG;
   if (!stride_ok(row_stride) || !stride_ok(head_stride)) return QSA_ERR_INVALID_ARG;
@@ -122,8 +126,36 @@ int qsa_rope_apply(void* x, int64_t row_stride, int64_t head_stride, int32_t n_h
   int64_t gx = (n_pairs + 7) / 8;
   if (gx > 1 << 20) gx = 1 << 20;
   hipLaunchKernelGGL(qsa::rope_apply_kernel, dim3((unsigned)gx), dim3(256), 0, (hipStream_t)stream,
-                     (uint16_t*)x, row_stride, head_stride, n_heads, pos, pos0, n_pairs);
+                     (uint16_t*)x, row_stride, head_stride, n_heads, pos, pos0, n_pairs, fr);
   return launch_status();
+}
+
+// YaRN (Peng et al., 2023) for the 32 rotary pairs: a pair of frequency
+// theta turns r = orig_ctx / (2 pi / theta) times over the native window;
+// gamma = clamp((r - alpha) / (beta - alpha), 0, 1); the new frequency is
+// (1 - gamma) theta / factor + gamma theta.  The logit multiplier is
+// (0.1 ln factor + 1)^2 (the paper's temperature, sqrt(1/t) = 0.1 ln s + 1).
+int qsa_yarn_rope(double base, double factor, double orig_ctx, double alpha, double beta,
+                  double* inv_freq, float* softmax_scale) {
+  if (!inv_freq) return QSA_ERR_INVALID_ARG;
+  if (!std::isfinite(base) || base <= 1.0 || !std::isfinite(factor) || factor < 1.0 ||
+      !std::isfinite(orig_ctx) || orig_ctx <= 0.0 || !std::isfinite(alpha) ||
+      !std::isfinite(beta) || !(alpha >= 0.0) || !(beta > alpha))
+    return QSA_ERR_INVALID_ARG;
+  const double two_pi = 2.0 * 3.14159265358979323846;
+  for (int j = 0; j < qsa::kRopePairs; ++j) {
+    const double theta = std::pow(base, -2.0 * (double)j / (double)qsa::kRopeDim);
+    const double wavelength = two_pi / theta;
+    const double r = orig_ctx / wavelength;
+    double gamma = (r - alpha) / (beta - alpha);
+    gamma = gamma < 0.0 ? 0.0 : (gamma > 1.0 ? 1.0 : gamma);
+    inv_freq[j] = (1.0 - gamma) * theta / factor + gamma * theta;
+  }
+  if (softmax_scale) {
+    const double t = 0.1 * std::log(factor) + 1.0;
+    *softmax_scale = (float)(t * t / 16.0);
+  }
+  return QSA_OK;
 }
 
 }  // extern "C"

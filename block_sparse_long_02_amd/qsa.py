@@ -21,6 +21,7 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID_ARG", 2: "QSA_ERR_UNSUPPORTED",
           3: "QSA_ERR_WORKSPACE_TOO_SMALL", 4: "QSA_ERR_LAUNCH_FAILED", 5: "QSA_ERR_INTERNAL"}
 
 BLOCK, IDX_HEADS, IDX_DIM, Q_HEADS, KV_HEADS, HEAD_DIM, ROPE_DIM, MAX_BUDGET = 4, 4, 128, 24, 2, 256, 64, 512
+SOFTMAX_SCALE = 1.0 / 16.0
 
 _c_void_p, _i32, _i64, _size = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 
@@ -30,7 +31,9 @@ SIGNATURES = {
     "qsa_abi_version": (ctypes.c_int, []),
     "qsa_pool_block_keys": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _c_void_p,
                                            _i32, _i32, _c_void_p]),
-    "qsa_rope_apply": (ctypes.c_int, [_c_void_p, _i64, _i64, _i32, _c_void_p, _i32, _i32, _c_void_p]),
+    "qsa_rope_apply": (ctypes.c_int, [_c_void_p, _i64, _i64, _i32, _c_void_p, _i32, _i32, _c_void_p,
+                                      _c_void_p]),
+    "qsa_yarn_rope": (ctypes.c_int, [ctypes.c_double] * 5 + [_c_void_p, _c_void_p]),
     "qsa_pool_block_keys_normed": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _i64, _c_void_p,
                                                   _c_void_p, _i32, _i32, _c_void_p, ctypes.c_double,
                                                   _c_void_p, _c_void_p]),
@@ -43,15 +46,16 @@ SIGNATURES = {
                                         _size, _c_void_p]),
     "qsa_attend_prefill": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p,
                                           _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32, _c_void_p,
-                                          _c_void_p, _c_void_p]),
+                                          _c_void_p, _c_void_p, ctypes.c_float, _c_void_p]),
     "qsa_attend_decode_workspace": (_size, [_i32]),
     "qsa_attend_decode": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i64, _i64,
                                          _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p,
-                                         _size, _c_void_p]),
+                                         _size, _c_void_p, ctypes.c_float, _c_void_p]),
     "qsa_attend_decode_multi_workspace": (_size, [_i32]),
     "qsa_attend_decode_multi": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
                                                _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32,
-                                               _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+                                               _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p,
+                                               ctypes.c_float, _c_void_p]),
 }
 
 _lib = None
@@ -99,6 +103,16 @@ def _dev(*ts):
             raise ValueError("QSA tensors must be on the GPU")
 
 
+def _host_f64(a):
+    """(pointer, keep-alive) for an optional host float64 array of 32 frequencies."""
+    if a is None:
+        return None, None
+    if len(a) != 32:
+        raise ValueError("inv_freq holds 32 float64 frequencies")
+    buf = (ctypes.c_double * 32)(*[float(v) for v in a])
+    return ctypes.cast(buf, ctypes.c_void_p), buf
+
+
 def status_string(status: int) -> str:
     return lib().qsa_status_string(status).decode()
 
@@ -116,22 +130,25 @@ def pool_block_keys(idx_k, block_keys, blk_begin, blk_end, max_span, stream=None
     _check("qsa_pool_block_keys", st)
 
 
-def rope_apply(x, row_stride, head_stride, n_heads, n_rows, pos=None, pos0=0, stream=None):
+def rope_apply(x, row_stride, head_stride, n_heads, n_rows, pos=None, pos0=0, inv_freq=None,
+               stream=None):
     """Rotate dims 0..63 of n_rows x n_heads bf16 vectors of x in place."""
     _dev(x, pos)
+    fp, _keep = _host_f64(inv_freq)
     st = lib().qsa_rope_apply(_p(x), int(row_stride), int(head_stride), int(n_heads), _p(pos),
-                              int(pos0), int(n_rows), _stream(stream))
+                              int(pos0), int(n_rows), fp, _stream(stream))
     _check("qsa_rope_apply", st)
 
 
-def _host_f64(a):
-    """(pointer, keep-alive) for an optional host float64 array of 32 frequencies."""
-    if a is None:
-        return None, None
-    if len(a) != 32:
-        raise ValueError("inv_freq holds 32 float64 frequencies")
-    buf = (ctypes.c_double * 32)(*[float(v) for v in a])
-    return ctypes.cast(buf, ctypes.c_void_p), buf
+def yarn_rope(base=1.0e7, factor=4.0, orig_ctx=262144, alpha=1.0, beta=32.0):
+    """(32 YaRN rotary frequencies, softmax scale) from the library's host helper."""
+    buf = (ctypes.c_double * 32)()
+    sc = ctypes.c_float()
+    st = lib().qsa_yarn_rope(float(base), float(factor), float(orig_ctx), float(alpha), float(beta),
+                             ctypes.cast(buf, ctypes.c_void_p), ctypes.cast(ctypes.pointer(sc),
+                                                                             ctypes.c_void_p))
+    _check("qsa_yarn_rope", st)
+    return list(buf), sc.value
 
 
 def pool_block_keys_normed(idx_k, block_keys, blk_begin, blk_end, max_span, gamma=None, eps=1e-6,
@@ -173,12 +190,13 @@ def index_select(idx_q, w, cu_q, seq_len, max_q_len, max_blocks, block_keys, bud
 
 
 def attend_prefill(q, cu_q, seq_len, max_q_len, k_cache, v_cache, sel, sel_count, budget, out,
-                   lse=None, stream=None):
+                   lse=None, inv_freq=None, softmax_scale=SOFTMAX_SCALE, stream=None):
     _dev(q, cu_q, seq_len, k_cache, v_cache, sel, sel_count, out, lse)
+    fp, _keep = _host_f64(inv_freq)
     st = lib().qsa_attend_prefill(_p(q), _p(cu_q), _p(seq_len), seq_len.numel(), q.shape[0],
                                   int(max_q_len), _p(k_cache), _p(v_cache), k_cache.stride(0),
                                   k_cache.stride(1), _p(sel), _p(sel_count), int(budget), _p(out),
-                                  _p(lse), _stream(stream))
+                                  _p(lse), fp, float(softmax_scale), _stream(stream))
     _check("qsa_attend_prefill", st)
 
 
@@ -187,12 +205,14 @@ def attend_decode_workspace(n_seq) -> int:
 
 
 def attend_decode(q, seq_len, k_cache, v_cache, sel, sel_count, budget, out, lse, workspace,
-                  stream=None):
+                  inv_freq=None, softmax_scale=SOFTMAX_SCALE, stream=None):
     _dev(q, seq_len, k_cache, v_cache, sel, sel_count, out, lse, workspace)
+    fp, _keep = _host_f64(inv_freq)
     st = lib().qsa_attend_decode(_p(q), _p(seq_len), seq_len.numel(), _p(k_cache), _p(v_cache),
                                  k_cache.stride(0), k_cache.stride(1), _p(sel), _p(sel_count),
                                  int(budget), _p(out), _p(lse), _p(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(stream))
+                                 workspace.numel() * workspace.element_size(), fp,
+                                 float(softmax_scale), _stream(stream))
     _check("qsa_attend_decode", st)
 
 
@@ -201,12 +221,13 @@ def attend_decode_multi_workspace(n_q) -> int:
 
 
 def attend_decode_multi(q, cu_q, seq_len, k_cache, v_cache, sel, sel_count, budget, out, lse,
-                        workspace, stream=None):
+                        workspace, inv_freq=None, softmax_scale=SOFTMAX_SCALE, stream=None):
     _dev(q, cu_q, seq_len, k_cache, v_cache, sel, sel_count, out, lse, workspace)
+    fp, _keep = _host_f64(inv_freq)
     st = lib().qsa_attend_decode_multi(_p(q), _p(cu_q), _p(seq_len), seq_len.numel(), q.shape[0],
                                        _p(k_cache), _p(v_cache), k_cache.stride(0),
                                        k_cache.stride(1), _p(sel), _p(sel_count), int(budget),
                                        _p(out), _p(lse), _p(workspace),
-                                       workspace.numel() * workspace.element_size(),
-                                       _stream(stream))
+                                       workspace.numel() * workspace.element_size(), fp,
+                                       float(softmax_scale), _stream(stream))
     _check("qsa_attend_decode_multi", st)

@@ -15,10 +15,13 @@ from .workloads import QSABatch, R, v_cache_layout
 
 class QSARunner:
     def __init__(self, batch: QSABatch, decode: bool | None = None, transforms: bool = False,
-                 gamma_k=None, gamma_q=None, eps: float = 1e-6):
+                 gamma_k=None, gamma_q=None, eps: float = 1e-6, yarn: bool = False):
         """transforms=True applies the pages' indexer transforms: block keys are
         pooled, RMS-normalised and rotated; each step first normalises and
-        rotates the indexer queries into a buffer of its own."""
+        rotates the indexer queries into a buffer of its own.  yarn=True
+        extends the native 262,144-token window with YaRN (factor 4): every
+        rotation (K cache, queries, indexer transforms) takes the YaRN
+        frequencies and the core attention its softmax scale."""
         b = batch
         assert b.idx_q.is_cuda, "batch must live on the GPU"
         self.b = b
@@ -35,12 +38,13 @@ class QSARunner:
         cap = b.l_cap
         self.transforms, self.gamma_k, self.gamma_q, self.eps = transforms, gamma_k, gamma_q, eps
         self.idx_q_t = torch.empty_like(b.idx_q) if transforms else None
+        self.inv_freq, self.softmax_scale = qsa.yarn_rope() if yarn else (None, qsa.SOFTMAX_SCALE)
 
         # caches: K rotated once at its positions (cache-write time), V re-laid out
         self.k_cache = b.k.clone()
         for s in range(self.n_seq):
             qsa.rope_apply(self.k_cache[s], row_stride=256, head_stride=cap * 256, n_heads=2,
-                           n_rows=lens[s], pos0=0)
+                           n_rows=lens[s], pos0=0, inv_freq=self.inv_freq)
         self.v_cache = v_cache_layout(b.v)
         self.block_keys = torch.zeros((self.n_seq, cap // R, 128), dtype=torch.bfloat16, device=dev)
 
@@ -68,7 +72,8 @@ class QSARunner:
     def _pool(self, begin, end, span, stream=None):
         if self.transforms:
             qsa.pool_block_keys_normed(self.b.idx_k, self.block_keys, begin, end, span,
-                                       gamma=self.gamma_k, eps=self.eps, stream=stream)
+                                       gamma=self.gamma_k, eps=self.eps, inv_freq=self.inv_freq,
+                                       stream=stream)
         else:
             qsa.pool_block_keys(self.b.idx_k, self.block_keys, begin, end, span, stream=stream)
 
@@ -82,7 +87,8 @@ class QSARunner:
         idx_q = b.idx_q
         if self.transforms:
             qsa.index_query_transform(b.idx_q, self.idx_q_t, b.cu_q, b.seq_len, self.max_q_len,
-                                      gamma=self.gamma_q, eps=self.eps, stream=stream)
+                                      gamma=self.gamma_q, eps=self.eps, inv_freq=self.inv_freq,
+                                      stream=stream)
             idx_q = self.idx_q_t
         qsa.index_select(idx_q, b.w, b.cu_q, b.seq_len, self.max_q_len, self.max_blocks,
                          self.block_keys, self.budget, self.sel, self.sel_count, self.ws_index,
@@ -90,17 +96,17 @@ class QSARunner:
 
     def attend(self, stream=None):
         b = self.b
+        rope = dict(inv_freq=self.inv_freq, softmax_scale=self.softmax_scale, stream=stream)
         if self.decode:
             qsa.attend_decode(b.q, b.seq_len, self.k_cache, self.v_cache, self.sel, self.sel_count,
-                              self.budget, self.out, self.lse, self.ws_decode, stream=stream)
+                              self.budget, self.out, self.lse, self.ws_decode, **rope)
         elif self.mtp:
             qsa.attend_decode_multi(b.q, b.cu_q, b.seq_len, self.k_cache, self.v_cache, self.sel,
                                     self.sel_count, self.budget, self.out, self.lse, self.ws_decode,
-                                    stream=stream)
+                                    **rope)
         else:
             qsa.attend_prefill(b.q, b.cu_q, b.seq_len, self.max_q_len, self.k_cache, self.v_cache,
-                               self.sel, self.sel_count, self.budget, self.out, self.lse,
-                               stream=stream)
+                               self.sel, self.sel_count, self.budget, self.out, self.lse, **rope)
 
     def step(self, stream=None):
         self.pool(stream)

@@ -111,17 +111,39 @@ int qsa_pool_block_keys(const void* idx_k, int64_t ik_seq_stride,
  * a5 helper -- partial RoPE of cache keys at write time.  [card] and
  * [ailearn] config table: rotary on 64 of the 256 dims of a core head;
  * [ailearn] §03 second QSA step.  Rotate-half on dims 0..63 with pairs
- * (j, j+32), theta_j = pos * 1e7^(-j/32) taken in float64, cos/sin in float64
+ * (j, j+32), theta_j = pos * f_j taken in float64, cos/sin in float64
  * rounded to float32, rotation in float32, result rounded to bf16; dims
  * 64..255 are untouched.  In place.
  *
  * Row r, head h occupies x + r*row_stride + h*head_stride (bf16, 256 dims).
  * Its position is pos[r] (device int32) or, when pos == NULL, pos0 + r.
  * Used on the K cache once per token; queries are rotated inside the
- * attention kernels instead.
+ * attention kernels instead, which must be given the same frequencies.
+ * inv_freq: HOST float64 [32] table of f_j, copied at the call; NULL gives
+ * the native 1e7^(-j/32); qsa_yarn_rope fills the YaRN table.
  */
 int qsa_rope_apply(void* x, int64_t row_stride, int64_t head_stride, int32_t n_heads,
-                   const int32_t* pos, int32_t pos0, int32_t n_rows, void* stream);
+                   const int32_t* pos, int32_t pos0, int32_t n_rows,
+                   const double* inv_freq, void* stream);
+
+/*
+ * f4 -- YaRN context extension (host only, enqueues nothing).  [card]
+ * structure paragraph and [ailearn] headline figures and §07 Deployment: the
+ * native 262,144-token window is extended statically to 1M with YaRN.  The
+ * pages give no constants; this is the YaRN paper's formula (Peng et al.,
+ * 2023).  For pair j with theta = base^(-2j/64) and wavelength 2 pi / theta,
+ *   r = orig_ctx / wavelength,  gamma = clamp((r - alpha) / (beta - alpha), 0, 1),
+ *   inv_freq[j] = (1 - gamma) * theta / factor + gamma * theta      (float64)
+ * and *softmax_scale = (0.1 ln factor + 1)^2 / 16 (float32; may be NULL), the
+ * paper's temperature applied to the core logits.  The model's values are
+ * base 1e7, factor 4, orig_ctx 262144, alpha 1, beta 32.  Give the table to
+ * qsa_rope_apply, the attention calls and the indexer transforms, and the
+ * scale to the attention calls.
+ * Errors: QSA_ERR_INVALID_ARG for inv_freq == NULL, base <= 1, factor < 1,
+ * orig_ctx <= 0, alpha < 0, beta <= alpha, or non-finite values.
+ */
+int qsa_yarn_rope(double base, double factor, double orig_ctx, double alpha, double beta,
+                  double* inv_freq, float* softmax_scale);
 
 /*
  * The pages' indexer transforms (optional; the plain path above omits them).
@@ -214,20 +236,24 @@ int qsa_index_select(const void* idx_q, const float* w,
  * unfinished tail {4*n_c, ..., p}) and fifth QSA step (exact attention of the
  * 24 query heads / 2 KV heads over the original tokens of S_i).
  *
- * For every row i and head h (KV head g = h/12):
- *   out[i][h] = sum_{t in S_i} softmax_t( RoPE(q[i][h], p) . k_cache[g][t] / 16 ) v_cache[g][t]
- *   lse[i][h] = natural log of the softmax denominator (logits already / 16)
+ * For every row i and head h (KV head g = h/12), with c = softmax_scale:
+ *   out[i][h] = sum_{t in S_i} softmax_t( c * RoPE(q[i][h], p) . k_cache[g][t] ) v_cache[g][t]
+ *   lse[i][h] = natural log of the softmax denominator (logits already scaled)
  * q is the raw (unrotated) query; k_cache holds keys already rotated at their
- * positions (qsa_rope_apply).  sel / sel_count as written by qsa_index_select
- * (ascending ids; a row with count < 0 gets NaN output).
+ * positions (qsa_rope_apply with the same inv_freq).  sel / sel_count as
+ * written by qsa_index_select (ascending ids; a row with count < 0 gets NaN
+ * output).
  *   q    bf16 [n_q][24][256]   out bf16 [n_q][24][256]   lse fp32 [n_q][24] or NULL
+ *   inv_freq       HOST float64 [32] rotary frequencies, or NULL (1e7^(-j/32))
+ *   softmax_scale  finite, > 0: 1/16 = 1/sqrt(256) natively; YaRN's from qsa_yarn_rope
  */
 int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_len,
                        int32_t n_seq, int32_t n_q, int32_t max_q_len,
                        const void* k_cache, const void* v_cache,
                        int64_t kv_seq_stride, int64_t kv_head_stride,
                        const int32_t* sel, const int32_t* sel_count, int32_t budget,
-                       void* out, float* lse, void* stream);
+                       void* out, float* lse, const double* inv_freq, float softmax_scale,
+                       void* stream);
 
 /*
  * a7 -- split-K decode attention plus combine.  Same mathematics as
@@ -241,7 +267,8 @@ int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq,
                       const void* k_cache, const void* v_cache,
                       int64_t kv_seq_stride, int64_t kv_head_stride,
                       const int32_t* sel, const int32_t* sel_count, int32_t budget,
-                      void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
+                      void* out, float* lse, void* workspace, size_t ws_bytes,
+                      const double* inv_freq, float softmax_scale, void* stream);
 
 /*
  * f1 (multi-token decode) -- the split-K decode of qsa_attend_decode for a
@@ -259,7 +286,7 @@ int qsa_attend_decode_multi(const void* q, const int32_t* cu_q, const int32_t* s
                             int64_t kv_seq_stride, int64_t kv_head_stride,
                             const int32_t* sel, const int32_t* sel_count, int32_t budget,
                             void* out, float* lse, void* workspace, size_t ws_bytes,
-                            void* stream);
+                            const double* inv_freq, float softmax_scale, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,10 +19,15 @@ def np64(t: torch.Tensor) -> np.ndarray:
 class OracleView:
     """Oracle-side view of one QSABatch (float64 arrays, per sequence)."""
 
-    def __init__(self, b, transforms=False, gamma_k=None, gamma_q=None, eps=O.RMS_EPS):
+    def __init__(self, b, transforms=False, gamma_k=None, gamma_q=None, eps=O.RMS_EPS,
+                 yarn=False):
         """transforms=True: block keys and indexer queries as the pages'
-        transforms make them (gamma_* are numpy arrays or None)."""
+        transforms make them (gamma_* are numpy arrays or None).  yarn=True:
+        every rotation takes the oracle's YaRN table and the core attention
+        its softmax scale."""
         self.b = b
+        self.inv_freq = O.yarn_inv_freq() if yarn else None
+        self.scale = O.yarn_softmax_scale() if yarn else None
         self.lens = b.seq_lens_host()
         self.cu = b.cu_q_host()
         self.pos = b.q_pos_host()
@@ -33,15 +38,15 @@ class OracleView:
     def kbar(self, s):
         if s not in self._kb:
             k, n = np64(self.b.idx_k[s]), self.lens[s] // O.R
-            self._kb[s] = (O.transform_block_keys(k, n, self.gamma_k, self.eps) if self.transforms
-                           else O.pool_block_keys(k, n))
+            self._kb[s] = (O.transform_block_keys(k, n, self.gamma_k, self.eps, self.inv_freq)
+                           if self.transforms else O.pool_block_keys(k, n))
         return self._kb[s]
 
     def query(self, row):
         """The indexer query heads [4][128] of a row, as scored."""
         q = np64(self.b.idx_q[row])
         if self.transforms:
-            q = O.transform_queries(q, self.pos[row], self.gamma_q, self.eps)
+            q = O.transform_queries(q, self.pos[row], self.gamma_q, self.eps, self.inv_freq)
         return q
 
     def rows(self, s, tokens):
@@ -63,7 +68,7 @@ class OracleView:
         s, p = self.seq[row], self.pos[row]
         tokens = O.sparse_token_set(np.asarray(blocks, dtype=np.int64), p)
         k, v = self.rows(s, tokens)
-        return O.attend(np64(self.b.q[row]), k, v, tokens, p)
+        return O.attend(np64(self.b.q[row]), k, v, tokens, p, self.inv_freq, self.scale)
 
     def dense(self, row):
         """Textbook causal GQA over every token 0..pos (for budget >= n_c)."""

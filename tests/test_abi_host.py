@@ -31,7 +31,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
         assert n in qsa.SIGNATURES, n
@@ -41,7 +41,7 @@ def test_status_strings_and_version(L):
     for code, name in qsa.STATUS.items():
         assert qsa.status_string(code) == name
     assert qsa.status_string(99) == "QSA_ERR_UNKNOWN"
-    assert qsa.abi_version() == 2
+    assert qsa.abi_version() == 3
 
 
 def test_workspace_queries(L):
@@ -90,27 +90,27 @@ def test_index_select_rejects_bad_arguments(L):
 def test_attention_and_pool_reject_bad_arguments(L):
     A = ALIGNED
     # prefill: budget, alignment, null
-    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 0, A, None, None) == 1
-    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, MISALIGNED, 1024, 512, A, A, 16, A, None, None) == 1
-    assert L.qsa_attend_prefill(A, None, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, None) == 1
-    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1020, 512, A, A, 16, A, None, None) == 1
-    assert L.qsa_attend_prefill(A, A, A, 1, 0, 4, A, A, 1024, 512, A, A, 16, A, None, None) == 0
+    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 0, A, None, None, 0.0625, None) == 1
+    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, MISALIGNED, 1024, 512, A, A, 16, A, None, None, 0.0625, None) == 1
+    assert L.qsa_attend_prefill(A, None, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, None, 0.0625, None) == 1
+    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1020, 512, A, A, 16, A, None, None, 0.0625, None) == 1
+    assert L.qsa_attend_prefill(A, A, A, 1, 0, 4, A, A, 1024, 512, A, A, 16, A, None, None, 0.0625, None) == 0
     # decode: workspace too small, bad budget
-    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 100, None) == 3
-    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 600, A, A, A, 1 << 30, None) == 1
-    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, MISALIGNED, 1 << 30, None) == 1
+    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 100, None, 0.0625, None) == 3
+    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 600, A, A, A, 1 << 30, None, 0.0625, None) == 1
+    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, MISALIGNED, 1 << 30, None, 0.0625, None) == 1
     # multi-token decode: cu_q required, workspace sized by n_q
-    assert L.qsa_attend_decode_multi(A, None, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, None) == 1
-    assert L.qsa_attend_decode_multi(A, A, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 100, None) == 3
-    assert L.qsa_attend_decode_multi(A, A, A, 2, 0, A, A, 1024, 512, A, A, 16, A, A, A, 0, None) == 0
+    assert L.qsa_attend_decode_multi(A, None, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, None, 0.0625, None) == 1
+    assert L.qsa_attend_decode_multi(A, A, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 100, None, 0.0625, None) == 3
+    assert L.qsa_attend_decode_multi(A, A, A, 2, 0, A, A, 1024, 512, A, A, 16, A, A, A, 0, None, 0.0625, None) == 0
     # pooling and rope
     assert L.qsa_pool_block_keys(None, 128, A, 128, A, A, 1, 4, None) == 1
     assert L.qsa_pool_block_keys(A, 129, A, 128, A, A, 1, 4, None) == 1
     assert L.qsa_pool_block_keys(A, 128, A, 128, A, A, 0, 4, None) == 0
     assert L.qsa_pool_block_keys(A, 128, A, 128, A, A, -1, 4, None) == 1
-    assert L.qsa_rope_apply(MISALIGNED, 256, 256, 2, None, 0, 10, None) == 1
-    assert L.qsa_rope_apply(A, 256, 256, 2, None, 0, 0, None) == 0
-    assert L.qsa_rope_apply(A, 256, 256, 2, None, (1 << 22), 10, None) == 2
+    assert L.qsa_rope_apply(MISALIGNED, 256, 256, 2, None, 0, 10, None, None) == 1
+    assert L.qsa_rope_apply(A, 256, 256, 2, None, 0, 0, None, None) == 0
+    assert L.qsa_rope_apply(A, 256, 256, 2, None, (1 << 22), 10, None, None) == 2
 
 
 def test_indexer_transforms_reject_bad_arguments(L):
@@ -135,3 +135,42 @@ def test_indexer_transforms_reject_bad_arguments(L):
     assert pool(span=0) == 0 and pool(span=-1) == 1
     assert query(q=None) == 1 and query(o=MISALIGNED) == 1
     assert query(n_q=0) == 0 and query(mq=0) == 0 and query(n_q=-1) == 1
+
+
+def test_rope_tables_and_softmax_scale_are_validated(L):
+    A = ALIGNED
+    bad = (ctypes.c_double * 32)(*([1.0] * 31 + [float("nan")]))
+    badp = ctypes.cast(bad, ctypes.c_void_p)
+    for sc in (0.0, -0.0625, float("nan"), float("inf")):
+        assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, None, sc, None) == 1
+        assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, None, sc, None) == 1
+        assert L.qsa_attend_decode_multi(A, A, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, None, sc, None) == 1
+    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, badp, 0.0625, None) == 1
+    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, badp, 0.0625, None) == 1
+    assert L.qsa_rope_apply(A, 256, 256, 2, None, 0, 10, badp, None) == 1
+
+
+def test_yarn_helper_matches_the_oracle(L):
+    """Host logic: the library's YaRN table and scale against the oracle's,
+    each written separately from the YaRN paper's formula."""
+    from oracle import qsa_oracle as O
+    import numpy as np
+    f, sc = qsa.yarn_rope()
+    ref = O.yarn_inv_freq()
+    # same float64 steps; numpy's vectorised pow and the C library's pow may
+    # differ in the last bit of a frequency
+    assert np.allclose(np.asarray(f), ref, rtol=2.5e-16, atol=0)
+    assert abs(sc - O.yarn_softmax_scale()) <= 2 ** -24 * O.yarn_softmax_scale()
+    f1, sc1 = qsa.yarn_rope(factor=1.0)
+    assert np.allclose(f1, O.yarn_inv_freq(factor=1.0), rtol=5e-16, atol=0) and sc1 == 0.0625
+    for fac, ctx in ((2.0, 2 * np.pi * 24.25), (8.0, 32768.0)):
+        g, _ = qsa.yarn_rope(factor=fac, orig_ctx=ctx)
+        assert np.allclose(np.asarray(g), O.yarn_inv_freq(factor=fac, orig_ctx=ctx), rtol=5e-16, atol=0)
+    buf = (ctypes.c_double * 32)()
+    bp = ctypes.cast(buf, ctypes.c_void_p)
+    for args in ((1.0, 4.0, 262144.0, 1.0, 32.0), (1e7, 0.5, 262144.0, 1.0, 32.0),
+                 (1e7, 4.0, 0.0, 1.0, 32.0), (1e7, 4.0, 262144.0, 32.0, 32.0),
+                 (1e7, 4.0, 262144.0, -1.0, 32.0), (1e7, float("nan"), 262144.0, 1.0, 32.0)):
+        assert L.qsa_yarn_rope(*args, bp, None) == 1, args
+    assert L.qsa_yarn_rope(1e7, 4.0, 262144.0, 1.0, 32.0, None, None) == 1
+    assert L.qsa_yarn_rope(1e7, 4.0, 262144.0, 1.0, 32.0, bp, None) == 0

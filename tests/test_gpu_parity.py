@@ -93,6 +93,28 @@ def test_rope_helper_within_one_ulp():
     assert _ulps(xe, ref2).max() <= 1
 
 
+def test_rope_helper_yarn_table_within_one_ulp():
+    # the library's YaRN table against the oracle's (each from the YaRN paper)
+    g = torch.Generator().manual_seed(2)
+    n = 300
+    x = torch.randn(n, 2, 256, generator=g).to(torch.bfloat16)
+    pos = torch.randint(0, 1 << 20, (n,), generator=g, dtype=torch.int32)
+    pos[:3] = torch.tensor([0, 262143, (1 << 20) - 1], dtype=torch.int32)
+    f, _ = qsa.yarn_rope()
+    xd = x.cuda().clone()
+    qsa.rope_apply(xd, row_stride=512, head_stride=256, n_heads=2, n_rows=n, pos=pos.cuda(),
+                   inv_freq=f)
+    _sync()
+    ref = O.rope(np64(x), pos.numpy().astype(np.float64)[:, None], inv_freq=O.yarn_inv_freq())
+    assert np.array_equal(_bits(xd)[..., 64:], _bits(x)[..., 64:])
+    assert _ulps(xd, ref).max() <= 1
+    # the table is used: it differs from the native rotation at long positions
+    xn = x.cuda().clone()
+    qsa.rope_apply(xn, row_stride=512, head_stride=256, n_heads=2, n_rows=n, pos=pos.cuda())
+    _sync()
+    assert not np.array_equal(_bits(xn), _bits(xd))
+
+
 # ----------------------------------------------- attention on oracle choices
 
 def _load_oracle_selection(r, view, rows):
@@ -390,9 +412,9 @@ def test_index_select_with_transforms():
 
 # ------------------------------------------------------------- end to end
 
-def _end_to_end(b, rows, dense=False):
-    view = OracleView(b)
-    r = QSARunner(b if b.idx_q.is_cuda else b.to("cuda"))
+def _end_to_end(b, rows, dense=False, yarn=False, transforms=False):
+    view = OracleView(b, yarn=yarn, transforms=transforms)
+    r = QSARunner(b if b.idx_q.is_cuda else b.to("cuda"), yarn=yarn, transforms=transforms)
     r.step()
     _sync()
     sel, cnt = r.sel.cpu().numpy(), r.sel_count.cpu().numpy()
@@ -443,6 +465,28 @@ def test_end_to_end_ragged_decode_reduced():
     b = W.ragged_decode(n_seq=6, lo=4096, hi=200000)
     kinds, worst = _end_to_end(b, range(6))
     print("ragged decode:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_end_to_end_yarn_decode_and_prefill():
+    # YaRN-extended rotations (K cache, queries) and softmax scale, checked
+    # against the oracle's own YaRN table and scale; positions past the
+    # native 262,144 tokens included
+    b = W.make_decode(seq_lens=[270001, 131075, 5000], budget=512, n_plant=32, seed=66)
+    kinds, worst = _end_to_end(b, range(3), yarn=True)
+    print("yarn decode:", kinds, f"worst rel-L2 {worst:.2e}")
+    b = W.prefill_8k(T=2048)
+    kinds, worst = _end_to_end(b, [0, 5, 1000, 2047], dense=False, yarn=True)
+    print("yarn prefill:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_end_to_end_yarn_with_indexer_transforms():
+    # the whole path with the pages' indexer transforms and YaRN together
+    b = W.make_decode(seq_lens=[300001, 70003], budget=512, n_plant=32, seed=65)
+    kinds, worst = _end_to_end(b, range(2), yarn=True, transforms=True)
+    print("yarn + transforms decode:", kinds, f"worst rel-L2 {worst:.2e}")
+    b = W.tiny_prefill(T=512)
+    kinds, worst = _end_to_end(b, range(0, 512, 7), yarn=True, transforms=True)
+    print("yarn + transforms tiny prefill:", kinds, f"worst rel-L2 {worst:.2e}")
 
 
 # ------------------------------------------------------- multi-token decode

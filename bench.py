@@ -18,6 +18,8 @@ repeats the prefill step with the pages' indexer transforms (RMSNorm and
 partial RoPE of block keys and queries) and times each transform kernel;
 `yarn` repeats it with the transforms and the YaRN-extended rotations and
 softmax scale (the pages' configuration past the native 262,144 tokens).
+`paged` repeats the prefill and decode steps over caches kept in 256-token
+pages in a random physical order (block tables).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
@@ -40,6 +42,7 @@ MFMA_BF16_PEAK_TFS = 2500.0
 TOKEN_GATHER_BYTES = 2 * 2 * 256 * 2      # 2 KV heads x (K + V) x 256 dims x bf16
 Q_ROW_BYTES = 24 * 256 * 2
 BLOCK_KEY_BYTES = 128 * 2
+PAGE_TOKENS = 256                         # paged-cache runs: 256-token pages
 
 
 def log(*a):
@@ -87,7 +90,7 @@ def decode_traffic():
     return None if any(v is None for v in vals) else int(sum(vals))
 
 
-def time_prefill(args, transforms=False, batch=None, yarn=False):
+def time_prefill(args, transforms=False, batch=None, yarn=False, paged=None):
     """The chunked-prefill step; transforms=True runs it with the pages'
     indexer transforms (normalised, rotated block keys and queries), yarn=True
     with the YaRN-extended rotations and softmax scale."""
@@ -97,7 +100,7 @@ def time_prefill(args, transforms=False, batch=None, yarn=False):
 
     t0 = time.time()
     b = W.chunked_prefill_1m(device="cuda") if batch is None else batch
-    r = QSARunner(b, transforms=transforms, yarn=yarn)
+    r = QSARunner(b, transforms=transforms, yarn=yarn, paged=paged)
     torch.cuda.synchronize()
     log(f"prefill workload ready in {time.time() - t0:.1f}s")
     for _ in range(args.warmup):
@@ -190,16 +193,16 @@ def time_transforms(args, pre):
                           "frac": round(k_bytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
-def time_decode(args, mtp=False):
+def time_decode(args, mtp=False, paged=None):
     """Decode step (one query per sequence), or with mtp=True a multi-token
-    decode step (4 query tokens per sequence)."""
+    decode step (4 query tokens per sequence); paged=P over P-token pages."""
     import torch
     from block_sparse_long_02_amd import workloads as W
     from block_sparse_long_02_amd.runner import QSARunner
 
     t0 = time.time()
     b = W.mtp_decode_128k(device="cuda") if mtp else W.decode_128k(device="cuda")
-    r = QSARunner(b)
+    r = QSARunner(b, paged=paged)
     # 512 MB > MALL, swept by a read before each step so that the step starts
     # with none of its data cached and no dirty lines to write back
     flush = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
@@ -366,6 +369,14 @@ def main():
         out["yarn"], out["index_transforms"] = time_transforms(args, pre)
         log(f"prefill with indexer transforms: {out['index_transforms']}")
         log(f"prefill with indexer transforms and YaRN: {out['yarn']}")
+        pg = time_prefill(args, batch=pre["batch"], paged=PAGE_TOKENS)
+        out["paged"] = {"page_tokens": PAGE_TOKENS, "order": "random physical pages",
+                        "prefill": {"ms_per_step": round(pg["ms_per_step"], 4),
+                                    "value": round(pg["value"], 1), "unit": "tokens/s",
+                                    "stages_ms": {k: round(v, 4) for k, v in pg["stages_ms"].items()}}}
+        log(f"paged prefill: {out['paged']['prefill']}")
+        del pg
+        torch.cuda.empty_cache()
         del pre
         torch.cuda.empty_cache()
     if args.only in (None, "decode"):
@@ -386,6 +397,16 @@ def main():
                        config=d["config"], roofline=d["roofline"])
         else:
             out["decode"] = d
+        dec = None
+        torch.cuda.empty_cache()
+        dp = time_decode(args, paged=PAGE_TOKENS)
+        log(f"paged decode: {dp['ms_per_step']:.4f} ms/step, stages {dp['stages_ms']}")
+        out.setdefault("paged", {"page_tokens": PAGE_TOKENS, "order": "random physical pages"})
+        out["paged"]["decode"] = {"ms_per_step": round(dp["ms_per_step"], 4),
+                                  "value": round(dp["value"], 1), "unit": "tokens/s",
+                                  "stages_ms": {k: round(v, 4) for k, v in dp["stages_ms"].items()},
+                                  "hbm_frac": round(dp["hbm"]["gbs"] / HBM_PEAK_GBS, 4)}
+        dp = None
     dec = None
     torch.cuda.empty_cache()
     if args.only in (None, "mtp"):

@@ -64,7 +64,8 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
               int64_t seq_stride, int64_t head_stride,
               const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int budget,
               int n_splits, int one_per_seq, uint16_t* __restrict__ out,
-              float* __restrict__ lse, float* __restrict__ part, RopeFreq fr, float sm_scale) {
+              float* __restrict__ lse, float* __restrict__ part, RopeFreq fr, float sm_scale,
+              Pages pg) {
   __shared__ AttnShared sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -108,8 +109,10 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   const int t_end = (int)((int64_t)(my_part + 1) * n_tiles / parts);
   const int tail_slot = tail_len > 0 ? cnt : -1;
 
-  const uint16_t* kbase = kc + (int64_t)s * seq_stride + (int64_t)g * head_stride;
-  const uint16_t* vbase = vc + (int64_t)s * seq_stride + (int64_t)g * head_stride;
+  // paged caches: one pool per KV head, the list below holds physical blocks
+  const int64_t seq_off = pg.table ? 0 : (int64_t)s * seq_stride;
+  const uint16_t* kbase = kc + seq_off + (int64_t)g * head_stride;
+  const uint16_t* vbase = vc + seq_off + (int64_t)g * head_stride;
   const float scale = kLog2e * sm_scale;   // logits in log2 units
 
   f32x4 o[16];
@@ -142,9 +145,10 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   // ---- block list and the query's rotary angles into LDS
   for (int i = threadIdx.x; i < cnt; i += 256) {
     int id = sel[(int64_t)row * budget + i];
-    sh.list[i] = min(max(id, 0), n_c - 1);   // ids come ascending from the selection
+    id = min(max(id, 0), n_c - 1);   // ids come ascending from the selection
+    sh.list[i] = pg.table ? (int)phys_block(pg, s, id) : id;
   }
-  if (threadIdx.x == 0 && tail_len > 0) sh.list[cnt] = n_c;
+  if (threadIdx.x == 0 && tail_len > 0) sh.list[cnt] = pg.table ? (int)phys_block(pg, s, n_c) : n_c;
   if (threadIdx.x < kRopeDim / 2) {
     double sd, cd;
     sincos((double)pos * freq_at(fr, threadIdx.x), &sd, &cd);
@@ -374,11 +378,14 @@ int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_le
                        int32_t n_q, int32_t max_q_len, const void* k_cache, const void* v_cache,
                        int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
                        const int32_t* sel_count, int32_t budget, void* out, float* lse,
-                       const double* inv_freq, float softmax_scale, void* stream) {
+                       const double* inv_freq, float softmax_scale, const int32_t* block_table,
+                       int64_t table_stride, int32_t page_tokens, void* stream) {
   if (n_q < 0 || n_seq < 0 || max_q_len < 0) return QSA_ERR_INVALID_ARG;
   qsa::RopeFreq fr;
   if (!qsa_host::make_rope_freq(inv_freq, fr) || !qsa_host::softmax_scale_ok(softmax_scale))
     return QSA_ERR_INVALID_ARG;
+  qsa::Pages pg;
+  if (!qsa_host::make_pages(block_table, table_stride, page_tokens, pg)) return QSA_ERR_INVALID_ARG;
   if (n_q == 0) return QSA_OK;
   if (n_seq == 0 || !cu_q || !seq_len) return QSA_ERR_INVALID_ARG;
   int st = check_attend_common(q, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
@@ -388,7 +395,7 @@ int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_le
   hipLaunchKernelGGL(qsa::attend_kernel<true>, dim3(n_q * 2), dim3(256), 0, (hipStream_t)stream,
                      (const uint16_t*)q, cu_q, seq_len, n_seq, n_q, (const uint16_t*)k_cache,
                      (const uint16_t*)v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
-                     budget, 1, 0, (uint16_t*)out, lse, (float*)nullptr, fr, softmax_scale);
+                     budget, 1, 0, (uint16_t*)out, lse, (float*)nullptr, fr, softmax_scale, pg);
   return qsa_host::launch_status();
 }
 
@@ -402,11 +409,14 @@ int qsa_attend_decode_multi(const void* q, const int32_t* cu_q, const int32_t* s
                             int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
                             const int32_t* sel_count, int32_t budget, void* out, float* lse,
                             void* workspace, size_t ws_bytes, const double* inv_freq,
-                            float softmax_scale, void* stream) {
+                            float softmax_scale, const int32_t* block_table,
+                            int64_t table_stride, int32_t page_tokens, void* stream) {
   using namespace qsa_host;
   if (n_q < 0 || n_seq < 0) return QSA_ERR_INVALID_ARG;
   qsa::RopeFreq fr;
   if (!make_rope_freq(inv_freq, fr) || !softmax_scale_ok(softmax_scale)) return QSA_ERR_INVALID_ARG;
+  qsa::Pages pg;
+  if (!make_pages(block_table, table_stride, page_tokens, pg)) return QSA_ERR_INVALID_ARG;
   if (n_q == 0) return QSA_OK;
   if (n_seq == 0 || !cu_q || !seq_len) return QSA_ERR_INVALID_ARG;
   int st = check_attend_common(q, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
@@ -420,7 +430,7 @@ int qsa_attend_decode_multi(const void* q, const int32_t* cu_q, const int32_t* s
                      (hipStream_t)stream, (const uint16_t*)q, cu_q, seq_len, n_seq, n_q,
                      (const uint16_t*)k_cache, (const uint16_t*)v_cache, kv_seq_stride,
                      kv_head_stride, sel, sel_count, budget, kDecodeSplits, 0,
-                     (uint16_t*)nullptr, (float*)nullptr, part, fr, softmax_scale);
+                     (uint16_t*)nullptr, (float*)nullptr, part, fr, softmax_scale, pg);
   hipLaunchKernelGGL(qsa::combine_kernel<kDecodeSplits>, dim3(n_q * 2 * qsa::kGroup), dim3(256), 0,
                      (hipStream_t)stream, (const float*)part, n_q, (uint16_t*)out, lse);
   return launch_status();
@@ -435,11 +445,14 @@ int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq, cons
                       const void* v_cache, int64_t kv_seq_stride, int64_t kv_head_stride,
                       const int32_t* sel, const int32_t* sel_count, int32_t budget, void* out,
                       float* lse, void* workspace, size_t ws_bytes, const double* inv_freq,
-                      float softmax_scale, void* stream) {
+                      float softmax_scale, const int32_t* block_table, int64_t table_stride,
+                      int32_t page_tokens, void* stream) {
   using namespace qsa_host;
   if (n_seq < 0) return QSA_ERR_INVALID_ARG;
   qsa::RopeFreq fr;
   if (!make_rope_freq(inv_freq, fr) || !softmax_scale_ok(softmax_scale)) return QSA_ERR_INVALID_ARG;
+  qsa::Pages pg;
+  if (!make_pages(block_table, table_stride, page_tokens, pg)) return QSA_ERR_INVALID_ARG;
   if (n_seq == 0) return QSA_OK;
   if (!seq_len) return QSA_ERR_INVALID_ARG;
   int st = check_attend_common(q, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
@@ -453,7 +466,7 @@ int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq, cons
                      (hipStream_t)stream, (const uint16_t*)q, (const int32_t*)nullptr, seq_len,
                      n_seq, n_seq, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
                      kv_seq_stride, kv_head_stride, sel, sel_count, budget, kDecodeSplits, 1,
-                     (uint16_t*)nullptr, (float*)nullptr, part, fr, softmax_scale);
+                     (uint16_t*)nullptr, (float*)nullptr, part, fr, softmax_scale, pg);
   hipLaunchKernelGGL(qsa::combine_kernel<kDecodeSplits>, dim3(n_seq * 2 * qsa::kGroup), dim3(256), 0,
                      (hipStream_t)stream, (const float*)part, n_seq, (uint16_t*)out, lse);
   return launch_status();

@@ -71,6 +71,23 @@ __device__ __forceinline__ double freq_at(const RopeFreq& fr, int k) {
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
 
+// Paged caches: a sequence's caches live in pages of 2^shift micro-blocks
+// (4 * 2^shift tokens) inside shared pools; logical page p of sequence s is
+// physical page table[s * stride + p].  table == nullptr: the contiguous
+// per-sequence layout (the kernels then add their sequence strides).
+struct Pages {
+  const int32_t* table;
+  int64_t stride;
+  int shift;
+};
+
+// physical micro-block of logical micro-block b of sequence s (paged only)
+__device__ __forceinline__ int64_t phys_block(const Pages& pg, int s, int64_t b) {
+  const int64_t pi = b >> pg.shift;
+  return ((int64_t)pg.table[(int64_t)s * pg.stride + pi] << pg.shift) +
+         (b & (((int64_t)1 << pg.shift) - 1));
+}
+
 // --------------------------------------------------------- block helpers
 // Exclusive prefix sum over a 256-thread workgroup.  `tmp` holds >= 4 ints of
 // LDS.  Returns the exclusive prefix of `v`; `total` receives the sum.
@@ -120,5 +137,23 @@ inline bool make_rope_freq(const double* inv_freq, qsa::RopeFreq& fr) {
 }
 
 inline bool softmax_scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+// block_table == NULL: contiguous caches.  Otherwise page_tokens must be a
+// power of two in [256, 2^22] (a page then holds whole 64-block GEMM stages)
+// and table_stride >= 1.
+inline bool make_pages(const int32_t* block_table, int64_t table_stride, int32_t page_tokens,
+                       qsa::Pages& pg) {
+  pg.table = block_table;
+  pg.stride = table_stride;
+  pg.shift = 0;
+  if (!block_table) return true;
+  if (table_stride < 1 || page_tokens < 256 || page_tokens > (1 << 22) ||
+      (page_tokens & (page_tokens - 1)) != 0)
+    return false;
+  int sh = 0;
+  while ((qsa::kBlock << sh) < page_tokens) ++sh;
+  pg.shift = sh;
+  return true;
+}
 
 }  // namespace qsa_host

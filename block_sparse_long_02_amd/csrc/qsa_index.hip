@@ -117,12 +117,13 @@ constexpr int kDenseChunk = 1024;
 constexpr int kDenseTiles = kDenseChunk / 64;   // tiles per wave
 constexpr int kDenseDepth = 4;
 
+template <bool kPaged>
 __global__ void __launch_bounds__(256, 4)
 score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
                    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
                    int n_q, int max_blocks, const uint16_t* __restrict__ bk, int64_t bk_stride,
                    uint32_t* __restrict__ dense, int64_t dense_stride,
-                   uint32_t* __restrict__ dsmp, int64_t dsmp_stride) {
+                   uint32_t* __restrict__ dsmp, int64_t dsmp_stride, Pages pg) {
   __shared__ float s_w[4][4];
   __shared__ int s_nc[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -162,7 +163,14 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
       af[ks] = j < n_rows ? v : u32x4{0, 0, 0, 0};
     }
   }
-  const uint16_t* bseq = bk + (int64_t)s * bk_stride;
+  const uint16_t* bseq = bk + (kPaged ? 0 : (int64_t)s * bk_stride);
+  // paged: lane l holds the physical page of the chunk's l-th page (a chunk
+  // of 1024 blocks spans at most 17 pages of >= 64 blocks); only pages that
+  // hold blocks below v1 are read from the table
+  const int p0 = kPaged ? (v0 >> pg.shift) : 0;
+  int tabv = 0;
+  if (kPaged && p0 + lane <= ((v1 - 1) >> pg.shift))
+    tabv = pg.table[(int64_t)s * pg.stride + p0 + lane];
   const int c0 = v0 + wave * 16;
 #ifndef QSA_DENSE_SKEW
 #define QSA_DENSE_SKEW 1
@@ -174,7 +182,12 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
   // B fragment of tile t: column tcol(t) + col (clamped in bounds past v1)
   auto load_tile = [&](u32x4 (&bf)[4], int t) {
     const int b = min(tcol(t) + col, v1 - 1);
-    const uint16_t* src = bseq + (int64_t)b * kIdxDim + 8 * grp;
+    int64_t pb = b;
+    if constexpr (kPaged) {
+      const int pp = __shfl(tabv, (b >> pg.shift) - p0, 64);
+      pb = ((int64_t)pp << pg.shift) + (b & ((1 << pg.shift) - 1));
+    }
+    const uint16_t* src = bseq + pb * kIdxDim + 8 * grp;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) bf[ks] = ldg16(src + 32 * ks);
   };
@@ -234,17 +247,24 @@ constexpr int kStageCols = 64;
 #endif
 constexpr int kPending = QSA_PENDING;   // pending pre-filter passes per row and workgroup
 
-template <int MT, bool kSample>
+// Largest column chunk a workgroup takes (host-side chunks are <= this).
+constexpr int kMaxChunkCols = 2048;
+
+template <int MT, bool kSample, bool kPaged>
 __global__ void __launch_bounds__(256, QSA_SCORE_WGS)
 score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
                   const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
                   int n_seq, int n_q, int tiles_per_seq, int max_blocks,
                   const uint16_t* __restrict__ bk, int64_t bk_stride, int chunk_cols,
                   const uint32_t* __restrict__ thresh, int32_t* __restrict__ cnt,
-                  u32x2* __restrict__ cand, uint16_t* __restrict__ samples, int ns_stride) {
+                  u32x2* __restrict__ cand, uint16_t* __restrict__ samples, int ns_stride,
+                  Pages pg) {
   constexpr int QT = 16 * MT;
   constexpr int stride = kSample ? kPrefillSampleStride : 1;
   constexpr int kPend = kSample ? 1 : kPending;
+  // paged: the physical pages of the chunk's blocks (pages hold >= 64 blocks)
+  constexpr int kPgSlots = kPaged ? kMaxChunkCols * stride / 64 + 1 : 1;
+  __shared__ int s_pg[kPgSlots];
   __shared__ __attribute__((aligned(16))) uint16_t s_b[2][kStageCols * kIdxDim];
   __shared__ float s_w[QT][4];
   __shared__ f32x4 s_wc[QT];
@@ -272,6 +292,13 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
   if (kSample && nc_last <= kCandCap) return;
   const int v1 = min(v0 + chunk_cols, max_cols);
   const bool collect_all = !kSample && nc_last <= kCandCap;
+  int pg0 = 0;
+  if constexpr (kPaged) {
+    pg0 = (int)(((int64_t)v0 * stride) >> pg.shift);
+    const int pn = (int)((((int64_t)(v1 - 1) * stride) >> pg.shift) - pg0 + 1);
+    for (int i = threadIdx.x; i < pn; i += 256)
+      s_pg[i] = pg.table[(int64_t)s * pg.stride + pg0 + i];
+  }
 
   if (threadIdx.x < QT) {
     const int j = threadIdx.x;
@@ -332,7 +359,7 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
     r_pc[mt] = 0;
   }
 
-  const uint16_t* bseq = bk + (int64_t)s * bk_stride;
+  const uint16_t* bseq = bk + (kPaged ? 0 : (int64_t)s * bk_stride);
   const int n_stages = (v1 - v0 + kStageCols - 1) / kStageCols;
   // The sequence's block keys as a buffer resource whose range ends after
   // virtual column v1 - 1: loads past it return zeros (such columns are
@@ -351,11 +378,40 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
     loff[i] = (c * stride * kIdxDim + q * 8) * 2;
   }
   auto load_stage = [&](u32x4 (&r)[4], int st) {
-    const int base = (v0 + st * kStageCols) * stride * kIdxDim * 2;
+    if constexpr (kPaged && !kSample) {
+      // a 64-column stage lies inside one page (pages hold >= 64 blocks and
+      // stages start at multiples of 64): the contiguous path's offsets from
+      // a per-stage buffer resource at the stage's first physical block
+      const int c0 = v0 + st * kStageCols;
+      const int pidx = __builtin_amdgcn_readfirstlane((c0 >> pg.shift) - pg0);
+      const int64_t pb = ((int64_t)s_pg[pidx] << pg.shift) + (c0 & ((1 << pg.shift) - 1));
+      const int nrec_st = (min(v1 - c0, kStageCols) - 1) * kIdxDim * 2 + kIdxDim * 2;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(bseq + pb * kIdxDim), (short)0, nrec_st, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(bk_rsrc, base + loff[i], 0, 0));
+      for (int i = 0; i < 4; ++i)
+        r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, loff[i], 0, 0));
+    } else if constexpr (kPaged) {
+      // sample pass: each column is its own block (32 apart), looked up in
+      // the LDS page slice; columns past v1 - 1 read column v1 - 1 and are zeroed
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * wave + 4 * i + (lane >> 4);
+        const int q = (lane & 15) ^ (c & 15);
+        const int vcol = v0 + st * kStageCols + c;
+        const int64_t blk = (int64_t)min(vcol, v1 - 1) * stride;
+        const int64_t pb = ((int64_t)s_pg[(int)(blk >> pg.shift) - pg0] << pg.shift) +
+                           (blk & (((int64_t)1 << pg.shift) - 1));
+        const u32x4 v = ldg16(bseq + pb * kIdxDim + q * 8);
+        r[i] = vcol < v1 ? v : u32x4{0, 0, 0, 0};
+      }
+    } else {
+      const int base = (v0 + st * kStageCols) * stride * kIdxDim * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(bk_rsrc, base + loff[i], 0, 0));
+      }
     }
   };
   auto store_stage = [&](const u32x4 (&r)[4], int st) {
@@ -734,12 +790,14 @@ __device__ __forceinline__ uint32_t recompute_key(const uint16_t* __restrict__ q
 }
 
 __device__ void exact_select_recompute(const uint16_t* __restrict__ q4, const float* __restrict__ w4,
-                                       const uint16_t* __restrict__ bseq, int n_c, int k,
+                                       const uint16_t* __restrict__ bseq, const Pages& pg,
+                                       int seq, int n_c, int k,
                                        int32_t* __restrict__ out, int budget, int* hist, int* tmp,
                                        int* res) {
   auto key_of = [&](int b, bool& in) {
     in = true;
-    return recompute_key(q4, w4, bseq + (int64_t)b * kIdxDim);
+    const int64_t pb = pg.table ? phys_block(pg, seq, b) : b;
+    return recompute_key(q4, w4, bseq + pb * kIdxDim);
   };
   const uint32_t tau = block_kth_largest(key_of, n_c, k, 31, hist, tmp, res);
   int above = 0;
@@ -893,7 +951,7 @@ final_select_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict_
                     int n_seq, int max_blocks, int budget, const uint16_t* __restrict__ bk,
                     int64_t bk_stride, const int32_t* __restrict__ cnt,
                     const u32x2* __restrict__ cand, int32_t* __restrict__ sel,
-                    int32_t* __restrict__ sel_count) {
+                    int32_t* __restrict__ sel_count, Pages pg) {
   __shared__ SelectShared sh;
   const int row = blockIdx.x;
   const RowGeom g = row_geom(cu_q, seq_len, n_seq, row, max_blocks);
@@ -907,8 +965,8 @@ final_select_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict_
   const int c = cnt[row];
   if (k > 0 && (c < k || c > kCandCap)) {
     exact_select_recompute(idx_q + (int64_t)row * 4 * kIdxDim, w + (int64_t)row * 4,
-                           bk + (int64_t)g.seq * bk_stride, g.n_c, k, out, budget, sh.hist, sh.tmp,
-                           sh.res);
+                           bk + (pg.table ? 0 : (int64_t)g.seq * bk_stride), pg, g.seq, g.n_c, k,
+                           out, budget, sh.hist, sh.tmp, sh.res);
     if (threadIdx.x == 0) sel_count[row] = k;
     return;
   }
@@ -1178,10 +1236,13 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
                      const int32_t* seq_len, int32_t n_seq, int32_t n_q, int32_t max_q_len,
                      int32_t max_blocks, const void* block_keys, int64_t bk_seq_stride,
                      int32_t budget, int32_t* sel, int32_t* sel_count, void* workspace,
-                     size_t ws_bytes, void* stream) {
+                     size_t ws_bytes, const int32_t* block_table, int64_t table_stride,
+                     int32_t page_tokens, void* stream) {
   using namespace qsa_host;
   using namespace qsa;
   if (n_q < 0 || n_seq < 0 || max_q_len < 0 || max_blocks < 0) return QSA_ERR_INVALID_ARG;
+  Pages pg;
+  if (!make_pages(block_table, table_stride, page_tokens, pg)) return QSA_ERR_INVALID_ARG;
   if (budget < 1 || budget > QSA_MAX_BUDGET) return QSA_ERR_INVALID_ARG;
   if (n_q == 0) return QSA_OK;
   if (n_seq == 0 || max_q_len == 0) return QSA_ERR_INVALID_ARG;
@@ -1201,9 +1262,13 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
     if (max_blocks > 0) {
       dim3 grid((unsigned)n_seq, (max_blocks + kDenseChunk - 1) / kDenseChunk);
       if (grid.y > 65535) return QSA_ERR_UNSUPPORTED;
-      hipLaunchKernelGGL(score_dense_kernel, grid, dim3(256), 0, st, (const uint16_t*)idx_q, w,
-                         cu_q, seq_len, n_q, max_blocks, (const uint16_t*)block_keys,
-                         bk_seq_stride, ws.dense, ws.dense_stride, ws.dsmp, ws.dsmp_stride);
+      auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const uint16_t*)idx_q, w, cu_q, seq_len,
+                           n_q, max_blocks, (const uint16_t*)block_keys, bk_seq_stride, ws.dense,
+                           ws.dense_stride, ws.dsmp, ws.dsmp_stride, pg);
+      };
+      if (pg.table) launch(score_dense_kernel<true>);
+      else launch(score_dense_kernel<false>);
     }
     hipLaunchKernelGGL(select_dense_kernel, dim3(n_q), dim3(256), 0, st, cu_q, seq_len, n_seq,
                        max_blocks, budget, (const uint32_t*)ws.dense, ws.dense_stride,
@@ -1219,13 +1284,21 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
 #define QSA_PREFILL_CHUNK 2048
 #endif
   constexpr int chunk = QSA_PREFILL_CHUNK;   // candidate blocks per workgroup
+  static_assert(chunk <= kMaxChunkCols && chunk % kStageCols == 0, "prefill chunk");
+  auto gemm = [&](auto sample_tag, dim3 grid, int chunk_cols) {
+    constexpr bool kS = decltype(sample_tag)::value;
+    auto launch = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const uint16_t*)idx_q, w, cu_q, seq_len,
+                         n_seq, n_q, (int)tiles_per_seq, max_blocks, (const uint16_t*)block_keys,
+                         bk_seq_stride, chunk_cols, ws.thresh, ws.cnt, ws.cand, ws.samples,
+                         ws.ns_stride, pg);
+    };
+    if (pg.table) launch(score_gemm_kernel<kPrefillMT, kS, true>);
+    else launch(score_gemm_kernel<kPrefillMT, kS, false>);
+  };
   // 1. sample pass (only rows with more than kCandCap candidates need it)
   if (max_blocks > kCandCap) {
-    dim3 grid((unsigned)gx, (ws.ns_stride + chunk - 1) / chunk);
-    hipLaunchKernelGGL((score_gemm_kernel<kPrefillMT, true>), grid, dim3(256), 0, st,
-                       (const uint16_t*)idx_q, w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq,
-                       max_blocks, (const uint16_t*)block_keys, bk_seq_stride, chunk, ws.thresh,
-                       ws.cnt, ws.cand, ws.samples, ws.ns_stride);
+    gemm(std::true_type{}, dim3((unsigned)gx, (ws.ns_stride + chunk - 1) / chunk), chunk);
   }
   // 2. thresholds (also preset the list counters)
   hipLaunchKernelGGL(threshold_kernel, dim3(n_q), dim3(256), 0, st, cu_q, seq_len, n_seq,
@@ -1246,16 +1319,13 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
       fchunk >>= 1;
     dim3 grid((unsigned)gx, (max_blocks + fchunk - 1) / fchunk);
     if (grid.y > 65535) return QSA_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((score_gemm_kernel<kPrefillMT, false>), grid, dim3(256), 0, st,
-                       (const uint16_t*)idx_q, w, cu_q, seq_len, n_seq, n_q, (int)tiles_per_seq,
-                       max_blocks, (const uint16_t*)block_keys, bk_seq_stride, fchunk, ws.thresh,
-                       ws.cnt, ws.cand, ws.samples, ws.ns_stride);
+    gemm(std::false_type{}, grid, fchunk);
   }
   // 4. exact select per row (rows whose list came out short or overflowed
   //    are selected exactly by recomputing their scores)
   hipLaunchKernelGGL(final_select_kernel, dim3(n_q), dim3(256), 0, st, (const uint16_t*)idx_q, w,
                      cu_q, seq_len, n_seq, max_blocks, budget, (const uint16_t*)block_keys,
-                     bk_seq_stride, ws.cnt, ws.cand, sel, sel_count);
+                     bk_seq_stride, ws.cnt, ws.cand, sel, sel_count, pg);
   return launch_status();
 }
 

@@ -84,7 +84,8 @@ pool_block_keys_normed_kernel(const uint16_t* __restrict__ idx_k, int64_t ik_str
                               uint16_t* __restrict__ bk, int64_t bk_stride,
                               const int32_t* __restrict__ blk_begin,
                               const int32_t* __restrict__ blk_end,
-                              const float* __restrict__ gamma, double eps, RopeFreq fr) {
+                              const float* __restrict__ gamma, double eps, RopeFreq fr,
+                              Pages pg) {
   const int s = blockIdx.y;
   const int64_t b0 = blk_begin[s], b1 = blk_end[s];
   const int part = threadIdx.x & 15;
@@ -92,11 +93,13 @@ pool_block_keys_normed_kernel(const uint16_t* __restrict__ idx_k, int64_t ik_str
   float g[8], gp[8];
   load_gamma(gamma, part, g, gp);
   const double f0 = freq_at(fr, 2 * part), f1 = freq_at(fr, 2 * part + 1);
-  const uint16_t* src_seq = idx_k + (int64_t)s * ik_stride;
-  uint16_t* dst_seq = bk + (int64_t)s * bk_stride;
+  const uint16_t* src_seq = idx_k + (pg.table ? 0 : (int64_t)s * ik_stride);
+  uint16_t* dst_seq = bk + (pg.table ? 0 : (int64_t)s * bk_stride);
   // every lane of a 16-lane group takes the same trips (the butterfly needs
   // all 16): the loop bound depends on the group's block only
-  for (int64_t b = b0 + (int64_t)blockIdx.x * 16 + sub; b < b1; b += (int64_t)gridDim.x * 16) {
+  for (int64_t lb = b0 + (int64_t)blockIdx.x * 16 + sub; lb < b1; lb += (int64_t)gridDim.x * 16) {
+    // the rotation uses the logical position; paged caches store at the physical block
+    const int64_t b = pg.table ? phys_block(pg, s, lb) : lb;
     const uint16_t* src = src_seq + b * (kBlock * kIdxDim) + part * 8;
     const u32x4 t0 = ldg16(src), t1 = ldg16(src + kIdxDim), t2 = ldg16(src + 2 * kIdxDim),
                 t3 = ldg16(src + 3 * kIdxDim);
@@ -114,7 +117,7 @@ pool_block_keys_normed_kernel(const uint16_t* __restrict__ idx_k, int64_t ik_str
     }
     // the block's 32 angles, two per lane (j = 2*part, 2*part + 1), then
     // gathered: pair j = 8*(part % 4) + i sits in lane j/2, slot j%2
-    const double pos = (double)(b * kBlock);
+    const double pos = (double)(lb * kBlock);
     double c2[2], s2[2];
     sincos(pos * f0, &s2[0], &c2[0]);
     sincos(pos * f1, &s2[1], &c2[1]);
@@ -188,9 +191,12 @@ int qsa_pool_block_keys_normed(const void* idx_k, int64_t ik_seq_stride, void* b
                                int64_t bk_seq_stride, const int32_t* blk_begin,
                                const int32_t* blk_end, int32_t n_seq, int32_t max_span,
                                const float* gamma, double eps, const double* inv_freq,
-                               void* stream) {
+                               const int32_t* block_table, int64_t table_stride,
+                               int32_t page_tokens, void* stream) {
   using namespace qsa_host;
   if (n_seq < 0 || max_span < 0 || !eps_ok(eps)) return QSA_ERR_INVALID_ARG;
+  qsa::Pages pg;
+  if (!make_pages(block_table, table_stride, page_tokens, pg)) return QSA_ERR_INVALID_ARG;
   qsa::RopeFreq fr;
   if (!make_rope_freq(inv_freq, fr)) return QSA_ERR_INVALID_ARG;
   if (n_seq == 0 || max_span == 0) return QSA_OK;
@@ -202,7 +208,7 @@ int qsa_pool_block_keys_normed(const void* idx_k, int64_t ik_seq_stride, void* b
   if (gx > 65536) gx = 65536;
   hipLaunchKernelGGL(qsa::pool_block_keys_normed_kernel, dim3(gx, n_seq), dim3(256), 0,
                      (hipStream_t)stream, (const uint16_t*)idx_k, ik_seq_stride,
-                     (uint16_t*)block_keys, bk_seq_stride, blk_begin, blk_end, gamma, eps, fr);
+                     (uint16_t*)block_keys, bk_seq_stride, blk_begin, blk_end, gamma, eps, fr, pg);
   return launch_status();
 }
 

@@ -16,14 +16,17 @@ namespace qsa {
 __global__ void __launch_bounds__(256)
 pool_block_keys_kernel(const uint16_t* __restrict__ idx_k, int64_t ik_stride,
                        uint16_t* __restrict__ bk, int64_t bk_stride,
-                       const int32_t* __restrict__ blk_begin, const int32_t* __restrict__ blk_end) {
+                       const int32_t* __restrict__ blk_begin, const int32_t* __restrict__ blk_end,
+                       Pages pg) {
   const int s = blockIdx.y;
   const int64_t b0 = blk_begin[s], b1 = blk_end[s];
   const int part = threadIdx.x & 15;   // which 8-dim slice
   const int sub = threadIdx.x >> 4;    // which block of the 16
-  const uint16_t* src_seq = idx_k + (int64_t)s * ik_stride;
-  uint16_t* dst_seq = bk + (int64_t)s * bk_stride;
-  for (int64_t b = b0 + (int64_t)blockIdx.x * 16 + sub; b < b1; b += (int64_t)gridDim.x * 16) {
+  // paged: the pools' bases, and physical blocks (a page holds whole blocks)
+  const uint16_t* src_seq = idx_k + (pg.table ? 0 : (int64_t)s * ik_stride);
+  uint16_t* dst_seq = bk + (pg.table ? 0 : (int64_t)s * bk_stride);
+  for (int64_t lb = b0 + (int64_t)blockIdx.x * 16 + sub; lb < b1; lb += (int64_t)gridDim.x * 16) {
+    const int64_t b = pg.table ? phys_block(pg, s, lb) : lb;
     const uint16_t* src = src_seq + b * (kBlock * kIdxDim) + part * 8;
     u32x4 t0 = ldg16(src), t1 = ldg16(src + kIdxDim), t2 = ldg16(src + 2 * kIdxDim),
           t3 = ldg16(src + 3 * kIdxDim);
@@ -87,13 +90,16 @@ const char* qsa_status_string(int status) {
   }
 }
 
-int qsa_abi_version(void) { return 3; }
+int qsa_abi_version(void) { return 4; }
 
 int qsa_pool_block_keys(const void* idx_k, int64_t ik_seq_stride, void* block_keys,
                         int64_t bk_seq_stride, const int32_t* blk_begin, const int32_t* blk_end,
-                        int32_t n_seq, int32_t max_span, void* stream) {
+                        int32_t n_seq, int32_t max_span, const int32_t* block_table,
+                        int64_t table_stride, int32_t page_tokens, void* stream) {
   using namespace qsa_host;
   if (n_seq < 0 || max_span < 0) return QSA_ERR_INVALID_ARG;
+  qsa::Pages pg;
+  if (!make_pages(block_table, table_stride, page_tokens, pg)) return QSA_ERR_INVALID_ARG;
   if (n_seq == 0 || max_span == 0) return QSA_OK;
   if (!idx_k || !block_keys || !blk_begin || !blk_end) return QSA_ERR_INVALID_ARG;
   if (!aligned16(idx_k) || !aligned16(block_keys)) return QSA_ERR_INVALID_ARG;
@@ -105,7 +111,7 @@ int qsa_pool_block_keys(const void* idx_k, int64_t ik_seq_stride, void* block_ke
   dim3 grid(gx, n_seq);
   hipLaunchKernelGGL(qsa::pool_block_keys_kernel, grid, dim3(256), 0, (hipStream_t)stream,
                      (const uint16_t*)idx_k, ik_seq_stride, (uint16_t*)block_keys, bk_seq_stride,
-                     blk_begin, blk_end);
+                     blk_begin, blk_end, pg);
   return launch_status();
 }
 

@@ -30,32 +30,34 @@ SIGNATURES = {
     "qsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qsa_abi_version": (ctypes.c_int, []),
     "qsa_pool_block_keys": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _c_void_p,
-                                           _i32, _i32, _c_void_p]),
+                                           _i32, _i32, _c_void_p, _i64, _i32, _c_void_p]),
     "qsa_rope_apply": (ctypes.c_int, [_c_void_p, _i64, _i64, _i32, _c_void_p, _i32, _i32, _c_void_p,
                                       _c_void_p]),
     "qsa_yarn_rope": (ctypes.c_int, [ctypes.c_double] * 5 + [_c_void_p, _c_void_p]),
     "qsa_pool_block_keys_normed": (ctypes.c_int, [_c_void_p, _i64, _c_void_p, _i64, _c_void_p,
                                                   _c_void_p, _i32, _i32, _c_void_p, ctypes.c_double,
-                                                  _c_void_p, _c_void_p]),
+                                                  _c_void_p, _c_void_p, _i64, _i32, _c_void_p]),
     "qsa_index_query_transform": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
                                                  _i32, _i32, _c_void_p, ctypes.c_double, _c_void_p,
                                                  _c_void_p]),
     "qsa_index_select_workspace": (_size, [_i32, _i32, _i32]),
     "qsa_index_select": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                         _i32, _c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p,
-                                        _size, _c_void_p]),
+                                        _size, _c_void_p, _i64, _i32, _c_void_p]),
     "qsa_attend_prefill": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p,
                                           _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32, _c_void_p,
-                                          _c_void_p, _c_void_p, ctypes.c_float, _c_void_p]),
+                                          _c_void_p, _c_void_p, ctypes.c_float, _c_void_p, _i64,
+                                          _i32, _c_void_p]),
     "qsa_attend_decode_workspace": (_size, [_i32]),
     "qsa_attend_decode": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i64, _i64,
                                          _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p,
-                                         _size, _c_void_p, ctypes.c_float, _c_void_p]),
+                                         _size, _c_void_p, ctypes.c_float, _c_void_p, _i64, _i32,
+                                         _c_void_p]),
     "qsa_attend_decode_multi_workspace": (_size, [_i32]),
     "qsa_attend_decode_multi": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
                                                _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32,
                                                _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p,
-                                               ctypes.c_float, _c_void_p]),
+                                               ctypes.c_float, _c_void_p, _i64, _i32, _c_void_p]),
 }
 
 _lib = None
@@ -113,6 +115,26 @@ def _host_f64(a):
     return ctypes.cast(buf, ctypes.c_void_p), buf
 
 
+def _pages(pages):
+    """(table pointer, table_stride, page_tokens) for pages = None (contiguous
+    caches) or (block_table int32 [n_seq][stride] on the GPU, page_tokens)."""
+    if pages is None:
+        return None, 0, 0
+    table, page_tokens = pages
+    _dev(table)
+    if table.dtype != torch.int32 or table.dim() != 2 or table.stride(1) != 1:
+        raise ValueError("block_table must be a row-major int32 [n_seq][stride] tensor")
+    return _p(table), table.stride(0), int(page_tokens)
+
+
+def _kv_strides(k_cache, pages):
+    """(kv_seq_stride, kv_head_stride): k_cache [n_seq][2][cap][256], or with
+    pages the pool [2][n_pages * page_tokens][256]."""
+    if pages is None:
+        return k_cache.stride(0), k_cache.stride(1)
+    return 0, k_cache.stride(0)
+
+
 def status_string(status: int) -> str:
     return lib().qsa_status_string(status).decode()
 
@@ -121,12 +143,13 @@ def abi_version() -> int:
     return lib().qsa_abi_version()
 
 
-def pool_block_keys(idx_k, block_keys, blk_begin, blk_end, max_span, stream=None):
-    """idx_k bf16 [n_seq][cap][128] -> block_keys bf16 [n_seq][cap/4][128] for blk_begin..blk_end."""
+def pool_block_keys(idx_k, block_keys, blk_begin, blk_end, max_span, pages=None, stream=None):
+    """idx_k bf16 [n_seq][cap][128] -> block_keys bf16 [n_seq][cap/4][128] for blk_begin..blk_end
+    (or the paged pools, pages = (block_table, page_tokens))."""
     _dev(idx_k, block_keys, blk_begin, blk_end)
     st = lib().qsa_pool_block_keys(_p(idx_k), idx_k.stride(0), _p(block_keys), block_keys.stride(0),
                                    _p(blk_begin), _p(blk_end), blk_begin.numel(), int(max_span),
-                                   _stream(stream))
+                                   *_pages(pages), _stream(stream))
     _check("qsa_pool_block_keys", st)
 
 
@@ -152,14 +175,14 @@ def yarn_rope(base=1.0e7, factor=4.0, orig_ctx=262144, alpha=1.0, beta=32.0):
 
 
 def pool_block_keys_normed(idx_k, block_keys, blk_begin, blk_end, max_span, gamma=None, eps=1e-6,
-                           inv_freq=None, stream=None):
+                           inv_freq=None, pages=None, stream=None):
     """Pool, RMS-normalise and rotate blocks blk_begin..blk_end (the pages' indexer keys)."""
     _dev(idx_k, block_keys, blk_begin, blk_end, gamma)
     fp, _keep = _host_f64(inv_freq)
     st = lib().qsa_pool_block_keys_normed(_p(idx_k), idx_k.stride(0), _p(block_keys),
                                           block_keys.stride(0), _p(blk_begin), _p(blk_end),
                                           blk_begin.numel(), int(max_span), _p(gamma), float(eps),
-                                          fp, _stream(stream))
+                                          fp, *_pages(pages), _stream(stream))
     _check("qsa_pool_block_keys_normed", st)
 
 
@@ -179,24 +202,26 @@ def index_select_workspace(n_q, max_q_len, max_blocks) -> int:
 
 
 def index_select(idx_q, w, cu_q, seq_len, max_q_len, max_blocks, block_keys, budget, sel,
-                 sel_count, workspace, stream=None):
+                 sel_count, workspace, pages=None, stream=None):
     _dev(idx_q, w, cu_q, seq_len, block_keys, sel, sel_count, workspace)
     st = lib().qsa_index_select(_p(idx_q), _p(w), _p(cu_q), _p(seq_len), seq_len.numel(),
                                 idx_q.shape[0], int(max_q_len), int(max_blocks), _p(block_keys),
                                 block_keys.stride(0), int(budget), _p(sel), _p(sel_count),
                                 _p(workspace), workspace.numel() * workspace.element_size(),
-                                _stream(stream))
+                                *_pages(pages), _stream(stream))
     _check("qsa_index_select", st)
 
 
 def attend_prefill(q, cu_q, seq_len, max_q_len, k_cache, v_cache, sel, sel_count, budget, out,
-                   lse=None, inv_freq=None, softmax_scale=SOFTMAX_SCALE, stream=None):
+                   lse=None, inv_freq=None, softmax_scale=SOFTMAX_SCALE, pages=None, stream=None):
     _dev(q, cu_q, seq_len, k_cache, v_cache, sel, sel_count, out, lse)
     fp, _keep = _host_f64(inv_freq)
     st = lib().qsa_attend_prefill(_p(q), _p(cu_q), _p(seq_len), seq_len.numel(), q.shape[0],
-                                  int(max_q_len), _p(k_cache), _p(v_cache), k_cache.stride(0),
-                                  k_cache.stride(1), _p(sel), _p(sel_count), int(budget), _p(out),
-                                  _p(lse), fp, float(softmax_scale), _stream(stream))
+                                  int(max_q_len), _p(k_cache), _p(v_cache),
+                                  *_kv_strides(k_cache, pages), _p(sel), _p(sel_count), int(budget),
+                                  _p(out),
+                                  _p(lse), fp, float(softmax_scale), *_pages(pages),
+                                  _stream(stream))
     _check("qsa_attend_prefill", st)
 
 
@@ -205,14 +230,14 @@ def attend_decode_workspace(n_seq) -> int:
 
 
 def attend_decode(q, seq_len, k_cache, v_cache, sel, sel_count, budget, out, lse, workspace,
-                  inv_freq=None, softmax_scale=SOFTMAX_SCALE, stream=None):
+                  inv_freq=None, softmax_scale=SOFTMAX_SCALE, pages=None, stream=None):
     _dev(q, seq_len, k_cache, v_cache, sel, sel_count, out, lse, workspace)
     fp, _keep = _host_f64(inv_freq)
     st = lib().qsa_attend_decode(_p(q), _p(seq_len), seq_len.numel(), _p(k_cache), _p(v_cache),
-                                 k_cache.stride(0), k_cache.stride(1), _p(sel), _p(sel_count),
+                                 *_kv_strides(k_cache, pages), _p(sel), _p(sel_count),
                                  int(budget), _p(out), _p(lse), _p(workspace),
                                  workspace.numel() * workspace.element_size(), fp,
-                                 float(softmax_scale), _stream(stream))
+                                 float(softmax_scale), *_pages(pages), _stream(stream))
     _check("qsa_attend_decode", st)
 
 
@@ -221,13 +246,14 @@ def attend_decode_multi_workspace(n_q) -> int:
 
 
 def attend_decode_multi(q, cu_q, seq_len, k_cache, v_cache, sel, sel_count, budget, out, lse,
-                        workspace, inv_freq=None, softmax_scale=SOFTMAX_SCALE, stream=None):
+                        workspace, inv_freq=None, softmax_scale=SOFTMAX_SCALE, pages=None,
+                        stream=None):
     _dev(q, cu_q, seq_len, k_cache, v_cache, sel, sel_count, out, lse, workspace)
     fp, _keep = _host_f64(inv_freq)
     st = lib().qsa_attend_decode_multi(_p(q), _p(cu_q), _p(seq_len), seq_len.numel(), q.shape[0],
-                                       _p(k_cache), _p(v_cache), k_cache.stride(0),
-                                       k_cache.stride(1), _p(sel), _p(sel_count), int(budget),
+                                       _p(k_cache), _p(v_cache), *_kv_strides(k_cache, pages),
+                                       _p(sel), _p(sel_count), int(budget),
                                        _p(out), _p(lse), _p(workspace),
                                        workspace.numel() * workspace.element_size(), fp,
-                                       float(softmax_scale), _stream(stream))
+                                       float(softmax_scale), *_pages(pages), _stream(stream))
     _check("qsa_attend_decode_multi", st)

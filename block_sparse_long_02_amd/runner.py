@@ -15,13 +15,18 @@ from .workloads import QSABatch, R, v_cache_layout
 
 class QSARunner:
     def __init__(self, batch: QSABatch, decode: bool | None = None, transforms: bool = False,
-                 gamma_k=None, gamma_q=None, eps: float = 1e-6, yarn: bool = False):
+                 gamma_k=None, gamma_q=None, eps: float = 1e-6, yarn: bool = False,
+                 paged: int | None = None, page_seed: int = 0, shared_pages=None):
         """transforms=True applies the pages' indexer transforms: block keys are
         pooled, RMS-normalised and rotated; each step first normalises and
         rotates the indexer queries into a buffer of its own.  yarn=True
         extends the native 262,144-token window with YaRN (factor 4): every
         rotation (K cache, queries, indexer transforms) takes the YaRN
-        frequencies and the core attention its softmax scale."""
+        frequencies and the core attention its softmax scale.  paged=P keeps
+        every cache in pools of P-token pages, in a seeded random physical
+        order; shared_pages = {dst: (src, n)} maps the first n pages of
+        sequence dst onto those of src (the caller makes their tokens equal),
+        as a prefix cache would."""
         b = batch
         assert b.idx_q.is_cuda, "batch must live on the GPU"
         self.b = b
@@ -46,7 +51,11 @@ class QSARunner:
             qsa.rope_apply(self.k_cache[s], row_stride=256, head_stride=cap * 256, n_heads=2,
                            n_rows=lens[s], pos0=0, inv_freq=self.inv_freq)
         self.v_cache = v_cache_layout(b.v)
+        self.idx_k = b.idx_k
         self.block_keys = torch.zeros((self.n_seq, cap // R, 128), dtype=torch.bfloat16, device=dev)
+        self.pages = None
+        if paged:
+            self._to_pages(int(paged), page_seed, shared_pages or {})
 
         # blocks already in the cache before this step, and the ones the step completes
         before = [(lens[s] - (cu[s + 1] - cu[s])) // R for s in range(self.n_seq)]
@@ -69,13 +78,38 @@ class QSARunner:
                qsa.attend_decode_multi_workspace(self.n_q) if self.mtp else 16)
         self.ws_decode = torch.empty((max(wsd, 16),), dtype=torch.uint8, device=dev)
 
+    def _to_pages(self, P, seed, shared):
+        """Move the caches into page pools (the layouts of the paged ABI)."""
+        dev, cap = self.idx_k.device, self.b.l_cap
+        npg = -(-cap // P)
+        g = torch.Generator().manual_seed(seed)
+        table = torch.randperm(self.n_seq * npg, generator=g).to(torch.int32).view(self.n_seq, npg)
+        for dst, (src, n) in shared.items():
+            table[dst, :n] = table[src, :n]
+        self.block_table = table.contiguous().to(dev)
+        self.pages = (self.block_table, P)
+        n_tok = self.n_seq * npg * P
+        t = torch.arange(cap, device=dev)
+        tok = (self.block_table[:, t // P].long() * P + t % P).reshape(-1)
+        tb = torch.arange(cap // R, device=dev)
+        blk = (self.block_table[:, (R * tb) // P].long() * (P // R) + tb % (P // R)).reshape(-1)
+        idx_k = torch.zeros((n_tok, 128), dtype=torch.bfloat16, device=dev)
+        idx_k[tok] = self.idx_k.reshape(-1, 128)
+        k = torch.zeros((2, n_tok, 256), dtype=torch.bfloat16, device=dev)
+        k[:, tok] = self.k_cache.permute(1, 0, 2, 3).reshape(2, -1, 256)
+        v = torch.zeros((2, n_tok // R, 256, R), dtype=torch.bfloat16, device=dev)
+        v[:, blk] = self.v_cache.permute(1, 0, 2, 3, 4).reshape(2, -1, 256, R)
+        self.idx_k, self.k_cache, self.v_cache = idx_k, k, v
+        self.block_keys = torch.zeros((n_tok // R, 128), dtype=torch.bfloat16, device=dev)
+
     def _pool(self, begin, end, span, stream=None):
         if self.transforms:
-            qsa.pool_block_keys_normed(self.b.idx_k, self.block_keys, begin, end, span,
+            qsa.pool_block_keys_normed(self.idx_k, self.block_keys, begin, end, span,
                                        gamma=self.gamma_k, eps=self.eps, inv_freq=self.inv_freq,
-                                       stream=stream)
+                                       pages=self.pages, stream=stream)
         else:
-            qsa.pool_block_keys(self.b.idx_k, self.block_keys, begin, end, span, stream=stream)
+            qsa.pool_block_keys(self.idx_k, self.block_keys, begin, end, span, pages=self.pages,
+                                stream=stream)
 
     # the three calls of a step ------------------------------------------
     def pool(self, stream=None):
@@ -92,11 +126,12 @@ class QSARunner:
             idx_q = self.idx_q_t
         qsa.index_select(idx_q, b.w, b.cu_q, b.seq_len, self.max_q_len, self.max_blocks,
                          self.block_keys, self.budget, self.sel, self.sel_count, self.ws_index,
-                         stream=stream)
+                         pages=self.pages, stream=stream)
 
     def attend(self, stream=None):
         b = self.b
-        rope = dict(inv_freq=self.inv_freq, softmax_scale=self.softmax_scale, stream=stream)
+        rope = dict(inv_freq=self.inv_freq, softmax_scale=self.softmax_scale, pages=self.pages,
+                    stream=stream)
         if self.decode:
             qsa.attend_decode(b.q, b.seq_len, self.k_cache, self.v_cache, self.sel, self.sel_count,
                               self.budget, self.out, self.lse, self.ws_decode, **rope)

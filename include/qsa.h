@@ -49,6 +49,21 @@
  *    `cap` is a multiple of 4 and covers every token of the sequence, so the
  *    unfinished tail block is always in bounds; cache rows at positions
  *    >= seq_len[s] inside that block may hold anything and are never used.
+ *  - Paged caches (f3: prefix-cache reuse, [ailearn] performance box): every
+ *    call that reads or writes a cache takes (block_table, table_stride,
+ *    page_tokens).  block_table == NULL selects the contiguous layouts above.
+ *    Otherwise the caches are pools of pages of page_tokens tokens (a power of
+ *    two, 256 <= page_tokens <= 2^22); logical page p = t / page_tokens of
+ *    sequence s is physical page P = block_table[s*table_stride + p] (device
+ *    int32; table_stride >= 1), and the sequence strides are ignored:
+ *      idx_k       bf16 [n_pages*page_tokens][128]      token row P*page_tokens + t%page_tokens
+ *      block_keys  bf16 [n_pages*page_tokens/4][128]    block row P*page_tokens/4 + b%(page_tokens/4)
+ *      k_cache     bf16 [2][n_pages*page_tokens][256]   kv_head_stride apart per KV head
+ *      v_cache     bf16 [2][n_pages*page_tokens/4][256][4]   (same head stride, same block order)
+ *    A sequence's table row must name a valid page for every page that holds
+ *    one of its positions < seq_len[s]; sequences may share pages (a common
+ *    prefix).  A page holds whole micro-blocks, so a chunk may start at any
+ *    position: the block it completes is pooled from its page.
  */
 #ifndef QSA_H_
 #define QSA_H_
@@ -105,7 +120,9 @@ int qsa_abi_version(void);
 int qsa_pool_block_keys(const void* idx_k, int64_t ik_seq_stride,
                         void* block_keys, int64_t bk_seq_stride,
                         const int32_t* blk_begin, const int32_t* blk_end,
-                        int32_t n_seq, int32_t max_span, void* stream);
+                        int32_t n_seq, int32_t max_span,
+                        const int32_t* block_table, int64_t table_stride, int32_t page_tokens,
+                        void* stream);
 
 /*
  * a5 helper -- partial RoPE of cache keys at write time.  [card] and
@@ -184,7 +201,8 @@ int qsa_pool_block_keys_normed(const void* idx_k, int64_t ik_seq_stride,
                                const int32_t* blk_begin, const int32_t* blk_end,
                                int32_t n_seq, int32_t max_span,
                                const float* gamma, double eps, const double* inv_freq,
-                               void* stream);
+                               const int32_t* block_table, int64_t table_stride,
+                               int32_t page_tokens, void* stream);
 
 /* Query side: q_raw and q_out are bf16 [n_q][4][128] (q_out may equal q_raw;
  * other overlaps are not allowed).  Row cu_q[s] + j of sequence s is
@@ -228,7 +246,9 @@ int qsa_index_select(const void* idx_q, const float* w,
                      int32_t n_seq, int32_t n_q, int32_t max_q_len, int32_t max_blocks,
                      const void* block_keys, int64_t bk_seq_stride,
                      int32_t budget, int32_t* sel, int32_t* sel_count,
-                     void* workspace, size_t ws_bytes, void* stream);
+                     void* workspace, size_t ws_bytes,
+                     const int32_t* block_table, int64_t table_stride, int32_t page_tokens,
+                     void* stream);
 
 /*
  * a4 + a5 + a6 -- sparse prefill attention.  [ailearn] §03 CAUSAL SPARSE SET
@@ -253,6 +273,7 @@ int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_le
                        int64_t kv_seq_stride, int64_t kv_head_stride,
                        const int32_t* sel, const int32_t* sel_count, int32_t budget,
                        void* out, float* lse, const double* inv_freq, float softmax_scale,
+                       const int32_t* block_table, int64_t table_stride, int32_t page_tokens,
                        void* stream);
 
 /*
@@ -268,7 +289,9 @@ int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq,
                       int64_t kv_seq_stride, int64_t kv_head_stride,
                       const int32_t* sel, const int32_t* sel_count, int32_t budget,
                       void* out, float* lse, void* workspace, size_t ws_bytes,
-                      const double* inv_freq, float softmax_scale, void* stream);
+                      const double* inv_freq, float softmax_scale,
+                      const int32_t* block_table, int64_t table_stride, int32_t page_tokens,
+                      void* stream);
 
 /*
  * f1 (multi-token decode) -- the split-K decode of qsa_attend_decode for a
@@ -286,7 +309,9 @@ int qsa_attend_decode_multi(const void* q, const int32_t* cu_q, const int32_t* s
                             int64_t kv_seq_stride, int64_t kv_head_stride,
                             const int32_t* sel, const int32_t* sel_count, int32_t budget,
                             void* out, float* lse, void* workspace, size_t ws_bytes,
-                            const double* inv_freq, float softmax_scale, void* stream);
+                            const double* inv_freq, float softmax_scale,
+                            const int32_t* block_table, int64_t table_stride,
+                            int32_t page_tokens, void* stream);
 
 #ifdef __cplusplus
 }

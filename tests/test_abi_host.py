@@ -41,7 +41,7 @@ def test_status_strings_and_version(L):
     for code, name in qsa.STATUS.items():
         assert qsa.status_string(code) == name
     assert qsa.status_string(99) == "QSA_ERR_UNKNOWN"
-    assert qsa.abi_version() == 3
+    assert qsa.abi_version() == 4
 
 
 def test_workspace_queries(L):
@@ -71,7 +71,8 @@ def _select(L, **kw):
     a.update(kw)
     return L.qsa_index_select(a["idx_q"], a["w"], a["cu_q"], a["seq_len"], a["n_seq"], a["n_q"],
                               a["max_q_len"], a["max_blocks"], a["bk"], a["bk_stride"],
-                              a["budget"], a["sel"], a["cnt"], a["ws"], a["ws_bytes"], a["stream"])
+                              a["budget"], a["sel"], a["cnt"], a["ws"], a["ws_bytes"],
+                              a.get("table"), a.get("tstride", 0), a.get("ptok", 0), a["stream"])
 
 
 def test_index_select_rejects_bad_arguments(L):
@@ -90,24 +91,24 @@ def test_index_select_rejects_bad_arguments(L):
 def test_attention_and_pool_reject_bad_arguments(L):
     A = ALIGNED
     # prefill: budget, alignment, null
-    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 0, A, None, None, 0.0625, None) == 1
-    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, MISALIGNED, 1024, 512, A, A, 16, A, None, None, 0.0625, None) == 1
-    assert L.qsa_attend_prefill(A, None, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, None, 0.0625, None) == 1
-    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1020, 512, A, A, 16, A, None, None, 0.0625, None) == 1
-    assert L.qsa_attend_prefill(A, A, A, 1, 0, 4, A, A, 1024, 512, A, A, 16, A, None, None, 0.0625, None) == 0
+    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 0, A, None, None, 0.0625, None, 0, 0, None) == 1
+    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, MISALIGNED, 1024, 512, A, A, 16, A, None, None, 0.0625, None, 0, 0, None) == 1
+    assert L.qsa_attend_prefill(A, None, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, None, 0.0625, None, 0, 0, None) == 1
+    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1020, 512, A, A, 16, A, None, None, 0.0625, None, 0, 0, None) == 1
+    assert L.qsa_attend_prefill(A, A, A, 1, 0, 4, A, A, 1024, 512, A, A, 16, A, None, None, 0.0625, None, 0, 0, None) == 0
     # decode: workspace too small, bad budget
-    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 100, None, 0.0625, None) == 3
-    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 600, A, A, A, 1 << 30, None, 0.0625, None) == 1
-    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, MISALIGNED, 1 << 30, None, 0.0625, None) == 1
+    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 100, None, 0.0625, None, 0, 0, None) == 3
+    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 600, A, A, A, 1 << 30, None, 0.0625, None, 0, 0, None) == 1
+    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, MISALIGNED, 1 << 30, None, 0.0625, None, 0, 0, None) == 1
     # multi-token decode: cu_q required, workspace sized by n_q
-    assert L.qsa_attend_decode_multi(A, None, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, None, 0.0625, None) == 1
-    assert L.qsa_attend_decode_multi(A, A, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 100, None, 0.0625, None) == 3
-    assert L.qsa_attend_decode_multi(A, A, A, 2, 0, A, A, 1024, 512, A, A, 16, A, A, A, 0, None, 0.0625, None) == 0
+    assert L.qsa_attend_decode_multi(A, None, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, None, 0.0625, None, 0, 0, None) == 1
+    assert L.qsa_attend_decode_multi(A, A, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 100, None, 0.0625, None, 0, 0, None) == 3
+    assert L.qsa_attend_decode_multi(A, A, A, 2, 0, A, A, 1024, 512, A, A, 16, A, A, A, 0, None, 0.0625, None, 0, 0, None) == 0
     # pooling and rope
-    assert L.qsa_pool_block_keys(None, 128, A, 128, A, A, 1, 4, None) == 1
-    assert L.qsa_pool_block_keys(A, 129, A, 128, A, A, 1, 4, None) == 1
-    assert L.qsa_pool_block_keys(A, 128, A, 128, A, A, 0, 4, None) == 0
-    assert L.qsa_pool_block_keys(A, 128, A, 128, A, A, -1, 4, None) == 1
+    assert L.qsa_pool_block_keys(None, 128, A, 128, A, A, 1, 4, None, 0, 0, None) == 1
+    assert L.qsa_pool_block_keys(A, 129, A, 128, A, A, 1, 4, None, 0, 0, None) == 1
+    assert L.qsa_pool_block_keys(A, 128, A, 128, A, A, 0, 4, None, 0, 0, None) == 0
+    assert L.qsa_pool_block_keys(A, 128, A, 128, A, A, -1, 4, None, 0, 0, None) == 1
     assert L.qsa_rope_apply(MISALIGNED, 256, 256, 2, None, 0, 10, None, None) == 1
     assert L.qsa_rope_apply(A, 256, 256, 2, None, 0, 0, None, None) == 0
     assert L.qsa_rope_apply(A, 256, 256, 2, None, (1 << 22), 10, None, None) == 2
@@ -119,7 +120,7 @@ def test_indexer_transforms_reject_bad_arguments(L):
     pool = lambda **kw: L.qsa_pool_block_keys_normed(
         kw.get("ik", ALIGNED), 128 * 64, kw.get("bk", ALIGNED), 128 * 16, ALIGNED, ALIGNED,
         kw.get("n_seq", 1), kw.get("span", 16), None, kw.get("eps", 1e-6),
-        kw.get("freq", None), None)
+        kw.get("freq", None), None, 0, 0, None)
     query = lambda **kw: L.qsa_index_query_transform(
         kw.get("q", ALIGNED), kw.get("o", ALIGNED), ALIGNED, ALIGNED, kw.get("n_seq", 1),
         kw.get("n_q", 4), kw.get("mq", 4), None, kw.get("eps", 1e-6), kw.get("freq", None), None)
@@ -142,11 +143,11 @@ def test_rope_tables_and_softmax_scale_are_validated(L):
     bad = (ctypes.c_double * 32)(*([1.0] * 31 + [float("nan")]))
     badp = ctypes.cast(bad, ctypes.c_void_p)
     for sc in (0.0, -0.0625, float("nan"), float("inf")):
-        assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, None, sc, None) == 1
-        assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, None, sc, None) == 1
-        assert L.qsa_attend_decode_multi(A, A, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, None, sc, None) == 1
-    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, badp, 0.0625, None) == 1
-    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, badp, 0.0625, None) == 1
+        assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, None, sc, None, 0, 0, None) == 1
+        assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, None, sc, None, 0, 0, None) == 1
+        assert L.qsa_attend_decode_multi(A, A, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, None, sc, None, 0, 0, None) == 1
+    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, badp, 0.0625, None, 0, 0, None) == 1
+    assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, badp, 0.0625, None, 0, 0, None) == 1
     assert L.qsa_rope_apply(A, 256, 256, 2, None, 0, 10, badp, None) == 1
 
 
@@ -174,3 +175,25 @@ def test_yarn_helper_matches_the_oracle(L):
         assert L.qsa_yarn_rope(*args, bp, None) == 1, args
     assert L.qsa_yarn_rope(1e7, 4.0, 262144.0, 1.0, 32.0, None, None) == 1
     assert L.qsa_yarn_rope(1e7, 4.0, 262144.0, 1.0, 32.0, bp, None) == 0
+
+
+def test_page_arguments_are_validated(L):
+    A = ALIGNED
+    # (table_stride, page_tokens): page_tokens must be a power of two in [256, 2^22]
+    bad = [(1, 0), (1, 128), (1, 384), (1, 1 << 23), (0, 256), (-4, 256)]
+    for ts, pt in bad:
+        assert _select(L, table=A, tstride=ts, ptok=pt) == 1, (ts, pt)
+        assert L.qsa_pool_block_keys(A, 128, A, 128, A, A, 1, 4, A, ts, pt, None) == 1
+        assert L.qsa_pool_block_keys_normed(A, 128, A, 128, A, A, 1, 4, None, 1e-6, None, A, ts, pt,
+                                            None) == 1
+        assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 0, 512, A, A, 16, A, None, None, 0.0625,
+                                    A, ts, pt, None) == 1
+        assert L.qsa_attend_decode(A, A, 4, A, A, 0, 512, A, A, 16, A, A, A, 1 << 30, None, 0.0625,
+                                   A, ts, pt, None) == 1
+        assert L.qsa_attend_decode_multi(A, A, A, 2, 8, A, A, 0, 512, A, A, 16, A, A, A, 1 << 30,
+                                         None, 0.0625, A, ts, pt, None) == 1
+    # a NULL table ignores the page arguments; valid pages with nothing to do enqueue nothing
+    assert L.qsa_pool_block_keys(A, 128, A, 128, A, A, 0, 4, None, -1, 3, None) == 0
+    assert L.qsa_pool_block_keys(A, 128, A, 128, A, A, 0, 4, A, 16, 256, None) == 0
+    assert L.qsa_attend_prefill(A, A, A, 1, 0, 4, A, A, 0, 512, A, A, 16, A, None, None, 0.0625,
+                                A, 4, 1 << 22, None) == 0

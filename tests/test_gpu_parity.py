@@ -489,6 +489,76 @@ def test_end_to_end_yarn_with_indexer_transforms():
     print("yarn + transforms tiny prefill:", kinds, f"worst rel-L2 {worst:.2e}")
 
 
+# ------------------------------------------------------------ paged caches
+
+def _same_results(a, b):
+    """Two runners of one batch gave the same selections and outputs, bit for bit."""
+    assert torch.equal(a.sel_count, b.sel_count) and torch.equal(a.sel, b.sel)
+    assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+    assert torch.equal(a.lse.view(torch.int32), b.lse.view(torch.int32))
+
+
+def _check_rows(r, view, rows):
+    sel, cnt = r.sel.cpu().numpy(), r.sel_count.cpu().numpy()
+    kinds, worst = {"exact": 0, "near": 0}, 0.0
+    for row in rows:
+        kinds[check_selection(view, row, sel[row], int(cnt[row]))] += 1
+        ref_o, ref_l = view.attend(row, sel[row][:cnt[row]])
+        worst = max(worst, check_attention(r.out[row], r.lse[row], ref_o, ref_l, f"row {row}")[1])
+    return kinds, worst
+
+
+def test_paged_prefill_unaligned_chunk_start():
+    # a chunk that starts inside a micro-block (prefix 40001 = 4*10000 + 1) and
+    # more than 4096 candidates per row (sampled path); pages of 256 and 1024
+    # tokens in a random physical order against the contiguous caches
+    b = W.make_prefill(prefix=40001, chunk=333, budget=512, seg=64, n_plant=32, seed=70).to("cuda")
+    r0 = QSARunner(b)
+    r0.step()
+    for P in (256, 1024):
+        print(f"paged prefill, {P}-token pages", flush=True)
+        r1 = QSARunner(b, paged=P, page_seed=P)
+        r1.step()
+        _sync()
+        _same_results(r0, r1)
+    view = OracleView(b)
+    kinds, worst = _check_rows(r1, view, list(range(0, 333, 11)) + [332])
+    print("paged prefill:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_paged_decode_shared_prefix():
+    # sequence 1 starts with sequence 0's first 16,384 tokens and maps them to
+    # the same 64 physical pages (a prefix-cache hit); ragged lengths
+    b = W.make_decode(seq_lens=[70001, 70005, 20003, 3], budget=512, n_plant=32, seed=71)
+    n = 16384
+    for t in (b.idx_k, b.k, b.v):
+        t[1, ..., :n, :] = t[0, ..., :n, :]
+    b = b.to("cuda")
+    r0 = QSARunner(b)
+    r0.step()
+    r1 = QSARunner(b, paged=256, page_seed=3, shared_pages={1: (0, n // 256)})
+    assert torch.equal(r1.block_table[1, :64], r1.block_table[0, :64])
+    r1.step()
+    _sync()
+    _same_results(r0, r1)
+    kinds, worst = _check_rows(r1, OracleView(b), range(4))
+    print("paged decode, shared prefix:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_paged_mtp_with_transforms_and_yarn():
+    # multi-token decode over paged caches with the indexer transforms and YaRN
+    b = W.make_mtp_decode(seq_lens=[4 * 20000 + 2, 300005], q_len=4, budget=512, n_plant=32,
+                          seed=72).to("cuda")
+    r0 = QSARunner(b, transforms=True, yarn=True)
+    r0.step()
+    r1 = QSARunner(b, transforms=True, yarn=True, paged=512, page_seed=5)
+    r1.step()
+    _sync()
+    _same_results(r0, r1)
+    kinds, worst = _check_rows(r1, OracleView(b, transforms=True, yarn=True), range(b.n_q))
+    print("paged mtp + transforms + yarn:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
 # ------------------------------------------------------- multi-token decode
 
 def test_mtp_decode_selection_exact_grid():

@@ -32,15 +32,18 @@ COPY_BYTES = 1 << 30
 # runs three times: the prefill runner pools its cached prefix, the prefill
 # step pools the chunk's new blocks, the decode runner pools its prefix (a
 # decode step of 131,073 tokens completes no new block).  The transformed
-# pooling runs twice (prefix, then the step's new blocks).
+# pooling runs twice (prefix, then the step's new blocks).  The prefill
+# kernels run twice, in the plain step (dispatch 0) and in the step with the
+# indexer transforms (dispatch 1), which selects other blocks.
 KERNELS = {
     "pool_block_keys_prefill_1m": ("pool_block_keys_kernel", "qsa_pool.hip", 1),
-    "score_sample_prefill_1m": ("score_gemm_kernel<2, true>", "qsa_index.hip", None),
-    "threshold_prefill_1m": ("threshold_kernel", "qsa_index.hip", None),
-    "score_filter_prefill_1m": ("score_gemm_kernel<2, false>", "qsa_index.hip", None),
-    "final_select_prefill_1m": ("final_select_kernel", "qsa_index.hip", None),
-    "attend_prefill_1m": ("attend_kernel<true>", "qsa_attend.hip", None),
-    "score_dense_decode_128k": ("score_dense_kernel", "qsa_index.hip", None),
+    "score_sample_prefill_1m": ("score_gemm_kernel<2, true, false>", "qsa_index.hip", 0),
+    "threshold_prefill_1m": ("threshold_kernel", "qsa_index.hip", 0),
+    "score_filter_prefill_1m": ("score_gemm_kernel<2, false, false>", "qsa_index.hip", 0),
+    "final_select_prefill_1m": ("final_select_kernel", "qsa_index.hip", 0),
+    "attend_prefill_1m": ("attend_kernel<true>", "qsa_attend.hip", 0),
+    "attend_prefill_1m_transformed": ("attend_kernel<true>", "qsa_attend.hip", 1),
+    "score_dense_decode_128k": ("score_dense_kernel<false>", "qsa_index.hip", None),
     "select_dense_decode_128k": ("select_dense_kernel", "qsa_index.hip", None),
     "key_transform_prefill_1m": ("pool_block_keys_normed_kernel", "qsa_index_transform.hip", 1),
     "query_transform_prefill_1m": ("index_query_transform_kernel", "qsa_index_transform.hip", None),

@@ -614,3 +614,50 @@ def test_graph_replays_match_eager():
             got = (r.sel, r.sel_count, r.out, r.lse)
             for a, e in zip(got, want):
                 assert torch.equal(a, e), f"replay {rep} differs"
+
+
+# ------------------------------------------------ full sizes, sampled rows
+
+def _sampled(n, k, seed, always=()):
+    rng = np.random.default_rng(seed)
+    return sorted(set(rng.choice(n, k, replace=False).tolist()) | set(always))
+
+
+def test_full_size_chunked_prefill_1m_sampled_rows():
+    # the benchmark's prefill workload and launch configuration: a 32,768-row
+    # chunk on a 1,015,808-token prefix; the oracle checks sampled rows
+    b = W.chunked_prefill_1m(device="cuda")
+    rows = _sampled(b.n_q, 10, 80, always=(0, 1, 4095, b.n_q - 1))
+    r = QSARunner(b)
+    r.step()
+    _sync()
+    kinds, worst = _check_rows(r, OracleView(b), rows)
+    print("1M prefill, plain:", kinds, f"worst rel-L2 {worst:.2e}", flush=True)
+    del r
+    torch.cuda.empty_cache()
+    # the pages' configuration: indexer transforms and YaRN, over paged caches
+    r = QSARunner(b, transforms=True, yarn=True, paged=256, page_seed=9)
+    r.step()
+    _sync()
+    kinds, worst = _check_rows(r, OracleView(b, transforms=True, yarn=True), rows[:8])
+    print("1M prefill, transforms + YaRN, paged:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_full_size_decode_128k_sampled_rows():
+    # 32 sequences x (131,072 + 1) tokens, as benchmarked (also replayed from
+    # a graph there; the graph test covers replays)
+    b = W.decode_128k(device="cuda")
+    r = QSARunner(b)
+    r.step()
+    _sync()
+    kinds, worst = _check_rows(r, OracleView(b), _sampled(b.n_q, 6, 81, always=(0, 31)))
+    print("decode 32 x 128K:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_full_size_mtp_decode_128k_sampled_rows():
+    b = W.mtp_decode_128k(device="cuda")
+    r = QSARunner(b)
+    r.step()
+    _sync()
+    kinds, worst = _check_rows(r, OracleView(b), _sampled(b.n_q, 8, 82, always=(0, 3, b.n_q - 1)))
+    print("mtp decode 32 x 4 at 128K:", kinds, f"worst rel-L2 {worst:.2e}")

@@ -721,21 +721,28 @@ __device__ void bitonic_sort_512(int* a) {
 
 // ------------------------------------------------------------ threshold
 // Per row: rows with <= kCandCap candidates keep them all (count preset to
-// n_c, tau = 0); other rows get tau = the r-th largest sampled score, found
-// by an LDS radix select (samples staged in LDS when they fit).
-constexpr int kLdsSamples = 16384;
-
+// n_c, tau = 0); other rows get tau = the r-th largest sampled score.
 // Samples are the top 16 bits of the sampled score keys; tau is the lower edge
-// of the r-th largest one, so at least r*16 candidates are expected above it.
+// of the r-th largest one, so at least r*32 candidates are expected above it.
+//
+// Up to 8192 samples (rows to about 1M tokens): each thread holds 32 samples
+// as packed 16-bit pairs and tau16 = max{v : #(samples >= v) >= r} is found by
+// a binary search on v; each step counts two samples per 32-bit word (a
+// borrow test and a population count) and does one block reduction.  Scores cluster in a few exponents, so radix
+// histograms would serialise on a few bins; counting has no contention.
+// Longer rows use the LDS radix select over the samples in global memory.
+constexpr int kBsearchSamples = 32 * 256;
+
 __global__ void __launch_bounds__(256)
 threshold_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len, int n_seq,
                  int max_blocks, int budget, const uint16_t* __restrict__ samples, int ns_stride,
                  uint32_t* __restrict__ thresh, int32_t* __restrict__ cnt) {
-  __shared__ uint16_t s_smp[kLdsSamples];
   __shared__ int hist[kBins];
   __shared__ int tmp[8];
   __shared__ int res[2];
+  __shared__ int red[2][4];
   const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const RowGeom g = row_geom(cu_q, seq_len, n_seq, row, max_blocks);
   if (!g.ok) {
     if (threadIdx.x == 0) { thresh[row] = 0xFFFFFFFFu; cnt[row] = 0; }
@@ -751,13 +758,52 @@ threshold_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ s
   const int r = min(ns, (k + kSampleExtra + kPrefillSampleStride - 1) / kPrefillSampleStride);
   const uint16_t* sp = samples + (int64_t)row * ns_stride;
   uint32_t t16;
-  if (ns <= kLdsSamples) {
-    for (int i = threadIdx.x; i < ns; i += 256) s_smp[i] = sp[i];
+  if (ns <= kBsearchSamples) {
+    // samples 32t .. 32t+31 as 16 words of two; rows are 16-byte aligned and
+    // padded to a multiple of 8, so a run that starts below ns is readable
+    // whole.  Samples are scores >= 0, so bit 15 of each half is clear:
+    // with xs = w | 0x80008000, bit 15 of each half of xs - mid*0x10001 is
+    // set exactly when that sample is >= mid (no borrow crosses halves, as
+    // 1 <= mid <= 0x8000).  Samples past ns become 0 (never >= mid).
+    uint32_t xs[16];
+    int mx = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i0 = 32 * threadIdx.x + 8 * v;
+      u32x4 q = {0u, 0u, 0u, 0u};
+      if (i0 < ns) q = ldg16(sp + i0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + 2 * e;
+        const uint32_t lo16 = i < ns ? (q[e] & 0xFFFFu) : 0u;
+        const uint32_t hi16 = i + 1 < ns ? (q[e] >> 16) : 0u;
+        mx = max(mx, (int)max(lo16, hi16));
+        xs[4 * v + e] = (lo16 | (hi16 << 16)) | 0x80008000u;
+      }
+    }
+    auto block_sum = [&](int c, int it) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+      if (lane == 0) red[it & 1][wave] = c;
+      __syncthreads();   // double-buffered: the next step writes the other half
+      return red[it & 1][0] + red[it & 1][1] + red[it & 1][2] + red[it & 1][3];
+    };
+    // hi = one past the largest sample (block maximum)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) red[1][wave] = mx;
     __syncthreads();
-    // 16-bit keys: two radix passes (11 + 5 bits) beat the range-adaptive
-    // search here, whose extra min/max pass buys nothing on 16-bit samples
-    t16 = block_kth_largest([&](int i, bool& in) { in = true; return (uint32_t)s_smp[i]; }, ns, r,
-                            16, hist, tmp, res);
+    int lo = 0, hi = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3])) + 1;
+    for (int it = 0; hi - lo > 1; ++it) {
+      const int mid = (lo + hi) >> 1;
+      const uint32_t mm = (uint32_t)mid * 0x10001u;
+      int c = 0;
+#pragma unroll
+      for (int p = 0; p < 16; ++p) c += __popc((xs[p] - mm) & 0x80008000u);
+      if (block_sum(c, it) >= r) lo = mid;
+      else hi = mid;
+    }
+    t16 = (uint32_t)lo;
   } else {
     t16 = block_kth_largest([&](int i, bool& in) { in = true; return (uint32_t)sp[i]; }, ns, r, 16,
                             hist, tmp, res);
@@ -1204,7 +1250,8 @@ inline IndexWs index_ws_layout(void* base, int n_q, int max_q_len, int max_block
   IndexWs ws = {};
   char* p = (char*)base;
   size_t off = 0;
-  ws.ns_stride = (max_blocks + kPrefillSampleStride - 1) / kPrefillSampleStride;
+  // sample rows padded to a multiple of 8 (16 bytes)
+  ws.ns_stride = ((max_blocks + kPrefillSampleStride - 1) / kPrefillSampleStride + 7) & ~7;
   ws.dense_stride = ((int64_t)max_blocks + 63) / 64 * 64;
   ws.dsmp_stride = ((int64_t)((max_blocks + kSampleStride - 1) / kSampleStride) + 63) / 64 * 64;
   if (use_dense(max_q_len)) {

@@ -123,6 +123,7 @@ def time_prefill(args, transforms=False, batch=None, yarn=False, paged=None):
     total_ms = start.elapsed_time(stop)
     stage = {n: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps
              for i, n in enumerate(["pool", "select", "attend"])}
+    per_step = sorted(ev[k][0].elapsed_time(ev[k][3]) for k in range(args.steps))
     sum_s, sum_nc = set_sizes(r)
     n_q = r.n_q
     attend_bytes = sum_s * TOKEN_GATHER_BYTES + n_q * (2 * Q_ROW_BYTES + 24 * 4 + r.budget * 4)
@@ -133,6 +134,7 @@ def time_prefill(args, transforms=False, batch=None, yarn=False, paged=None):
     index_flops = sum_nc * 1024
     res = dict(
         n_q=n_q, ms_per_step=total_ms / args.steps, stages_ms=stage,
+        step_ms_median=per_step[len(per_step) // 2], step_ms_min=per_step[0],
         value=n_q / (total_ms / args.steps * 1e-3),
         sum_set=sum_s, sum_candidates=sum_nc,
         attend=dict(bytes=attend_bytes, gbs=attend_gbs, flops=attend_flops),
@@ -217,7 +219,7 @@ def time_decode(args, mtp=False, paged=None):
     g_att = r.capture(("attend",))
     torch.cuda.synchronize()
 
-    def timed(graphs):
+    def timed(graphs, stats=False):
         evs = []
         for _ in range(args.steps):
             flush.sum()
@@ -228,11 +230,14 @@ def time_decode(args, mtp=False, paged=None):
                 e[i + 1].record()
             evs.append(e)
         torch.cuda.synchronize()
+        if stats:   # one graph: mean, median, minimum
+            d = sorted(e[0].elapsed_time(e[1]) for e in evs)
+            return sum(d) / len(d), d[len(d) // 2], d[0]
         return [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / len(evs) for i in range(len(graphs))]
 
     for g in (g_step, g_sel, g_att):
         g.replay()
-    ms = timed([g_step])[0]
+    ms, med, mn = timed([g_step], stats=True)
     sel_ms, att_ms = timed([g_sel, g_att])
     sum_s, sum_nc = set_sizes(r)
     n_seq, n_q = r.n_seq, r.n_q
@@ -241,7 +246,7 @@ def time_decode(args, mtp=False, paged=None):
     blocks_read = sum(L // 4 for L in b.seq_lens_host())
     step_bytes = blocks_read * BLOCK_KEY_BYTES + sum_s * TOKEN_GATHER_BYTES + n_q * (
         2 * Q_ROW_BYTES + 4 * 128 * 2 + 16)
-    return dict(value=n_q / (ms * 1e-3), ms_per_step=ms,
+    return dict(value=n_q / (ms * 1e-3), ms_per_step=ms, step_ms_median=med, step_ms_min=mn,
                 stages_ms=dict(select=sel_ms, attend=att_ms),
                 hbm=dict(bytes=step_bytes, gbs=step_bytes / (ms * 1e-3) / 1e9),
                 runner=r, batch=b)
@@ -292,7 +297,16 @@ def cpu_baseline(pre, budget_s):
         rows.append(int(row))
     per_row = t_rows / len(rows)
     est = t_pool + per_row * chunk
-    return dict(value=chunk / est, unit="tokens/s", cores=int(cores), kind="oracle",
+    cpu = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=chunk / est, unit="tokens/s", cores=int(cores), kind="oracle", cpu=cpu,
+                host_cpus=os.cpu_count(),
                 sample=(f"{len(rows)} of {chunk} query rows (random), full per-row pipeline "
                         f"(score {1015808 // 4}+ blocks, select, expand, attend) plus pooling of "
                         f"the chunk's {chunk // 4} new blocks; time scaled to the whole chunk"),
@@ -326,7 +340,9 @@ def main():
         log(f"prefill: {pre['ms_per_step']:.3f} ms/step, stages {pre['stages_ms']}")
         attend_file = os.path.join(ROOT, "block_sparse_long_02_amd", "csrc", "qsa_attend.hip")
         out.update(value=round(pre["value"], 1), unit="tokens/s",
-                   ms_per_step=round(pre["ms_per_step"], 4))
+                   ms_per_step=round(pre["ms_per_step"], 4),
+                   step_ms_median=round(pre["step_ms_median"], 4),
+                   step_ms_min=round(pre["step_ms_min"], 4))
         out["config"] = {
             "workload": "chunked prefill: 32768-token chunk on a 1015808-token cached prefix "
                         "(1048576 total), batch 1, budget 512 blocks + tail",
@@ -384,6 +400,8 @@ def main():
         log(f"decode: {dec['ms_per_step']:.4f} ms/step, stages {dec['stages_ms']}")
         d = {"value": round(dec["value"], 1), "unit": "tokens/s",
              "ms_per_step": round(dec["ms_per_step"], 4),
+             "step_ms_median": round(dec["step_ms_median"], 4),
+             "step_ms_min": round(dec["step_ms_min"], 4),
              "config": {"workload": "decode: 32 sequences x (131072 cached + 1 new) tokens, "
                                     "budget 512 blocks + tail, MALL flushed before each step"},
              "roofline": {"bound": "hbm", "scope": "whole step",
@@ -414,6 +432,8 @@ def main():
         log(f"mtp decode: {mt['ms_per_step']:.4f} ms/step, stages {mt['stages_ms']}")
         m = {"value": round(mt["value"], 1), "unit": "tokens/s",
              "ms_per_step": round(mt["ms_per_step"], 4),
+             "step_ms_median": round(mt["step_ms_median"], 4),
+             "step_ms_min": round(mt["step_ms_min"], 4),
              "config": {"workload": "multi-token decode: 32 sequences x (131072 cached + 4 new) "
                                     "tokens, 4 query tokens each (a new token and 3 speculative), "
                                     "budget 512 blocks + tail, MALL flushed before each step"},

@@ -7,6 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libqsa.so")
+PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")   # micro-benchmarks, measurement only
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -23,9 +24,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
-    tmp = LIB + ".tmp"
+def _link(srcs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(PKG, "csrc"), "-o", tmp, *srcs]
     if verbose:
@@ -33,7 +33,13 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """libqsa.so (the QSA path) and libqsa_probe.so (micro-benchmarks)."""
+    _link(sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip"))), LIB, verbose)
+    _link(sorted(glob.glob(os.path.join(PKG, "csrc", "probe", "*.hip"))), PROBE_LIB, verbose)
     return LIB
 
 

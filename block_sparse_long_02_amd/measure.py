@@ -15,6 +15,12 @@ factor = known bytes / counted bytes.  Then one step of each workload:
 `summarize` writes, per kernel, the calibrated bytes per launch and the hash
 of the source file the kernel was built from, so that a reader (bench.py)
 uses the figures only while that source is unchanged.
+
+    python3 -m block_sparse_long_02_amd.measure peaks OUT_JSON
+
+times the micro-benchmarks of libqsa_probe.so: the sustained rate of the
+16x16x32 bf16 MFMA and the sustained HBM read and copy bandwidth, beside the
+published peaks the roofline fractions use.
 """
 from __future__ import annotations
 
@@ -138,10 +144,72 @@ def summarize(fetch_csv: str, write_csv: str, out_json: str):
         print(k, v)
 
 
+def peaks(out_json: str):
+    """Sustained MFMA and HBM rates from libqsa_probe.so, timed with HIP events."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(_PKG, "libqsa_probe.so"))
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.qsa_probe_mfma_bf16.argtypes = [i32, i32, i32, vp, vp]
+    lib.qsa_probe_read.argtypes = [vp, i64, i32, vp, vp]
+    lib.qsa_probe_copy.argtypes = [vp, vp, i64, i32, vp]
+    st = vp(torch.cuda.current_stream().cuda_stream)
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+    props = torch.cuda.get_device_properties(0)
+    n_cu = props.multi_processor_count
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        return best
+
+    res = {"device": props.name, "compute_units": n_cu}
+    iters = 20000
+    # 16 chains per wave: with fewer, the compiler rotates the loop-carried
+    # accumulators through register moves and the loop measures those
+    for chains in (16,):
+        for wg_per_cu in (2, 8):
+            n_wg = wg_per_cu * n_cu
+            t = timed(lambda: lib.qsa_probe_mfma_bf16(n_wg, iters, chains, vp(sink.data_ptr()), st))
+            flops = n_wg * 4 * iters * chains * 16384
+            u = sink[:4].view(torch.int32).cpu().numpy().astype("int64") & 0xFFFFFFFF
+            cyc, ticks = int(u[0] | (u[1] << 32)), int(u[2] | (u[3] << 32))
+            ghz = cyc / (ticks / 100e6) / 1e9 if ticks else None
+            res[f"mfma_bf16_16x16x32_{chains}chains_{wg_per_cu}wg"] = {
+                "tflops": round(flops / t / 1e12, 1), "published_tflops": 2500.0,
+                "shader_clock_ghz": round(ghz, 3) if ghz else None,
+                "workgroups": n_wg, "seconds": t}
+    nbytes = 4 << 30
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for wg_per_cu in (8, 32):
+        n = wg_per_cu * n_cu
+        t = timed(lambda: lib.qsa_probe_read(vp(a.data_ptr()), nbytes, n, vp(sink.data_ptr()), st))
+        res[f"hbm_read_{wg_per_cu}wg"] = {"gbs": round(nbytes / t / 1e9, 1), "bytes": nbytes}
+        t = timed(lambda: lib.qsa_probe_copy(vp(a.data_ptr()), vp(b.data_ptr()), nbytes, n, st))
+        res[f"hbm_copy_{wg_per_cu}wg"] = {"gbs": round(2 * nbytes / t / 1e9, 1),
+                                          "bytes_moved": 2 * nbytes}
+    res["published_hbm_gbs"] = 8000.0
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res, indent=1))
+
+
 if __name__ == "__main__":
     if sys.argv[1:2] == ["probe"]:
         probe()
+    elif sys.argv[1:2] == ["peaks"] and len(sys.argv) == 3:
+        peaks(sys.argv[2])
     elif sys.argv[1:2] == ["summarize"] and len(sys.argv) == 5:
         summarize(*sys.argv[2:5])
     else:
-        sys.exit("usage: measure.py probe | summarize FETCH_CSV WRITE_CSV OUT_JSON")
+        sys.exit("usage: measure.py probe | summarize FETCH_CSV WRITE_CSV OUT_JSON | peaks OUT_JSON")

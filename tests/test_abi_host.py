@@ -197,3 +197,27 @@ def test_page_arguments_are_validated(L):
     assert L.qsa_pool_block_keys(A, 128, A, 128, A, A, 0, 4, A, 16, 256, None) == 0
     assert L.qsa_attend_prefill(A, A, A, 1, 0, 4, A, A, 0, 512, A, A, 16, A, None, None, 0.0625,
                                 A, 4, 1 << 22, None) == 0
+
+
+def test_probe_library_exports_and_validates():
+    """The measurement probes (include/qsa_probe.h) load and reject bad arguments on the host."""
+    path = os.path.join(os.path.dirname(qsa.LIB_PATH), "libqsa_probe.so")
+    assert os.path.exists(path), "libqsa_probe.so is not built"
+    P = ctypes.CDLL(path)
+    src = open(os.path.join(ROOT, "include", "qsa_probe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(qsa_[a-z_0-9]+)\s*\(", src)))
+    assert names == ["qsa_probe_copy", "qsa_probe_mfma_bf16", "qsa_probe_read"], names
+    for n in names:
+        assert hasattr(P, n), n
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    P.qsa_probe_mfma_bf16.argtypes = [i32, i32, i32, vp, vp]
+    P.qsa_probe_read.argtypes = [vp, i64, i32, vp, vp]
+    P.qsa_probe_copy.argtypes = [vp, vp, i64, i32, vp]
+    assert P.qsa_probe_mfma_bf16(0, 10, 8, ALIGNED, None) == 1
+    assert P.qsa_probe_mfma_bf16(8, 0, 8, ALIGNED, None) == 1
+    assert P.qsa_probe_mfma_bf16(8, 10, 8, None, None) == 1
+    assert P.qsa_probe_mfma_bf16(8, 10, 12, ALIGNED, None) == 1
+    assert P.qsa_probe_read(ALIGNED, 100, 8, ALIGNED, None) == 1        # not a multiple of 64
+    assert P.qsa_probe_read(MISALIGNED, 128, 8, ALIGNED, None) == 1
+    assert P.qsa_probe_copy(ALIGNED, ALIGNED, 0, 8, None) == 1

@@ -661,3 +661,15 @@ def test_full_size_mtp_decode_128k_sampled_rows():
     _sync()
     kinds, worst = _check_rows(r, OracleView(b), _sampled(b.n_q, 8, 82, always=(0, 3, b.n_q - 1)))
     print("mtp decode 32 x 4 at 128K:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_full_size_ragged_decode_all_rows():
+    # 8 sequences, log-uniform lengths up to 1M tokens, partial tail blocks,
+    # near ties in half of them: every row against the oracle
+    b = W.ragged_decode(device="cuda")
+    print("lengths", b.seq_lens_host(), flush=True)
+    r = QSARunner(b)
+    r.step()
+    _sync()
+    kinds, worst = _check_rows(r, OracleView(b), range(b.n_q))
+    print("ragged decode (full size):", kinds, f"worst rel-L2 {worst:.2e}")

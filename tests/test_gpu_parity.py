@@ -673,3 +673,44 @@ def test_full_size_ragged_decode_all_rows():
     _sync()
     kinds, worst = _check_rows(r, OracleView(b), range(b.n_q))
     print("ragged decode (full size):", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+# ------------------------------------------------------- mixed and small batches
+
+def _concat(a, b):
+    """One batch holding a's sequences then b's (caches padded to one length)."""
+    cap = max(a.l_cap, b.l_cap)
+
+    def pad(t):   # [n_seq][..., L][d] -> length cap on the token axis (dim -2)
+        out = torch.zeros(*t.shape[:-2], cap, t.shape[-1], dtype=t.dtype)
+        out[..., :t.shape[-2], :] = t
+        return out
+    cu = torch.cat([a.cu_q, b.cu_q[1:] + a.cu_q[-1]])
+    return W.QSABatch(seq_len=torch.cat([a.seq_len, b.seq_len]), cu_q=cu,
+                      idx_q=torch.cat([a.idx_q, b.idx_q]), w=torch.cat([a.w, b.w]),
+                      idx_k=torch.cat([pad(a.idx_k), pad(b.idx_k)]),
+                      q=torch.cat([a.q, b.q]), k=torch.cat([pad(a.k), pad(b.k)]),
+                      v=torch.cat([pad(a.v), pad(b.v)]), budget=a.budget,
+                      meta={"kind": "prefill"})
+
+
+def test_mixed_prefill_and_decode_rows_in_one_call():
+    # a 700-row prefill chunk (past 4096 candidates, sampled path) and three
+    # one-row sequences in one call: max_q_len 700 takes the tiled path for all
+    pre = W.make_prefill(prefix=20001, chunk=700, budget=512, seg=64, n_plant=16, seed=90)
+    dec = W.make_decode(seq_lens=[40001, 9, 70002], budget=512, n_plant=16, seed=91)
+    b = _concat(pre, dec)
+    assert b.max_q_len() == 700 and b.n_q == 703
+    r = QSARunner(b.to("cuda"))
+    r.step()
+    _sync()
+    rows = list(range(0, 700, 37)) + [699, 700, 701, 702]
+    kinds, worst = _check_rows(r, OracleView(b), rows)
+    print("mixed batch:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_small_budget_decode():
+    # budget 16 on the decode path (every score kept, one workgroup per row)
+    b = W.make_decode(seq_lens=[131073, 20001, 4099, 17], budget=16, n_plant=8, seed=92)
+    kinds, worst = _end_to_end(b, range(4))
+    print("decode, budget 16:", kinds, f"worst rel-L2 {worst:.2e}")

@@ -153,6 +153,7 @@ def peaks(out_json: str):
     lib.qsa_probe_mfma_bf16.argtypes = [i32, i32, i32, vp, vp]
     lib.qsa_probe_read.argtypes = [vp, i64, i32, vp, vp]
     lib.qsa_probe_copy.argtypes = [vp, vp, i64, i32, vp]
+    lib.qsa_probe_gather.argtypes = [vp, i64, vp, i64, i32, i32, vp, vp]
     st = vp(torch.cuda.current_stream().cuda_stream)
     sink = torch.zeros(256, dtype=torch.float32, device="cuda")
     props = torch.cuda.get_device_properties(0)
@@ -197,6 +198,21 @@ def peaks(out_json: str):
         t = timed(lambda: lib.qsa_probe_copy(vp(a.data_ptr()), vp(b.data_ptr()), nbytes, n, st))
         res[f"hbm_copy_{wg_per_cu}wg"] = {"gbs": round(2 * nbytes / t / 1e9, 1),
                                           "bytes_moved": 2 * nbytes}
+    del a, b
+    # gathers of fixed-size runs at random places in 8 GiB (32x the MALL),
+    # 1 GiB per launch: the access pattern of the attention kernels (2 KB runs)
+    gbytes = 8 << 30
+    g = torch.ones(gbytes // 4, dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    for run in (256, 512, 1024, 2048, 4096, 8192, 16384):
+        n_runs = (1 << 30) // run
+        idx = torch.randperm(gbytes // run, generator=gen, device="cuda")[:n_runs].to(torch.int32)
+        n = 8 * n_cu
+        t = timed(lambda: lib.qsa_probe_gather(vp(g.data_ptr()), gbytes, vp(idx.data_ptr()), n_runs,
+                                               run, n, vp(sink.data_ptr()), st))
+        res[f"hbm_gather_{run}B_8wg"] = {"gbs": round((1 << 30) / t / 1e9, 1), "bytes": 1 << 30,
+                                         "run_bytes": run}
+        del idx
     res["published_hbm_gbs"] = 8000.0
     with open(out_json, "w") as f:
         json.dump(res, f, indent=1)

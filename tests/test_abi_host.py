@@ -207,13 +207,15 @@ def test_probe_library_exports_and_validates():
     src = open(os.path.join(ROOT, "include", "qsa_probe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = sorted(set(re.findall(r"\b(qsa_[a-z_0-9]+)\s*\(", src)))
-    assert names == ["qsa_probe_copy", "qsa_probe_mfma_bf16", "qsa_probe_read"], names
+    assert names == ["qsa_probe_copy", "qsa_probe_gather", "qsa_probe_mfma_bf16",
+                     "qsa_probe_read"], names
     for n in names:
         assert hasattr(P, n), n
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     P.qsa_probe_mfma_bf16.argtypes = [i32, i32, i32, vp, vp]
     P.qsa_probe_read.argtypes = [vp, i64, i32, vp, vp]
     P.qsa_probe_copy.argtypes = [vp, vp, i64, i32, vp]
+    P.qsa_probe_gather.argtypes = [vp, i64, vp, i64, i32, i32, vp, vp]
     assert P.qsa_probe_mfma_bf16(0, 10, 8, ALIGNED, None) == 1
     assert P.qsa_probe_mfma_bf16(8, 0, 8, ALIGNED, None) == 1
     assert P.qsa_probe_mfma_bf16(8, 10, 8, None, None) == 1
@@ -221,3 +223,7 @@ def test_probe_library_exports_and_validates():
     assert P.qsa_probe_read(ALIGNED, 100, 8, ALIGNED, None) == 1        # not a multiple of 64
     assert P.qsa_probe_read(MISALIGNED, 128, 8, ALIGNED, None) == 1
     assert P.qsa_probe_copy(ALIGNED, ALIGNED, 0, 8, None) == 1
+    assert P.qsa_probe_gather(ALIGNED, 1 << 20, ALIGNED, 16, 3000, 8, ALIGNED, None) == 1  # not 2^k
+    assert P.qsa_probe_gather(ALIGNED, 1 << 20, None, 16, 2048, 8, ALIGNED, None) == 1
+    assert P.qsa_probe_gather(ALIGNED, 1 << 20, ALIGNED, 0, 2048, 8, ALIGNED, None) == 1
+    assert P.qsa_probe_gather(ALIGNED, 1 << 40, ALIGNED, 16, 16, 8, ALIGNED, None) == 2

@@ -223,12 +223,14 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
 }
 
 // ------------------------------------------------------- prefill GEMM
-// Prefill variant of the score GEMM: workgroup = 16*MT queries (4 waves, each
-// owning MT m-tiles of 16 rows = 4 queries x 4 heads) x a chunk of columns.
-// Block keys go through a 2-stage LDS ring of 64 columns (16 KB) shared by
-// the 4 waves: every thread loads 4 chunks of 16 bytes of the next stage into
-// registers while the current stage is multiplied, then writes them to LDS
-// (each wave instruction covers a 1 KB run of 4 columns).  Inside a stage,
+// Prefill variant of the score GEMM: workgroup = 4*MT*NW queries (NW waves,
+// each owning MT m-tiles of 16 rows = 4 queries x 4 heads) x a chunk of
+// columns.  The sample pass uses 4 waves, the filter pass 8 (64 queries, two
+// workgroups and 4 waves per SIMD, at most 128 VGPRs).  Block keys go through
+// a 2-stage LDS ring of 64 columns (16 KB) shared by the waves: every thread
+// loads 16/NW chunks of 16 bytes of the next stage into registers while the
+// current stage is multiplied, then writes them to LDS (each wave
+// instruction covers a 1 KB run of 4 columns).  Inside a stage,
 // chunk q (16 bytes) of column c sits at chunk slot q ^ (c % 16), which makes
 // the MFMA B-fragment reads (16 columns x one chunk) hit 16 distinct bank
 // groups.
@@ -242,16 +244,18 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
 // the exact tau test run once per workgroup over the pending lists, one entry
 // per lane.
 constexpr int kStageCols = 64;
-#ifndef QSA_PENDING
-#define QSA_PENDING 24
-#endif
-constexpr int kPending = QSA_PENDING;   // pending pre-filter passes per row and workgroup
+// pending pre-filter passes per row and workgroup: as many as the LDS of two
+// 8-wave (three 4-wave) workgroups per CU holds
+template <int NW>
+constexpr int kPending = NW == 8 ? 32 : 24;
 
 // Largest column chunk a workgroup takes (host-side chunks are <= this).
 constexpr int kMaxChunkCols = 2048;
 
-template <int MT, bool kSample, bool kPaged>
-__global__ void __launch_bounds__(256, QSA_SCORE_WGS)
+// (the second launch bound is the minimum number of waves per SIMD: 4-wave
+// workgroups at QSA_SCORE_WGS per CU, 8-wave workgroups at 2 per CU)
+template <int MT, int NW, bool kSample, bool kPaged>
+__global__ void __launch_bounds__(64 * NW, NW == 4 ? QSA_SCORE_WGS : 4)
 score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
                   const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
                   int n_seq, int n_q, int tiles_per_seq, int max_blocks,
@@ -259,9 +263,12 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
                   const uint32_t* __restrict__ thresh, int32_t* __restrict__ cnt,
                   u32x2* __restrict__ cand, uint16_t* __restrict__ samples, int ns_stride,
                   Pages pg) {
-  constexpr int QT = 16 * MT;
+  constexpr int QT = 4 * MT * NW;   // queries per workgroup
+  constexpr int CPT = 16 / NW;      // 16-byte chunks of a stage per thread
+  constexpr int kWaveCols = 4 * CPT;   // stage columns each wave loads
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int stride = kSample ? kPrefillSampleStride : 1;
-  constexpr int kPend = kSample ? 1 : kPending;
+  constexpr int kPend = kSample ? 1 : kPending<NW>;
   // paged: the physical pages of the chunk's blocks (pages hold >= 64 blocks)
   constexpr int kPgSlots = kPaged ? kMaxChunkCols * stride / 64 + 1 : 1;
   __shared__ int s_pg[kPgSlots];
@@ -367,17 +374,17 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
   const int nrec = ((v1 - 1) * stride + 1) * kIdxDim * 2;
   const __amdgpu_buffer_rsrc_t bk_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)bseq, (short)0, nrec, 0x00020000);
-  // This thread carries 4 chunks of a stage: column c = 16*wave + 4*i +
-  // lane/16, chunk slot lane%16, which holds chunk (lane%16) ^ (c%16); its
-  // byte offsets relative to the stage's first column are fixed.
-  int loff[4];
+  // This thread carries CPT chunks of a stage: column c = kWaveCols*wave +
+  // 4*i + lane/16, chunk slot lane%16, which holds chunk (lane%16) ^ (c%16);
+  // its byte offsets relative to the stage's first column are fixed.
+  int loff[CPT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = 16 * wave + 4 * i + (lane >> 4);
+  for (int i = 0; i < CPT; ++i) {
+    const int c = kWaveCols * wave + 4 * i + (lane >> 4);
     const int q = (lane & 15) ^ (c & 15);
     loff[i] = (c * stride * kIdxDim + q * 8) * 2;
   }
-  auto load_stage = [&](u32x4 (&r)[4], int st) {
+  auto load_stage = [&](u32x4 (&r)[CPT], int st) {
     if constexpr (kPaged && !kSample) {
       // a 64-column stage lies inside one page (pages hold >= 64 blocks and
       // stages start at multiples of 64): the contiguous path's offsets from
@@ -389,14 +396,14 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(bseq + pb * kIdxDim), (short)0, nrec_st, 0x00020000);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < CPT; ++i)
         r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, loff[i], 0, 0));
     } else if constexpr (kPaged) {
       // sample pass: each column is its own block (32 apart), looked up in
       // the LDS page slice; columns past v1 - 1 read column v1 - 1 and are zeroed
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 16 * wave + 4 * i + (lane >> 4);
+      for (int i = 0; i < CPT; ++i) {
+        const int c = kWaveCols * wave + 4 * i + (lane >> 4);
         const int q = (lane & 15) ^ (c & 15);
         const int vcol = v0 + st * kStageCols + c;
         const int64_t blk = (int64_t)min(vcol, v1 - 1) * stride;
@@ -408,17 +415,17 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
     } else {
       const int base = (v0 + st * kStageCols) * stride * kIdxDim * 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < CPT; ++i) {
         r[i] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(bk_rsrc, base + loff[i], 0, 0));
       }
     }
   };
-  auto store_stage = [&](const u32x4 (&r)[4], int st) {
+  auto store_stage = [&](const u32x4 (&r)[CPT], int st) {
     uint16_t* dst = s_b[st & 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = 16 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < CPT; ++i) {
+      const int c = kWaveCols * wave + 4 * i + (lane >> 4);
       *(u32x4*)(dst + c * kIdxDim + (lane & 15) * 8) = r[i];
     }
   };
@@ -494,7 +501,7 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
     }
   };
   auto run = [&](auto filter_tag) {
-    u32x4 stage_regs[4];
+    u32x4 stage_regs[CPT];
     load_stage(stage_regs, 0);
     store_stage(stage_regs, 0);
     __syncthreads();
@@ -530,8 +537,8 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
       for (int mt = 0; mt < MT; ++mt) s_pcnt[(wave * MT + mt) * 4 + grp] = r_pc[mt];
     }
     __syncthreads();
-    // exact score of every pending entry; each wave takes rows wave, wave+4, ...
-    for (int j = wave; j < QT; j += 4) {
+    // exact score of every pending entry; each wave takes rows wave, wave+NW, ...
+    for (int j = wave; j < QT; j += NW) {
       const int n = min(s_pcnt[j], kPend);
       uint32_t key = 0;
       bool take = false;
@@ -1323,29 +1330,36 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
     return launch_status();
   }
 
-  const int qt = 16 * kPrefillMT;
-  const int64_t tiles_per_seq = (max_q_len + qt - 1) / qt;
-  const int64_t gx = tiles_per_seq * n_seq;
+#ifndef QSA_FILTER_WAVES
+#define QSA_FILTER_WAVES 8
+#endif
+  constexpr int kFilterWaves = QSA_FILTER_WAVES;   // waves per filter-pass workgroup
+  auto row_tiles = [&](int nw) { return (max_q_len + 4 * kPrefillMT * nw - 1) / (4 * kPrefillMT * nw); };
+  const int64_t gx = (int64_t)row_tiles(4) * n_seq;
   if (gx > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
 #ifndef QSA_PREFILL_CHUNK
 #define QSA_PREFILL_CHUNK 2048
 #endif
   constexpr int chunk = QSA_PREFILL_CHUNK;   // candidate blocks per workgroup
   static_assert(chunk <= kMaxChunkCols && chunk % kStageCols == 0, "prefill chunk");
-  auto gemm = [&](auto sample_tag, dim3 grid, int chunk_cols) {
+  auto gemm = [&](auto sample_tag, auto waves_tag, unsigned gy, int chunk_cols) {
     constexpr bool kS = decltype(sample_tag)::value;
+    constexpr int kNW = decltype(waves_tag)::value;
+    const int tiles = row_tiles(kNW);
+    const dim3 grid((unsigned)((int64_t)tiles * n_seq), gy);
     auto launch = [&](auto kern) {
-      hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const uint16_t*)idx_q, w, cu_q, seq_len,
-                         n_seq, n_q, (int)tiles_per_seq, max_blocks, (const uint16_t*)block_keys,
+      hipLaunchKernelGGL(kern, grid, dim3(64 * kNW), 0, st, (const uint16_t*)idx_q, w, cu_q,
+                         seq_len, n_seq, n_q, tiles, max_blocks, (const uint16_t*)block_keys,
                          bk_seq_stride, chunk_cols, ws.thresh, ws.cnt, ws.cand, ws.samples,
                          ws.ns_stride, pg);
     };
-    if (pg.table) launch(score_gemm_kernel<kPrefillMT, kS, true>);
-    else launch(score_gemm_kernel<kPrefillMT, kS, false>);
+    if (pg.table) launch(score_gemm_kernel<kPrefillMT, kNW, kS, true>);
+    else launch(score_gemm_kernel<kPrefillMT, kNW, kS, false>);
   };
   // 1. sample pass (only rows with more than kCandCap candidates need it)
   if (max_blocks > kCandCap) {
-    gemm(std::true_type{}, dim3((unsigned)gx, (ws.ns_stride + chunk - 1) / chunk), chunk);
+    gemm(std::true_type{}, std::integral_constant<int, 4>{}, (ws.ns_stride + chunk - 1) / chunk,
+         chunk);
   }
   // 2. thresholds (also preset the list counters)
   hipLaunchKernelGGL(threshold_kernel, dim3(n_q), dim3(256), 0, st, cu_q, seq_len, n_seq,
@@ -1354,7 +1368,7 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
   //    the pre-filter, spread over its n_c / chunk workgroups; the chunk is
   //    halved (down to one stage) until the longest row expects at most
   //    kPassTarget passes per workgroup, so that short rows (a larger share
-  //    passes) rarely fill their kPending-entry lists.
+  //    passes) rarely fill their pending lists.
   if (max_blocks > 0) {
 #ifndef QSA_PASS_TARGET
 #define QSA_PASS_TARGET 24
@@ -1364,9 +1378,9 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
     while (fchunk > kStageCols &&
            (int64_t)fchunk * (budget + kSampleExtra) > (int64_t)kPassTarget * max_blocks)
       fchunk >>= 1;
-    dim3 grid((unsigned)gx, (max_blocks + fchunk - 1) / fchunk);
-    if (grid.y > 65535) return QSA_ERR_UNSUPPORTED;
-    gemm(std::false_type{}, grid, fchunk);
+    const int gy = (max_blocks + fchunk - 1) / fchunk;
+    if (gy > 65535) return QSA_ERR_UNSUPPORTED;
+    gemm(std::false_type{}, std::integral_constant<int, kFilterWaves>{}, (unsigned)gy, fchunk);
   }
   // 4. exact select per row (rows whose list came out short or overflowed
   //    are selected exactly by recomputing their scores)

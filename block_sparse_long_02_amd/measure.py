@@ -43,9 +43,9 @@ COPY_BYTES = 1 << 30
 # indexer transforms (dispatch 1), which selects other blocks.
 KERNELS = {
     "pool_block_keys_prefill_1m": ("pool_block_keys_kernel", "qsa_pool.hip", 1),
-    "score_sample_prefill_1m": ("score_gemm_kernel<2, true, false>", "qsa_index.hip", 0),
+    "score_sample_prefill_1m": ("score_gemm_kernel<2, 4, true, false>", "qsa_index.hip", 0),
     "threshold_prefill_1m": ("threshold_kernel", "qsa_index.hip", 0),
-    "score_filter_prefill_1m": ("score_gemm_kernel<2, false, false>", "qsa_index.hip", 0),
+    "score_filter_prefill_1m": ("score_gemm_kernel<2, 8, false, false>", "qsa_index.hip", 0),
     "final_select_prefill_1m": ("final_select_kernel", "qsa_index.hip", 0),
     "attend_prefill_1m": ("attend_kernel<true>", "qsa_attend.hip", 0),
     "attend_prefill_1m_transformed": ("attend_kernel<true>", "qsa_attend.hip", 1),

@@ -244,6 +244,14 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
 // the exact tau test run once per workgroup over the pending lists, one entry
 // per lane.
 constexpr int kStageCols = 64;
+
+// v_dot2_f32_bf16 with a destination of its own: for a loop-invariant
+// accumulator the compiler picks the accumulating form plus a register copy
+__device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float c) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
 // pending pre-filter passes per row and workgroup: as many as the LDS of two
 // 8-wave (three 4-wave) workgroups per CU holds
 template <int NW>
@@ -462,8 +470,13 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
       for (int ks = 0; ks < 4; ++ks) acc[mt] = mfma_16x16x32(af[mt][ks], bf[ks], acc[mt]);
     }
   };
-  auto epi = [&](auto filter_tag, const f32x4 (&acc)[MT], int vbase) {
-    constexpr bool kFilter = decltype(filter_tag)::value;
+  // mode 0: every score emitted exactly (sample pass, rows that keep all
+  // candidates); 1: pre-filter; 2: pre-filter in a chunk whose columns all
+  // lie below every row's candidate count and inside whole stages, so the
+  // column test is dropped and the pass mask is the pre-filter's ballot
+  auto epi = [&](auto mode_tag, const f32x4 (&acc)[MT], int vbase) {
+    constexpr int kMode = decltype(mode_tag)::value;
+    constexpr bool kFilter = kMode != 0;
     const int vcol = vbase + col;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -481,12 +494,13 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
       const bf16x2 r23 = __builtin_bit_cast(bf16x2, __builtin_elementwise_max(__builtin_bit_cast(s16x2, p23), z));
       // margin = fast - tau_lo (the sum starts at -tau_lo; its float32
       // rounding, ~2^-24 of tau, is far inside the 2^-7 slack)
-      float margin = __builtin_amdgcn_fdot2_f32_bf16(r23, r_wc23[mt], r_ntlo[mt], false);
+      float margin = dot2_bf16(r23, r_wc23[mt], r_ntlo[mt]);
       margin = __builtin_amdgcn_fdot2_f32_bf16(r01, r_wc01[mt], margin, false);
-      if (__ballot(margin >= 0.f)) {         // a few lanes: append raw accumulators
-        const bool pass = margin >= 0.f && vcol < r_nc[mt];
+      const uint64_t hit = __ballot(margin >= 0.f);
+      if (hit) {         // a few lanes: append raw accumulators
+        const bool pass = kMode == 2 ? margin >= 0.f : (margin >= 0.f && vcol < r_nc[mt]);
         // this lane's 16-lane group is its row: rank among the group's passes
-        const uint32_t gm = (uint32_t)(__ballot(pass) >> (16 * grp)) & 0xFFFFu;
+        const uint32_t gm = (uint32_t)((kMode == 2 ? hit : __ballot(pass)) >> (16 * grp)) & 0xFFFFu;
         const int slot = r_pc[mt] + __popc(gm & ((1u << col) - 1u));
         if (pass) {
           if (slot < kPend) {
@@ -500,7 +514,7 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
       }
     }
   };
-  auto run = [&](auto filter_tag) {
+  auto run = [&](auto mode_tag) {
     u32x4 stage_regs[CPT];
     load_stage(stage_regs, 0);
     store_stage(stage_regs, 0);
@@ -517,19 +531,22 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
       mfma_b(b0, a0);                       // tile 0
       read_b(sb, 2, b0);
       mfma_b(b1, a1);                       // tile 1
-      epi(filter_tag, a0, cbase);
+      epi(mode_tag, a0, cbase);
       read_b(sb, 3, b1);
       mfma_b(b0, a0);                       // tile 2
-      epi(filter_tag, a1, cbase + 16);
+      epi(mode_tag, a1, cbase + 16);
       mfma_b(b1, a1);                       // tile 3
-      epi(filter_tag, a0, cbase + 32);
-      epi(filter_tag, a1, cbase + 48);
+      epi(mode_tag, a0, cbase + 32);
+      epi(mode_tag, a1, cbase + 48);
       if (more) store_stage(stage_regs, st + 1);
       __syncthreads();   // stage st+1 visible; stage st's buffer free for st+2
     }
   };
-  if (kSample || collect_all) run(std::false_type{});
-  else run(std::true_type{});
+  // rows are in position order, so the first row has the fewest candidates
+  const bool full_chunk = v1 <= min((pos0 + 1) >> 2, max_blocks) && (v1 - v0) % kStageCols == 0;
+  if (kSample || collect_all) run(std::integral_constant<int, 0>{});
+  else if (full_chunk) run(std::integral_constant<int, 2>{});
+  else run(std::integral_constant<int, 1>{});
 
   if (!kSample && !collect_all) {
     if (col == 0) {

@@ -507,7 +507,12 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
             s_pacc[j][slot] = acc[mt];
             s_pidx[j][slot] = vcol;
           } else {
-            emit_exact(acc[mt], j, vcol, vcol);   // rare: list full
+            // rare: list full.  The row index goes through an empty asm so
+            // that the path's addresses are formed here instead of being
+            // kept live (spilled) across the loop.
+            int jr = j;
+            asm volatile("" : "+v"(jr));
+            emit_exact(acc[mt], jr, vcol, vcol);
           }
         }
         r_pc[mt] += __popc(gm);

@@ -7,6 +7,8 @@ It does no arithmetic of its own.
 """
 from __future__ import annotations
 
+import copy
+
 import torch
 
 from . import qsa
@@ -147,6 +149,57 @@ class QSARunner:
         self.pool(stream)
         self.select(stream)
         self.attend(stream)
+
+    # pipelined prefill ----------------------------------------------------
+    def _rows(self, a: int, c: int) -> "QSARunner":
+        """Query rows [a, c) of a one-sequence prefill chunk as a chunk of its
+        own (the sequence then ends at position prefix + c - 1): the same
+        caches and outputs (views)."""
+        b = self.b
+        L = b.seq_lens_host()[0]
+        dev = b.idx_q.device
+        v = copy.copy(self)
+        v.b = QSABatch(seq_len=torch.tensor([L - self.n_q + c], dtype=torch.int32, device=dev),
+                       cu_q=torch.tensor([0, c - a], dtype=torch.int32, device=dev),
+                       idx_q=b.idx_q[a:c], w=b.w[a:c], idx_k=b.idx_k, q=b.q[a:c], k=b.k, v=b.v,
+                       budget=b.budget, meta=dict(b.meta))
+        v.n_q = v.max_q_len = c - a
+        v.idx_q_t = self.idx_q_t[a:c] if self.idx_q_t is not None else None
+        v.sel, v.sel_count = self.sel[a:c], self.sel_count[a:c]
+        v.out, v.lse = self.out[a:c], self.lse[a:c]
+        return v
+
+    def step_pipelined(self, parts: int = 4):
+        """One prefill step with the chunk's query rows in `parts` consecutive
+        pieces: piece i's attention runs on a second stream while piece i+1
+        is selected, so the memory-bound attention overlaps the MFMA-bound
+        score GEMM.  Same calls on the same rows, so the same results as
+        step().  One-sequence prefill batches only."""
+        assert not (self.decode or self.mtp) and self.n_seq == 1, "one-sequence prefill"
+        key = ("pipe", parts)
+        if getattr(self, "_pipe_key", None) != key:
+            bounds = [self.n_q * i // parts for i in range(parts + 1)]
+            self._pipe_parts = [self._rows(a, c) for a, c in zip(bounds[:-1], bounds[1:]) if c > a]
+            self._pipe_streams = (torch.cuda.Stream(), torch.cuda.Stream())
+            self._pipe_key = key
+        sa, sb = self._pipe_streams
+        main = torch.cuda.current_stream()
+        sa.wait_stream(main)
+        sb.wait_stream(main)
+        done = []
+        with torch.cuda.stream(sa):
+            self.pool()
+            for u in self._pipe_parts:
+                u.select()
+                e = torch.cuda.Event()
+                e.record(sa)
+                done.append(e)
+        with torch.cuda.stream(sb):
+            for u, e in zip(self._pipe_parts, done):
+                sb.wait_event(e)
+                u.attend()
+        main.wait_stream(sa)
+        main.wait_stream(sb)
 
     # HIP graphs ----------------------------------------------------------
     def capture(self, parts=("pool", "select", "attend")) -> torch.cuda.CUDAGraph:

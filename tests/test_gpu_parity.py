@@ -526,6 +526,29 @@ def test_paged_prefill_unaligned_chunk_start():
     print("paged prefill:", kinds, f"worst rel-L2 {worst:.2e}")
 
 
+def test_pipelined_prefill_matches_sequential():
+    # the step with the chunk's rows in pieces, each piece's attention on a
+    # second stream while the next piece is selected, gives the sequential
+    # step's results bit for bit (plain; and with the indexer transforms, YaRN
+    # and paged caches, where every piece also transforms its own queries)
+    b = W.make_prefill(prefix=40001, chunk=333, budget=512, seg=64, n_plant=32, seed=71).to("cuda")
+    r0 = QSARunner(b)
+    r0.step()
+    for parts in (2, 3, 7):
+        print(f"pipelined prefill, {parts} pieces", flush=True)
+        r1 = QSARunner(b)
+        r1.step_pipelined(parts)
+        _sync()
+        _same_results(r0, r1)
+    cfg = dict(transforms=True, yarn=True, paged=256, page_seed=5)
+    r2 = QSARunner(b, **cfg)
+    r2.step()
+    r3 = QSARunner(b, **cfg)
+    r3.step_pipelined(4)
+    _sync()
+    _same_results(r2, r3)
+
+
 def test_paged_decode_shared_prefix():
     # sequence 1 starts with sequence 0's first 16,384 tokens and maps them to
     # the same 64 physical pages (a prefix-cache hit); ragged lengths
@@ -633,6 +656,15 @@ def test_full_size_chunked_prefill_1m_sampled_rows():
     _sync()
     kinds, worst = _check_rows(r, OracleView(b), rows)
     print("1M prefill, plain:", kinds, f"worst rel-L2 {worst:.2e}", flush=True)
+    # the benchmark's timed step runs the rows in 4 overlapped pieces
+    seq = (r.sel.clone(), r.sel_count.clone(), r.out.clone(), r.lse.clone())
+    r.sel.zero_(); r.out.zero_()
+    r.step_pipelined(4)
+    _sync()
+    assert torch.equal(seq[0], r.sel) and torch.equal(seq[1], r.sel_count)
+    assert torch.equal(seq[2].view(torch.int16), r.out.view(torch.int16))
+    assert torch.equal(seq[3].view(torch.int32), r.lse.view(torch.int32))
+    del seq
     del r
     torch.cuda.empty_cache()
     # the pages' configuration: indexer transforms and YaRN, over paged caches

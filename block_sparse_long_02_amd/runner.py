@@ -173,12 +173,17 @@ class QSARunner:
         """One prefill step with the chunk's query rows in `parts` consecutive
         pieces: piece i's attention runs on a second stream while piece i+1
         is selected, so the memory-bound attention overlaps the MFMA-bound
-        score GEMM.  Same calls on the same rows, so the same results as
-        step().  One-sequence prefill batches only."""
+        score GEMM.  The first piece is an eighth of the rows, so that the
+        attention starts early; the rest are equal.  Same calls on the same
+        rows, so the same results as step().  One-sequence prefill batches
+        only."""
         assert not (self.decode or self.mtp) and self.n_seq == 1, "one-sequence prefill"
         key = ("pipe", parts)
         if getattr(self, "_pipe_key", None) != key:
-            bounds = [self.n_q * i // parts for i in range(parts + 1)]
+            n = self.n_q
+            first = (n + 7) // 8 if parts > 1 else n
+            bounds = [0] + [first + (n - first) * i // (parts - 1) for i in range(parts)] \
+                if parts > 1 else [0, n]
             self._pipe_parts = [self._rows(a, c) for a, c in zip(bounds[:-1], bounds[1:]) if c > a]
             self._pipe_streams = (torch.cuda.Stream(), torch.cuda.Stream())
             self._pipe_key = key

@@ -675,6 +675,30 @@ def test_full_size_chunked_prefill_1m_sampled_rows():
     print("1M prefill, transforms + YaRN, paged:", kinds, f"worst rel-L2 {worst:.2e}")
 
 
+def test_max_context_4m_tokens():
+    # the ABI's longest sequence (2^22 tokens; 2^20 candidate blocks): a
+    # 1,024-row prefill chunk ending one token short of it (log-uniform
+    # planting, sampled rows), then decode rows at 2^22 - 1 tokens (one with
+    # near ties) beside a 3-token sequence
+    L = (1 << 22) - 1
+    b = W.make_prefill(prefix=L - 1024, chunk=1024, budget=512, seg=512, n_plant=64, seed=90,
+                       device="cuda", distance="loguniform")
+    r = QSARunner(b)
+    r.step()
+    _sync()
+    kinds, worst = _check_rows(r, OracleView(b), [0, 1, 511, 512, 1022, 1023])
+    print("4M-token prefill chunk:", kinds, f"worst rel-L2 {worst:.2e}", flush=True)
+    del r, b
+    torch.cuda.empty_cache()
+    b = W.make_decode(seq_lens=[L, 3, L - 2], budget=512, n_plant=32, seed=91,
+                      near_tie=[False, False, True], device="cuda")
+    r = QSARunner(b)
+    r.step()
+    _sync()
+    kinds, worst = _check_rows(r, OracleView(b), [0, 1, 2])
+    print("4M-token decode:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
 def test_full_size_decode_128k_sampled_rows():
     # 32 sequences x (131,072 + 1) tokens, as benchmarked (also replayed from
     # a graph there; the graph test covers replays)

@@ -252,8 +252,8 @@ __device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float c) {
   asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
   return d;
 }
-// pending pre-filter passes per row and workgroup: as many as the LDS of two
-// 8-wave (three 4-wave) workgroups per CU holds
+// pending pre-filter passes per row and workgroup: 32 for 8-wave workgroups
+// (the most that two per CU leave room for), 24 for 4-wave ones
 template <int NW>
 constexpr int kPending = NW == 8 ? 32 : 24;
 

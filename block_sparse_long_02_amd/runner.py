@@ -15,6 +15,16 @@ from . import qsa
 from .workloads import QSABatch, R, v_cache_layout
 
 
+def piece_bounds(n: int, parts: int) -> list[int]:
+    """Row boundaries [0, ..., n] of a chunk cut into `parts` consecutive
+    pieces: the first an eighth of the rows, the rest equal (some pieces may
+    be empty when n < parts)."""
+    if parts <= 1:
+        return [0, n]
+    first = (n + 7) // 8
+    return [0] + [first + (n - first) * i // (parts - 1) for i in range(parts)]
+
+
 class QSARunner:
     def __init__(self, batch: QSABatch, decode: bool | None = None, transforms: bool = False,
                  gamma_k=None, gamma_q=None, eps: float = 1e-6, yarn: bool = False,
@@ -180,10 +190,7 @@ class QSARunner:
         assert not (self.decode or self.mtp) and self.n_seq == 1, "one-sequence prefill"
         key = ("pipe", parts)
         if getattr(self, "_pipe_key", None) != key:
-            n = self.n_q
-            first = (n + 7) // 8 if parts > 1 else n
-            bounds = [0] + [first + (n - first) * i // (parts - 1) for i in range(parts)] \
-                if parts > 1 else [0, n]
+            bounds = piece_bounds(self.n_q, parts)
             self._pipe_parts = [self._rows(a, c) for a, c in zip(bounds[:-1], bounds[1:]) if c > a]
             self._pipe_streams = (torch.cuda.Stream(), torch.cuda.Stream())
             self._pipe_key = key

@@ -227,3 +227,15 @@ def test_probe_library_exports_and_validates():
     assert P.qsa_probe_gather(ALIGNED, 1 << 20, None, 16, 2048, 8, ALIGNED, None) == 1
     assert P.qsa_probe_gather(ALIGNED, 1 << 20, ALIGNED, 0, 2048, 8, ALIGNED, None) == 1
     assert P.qsa_probe_gather(ALIGNED, 1 << 40, ALIGNED, 16, 16, 8, ALIGNED, None) == 2
+
+
+def test_pipeline_piece_bounds():
+    """The overlapped prefill schedule covers every row once, in order, with
+    a short first piece."""
+    from block_sparse_long_02_amd.runner import piece_bounds
+    for n in (1, 3, 7, 8, 333, 32768):
+        for parts in (1, 2, 3, 4, 7):
+            b = piece_bounds(n, parts)
+            assert b[0] == 0 and b[-1] == n and len(b) == max(parts, 1) + 1
+            assert all(x <= y for x, y in zip(b, b[1:]))
+    assert piece_bounds(32768, 4) == [0, 4096, 13653, 23210, 32768]

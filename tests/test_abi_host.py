@@ -239,3 +239,13 @@ def test_pipeline_piece_bounds():
             assert b[0] == 0 and b[-1] == n and len(b) == max(parts, 1) + 1
             assert all(x <= y for x, y in zip(b, b[1:]))
     assert piece_bounds(32768, 4) == [0, 4096, 13653, 23210, 32768]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus above 1 exits with a message before touching a GPU."""
+    import subprocess
+    import sys
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode != 0
+    assert "one GPU" in (res.stdout + res.stderr)

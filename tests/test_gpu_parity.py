@@ -656,7 +656,7 @@ def test_full_size_chunked_prefill_1m_sampled_rows():
     _sync()
     kinds, worst = _check_rows(r, OracleView(b), rows)
     print("1M prefill, plain:", kinds, f"worst rel-L2 {worst:.2e}", flush=True)
-    # the benchmark's timed step runs the rows in 4 overlapped pieces
+    # the benchmark also times the step as 4 overlapped row pieces
     seq = (r.sel.clone(), r.sel_count.clone(), r.out.clone(), r.lse.clone())
     r.sel.zero_(); r.out.zero_()
     r.step_pipelined(4)

@@ -169,9 +169,13 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     const u32x4 v = ldg16(qrow + 32 * ks);
     qf[ks] = col < kGroup ? v : u32x4{0, 0, 0, 0};
   }
+  // The rotated dims 0..63 are carried as two bf16 terms (value and
+  // residual), so the rotation adds no bf16 rounding to the logits; dims
+  // 64..255 are the bf16 inputs themselves.
+  u32x4 ql[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
   {
     // rotate-half on dims 0..63: pair j = 8*grp + e sits in qf[0] (x1) and qf[1] (x2)
-    u32x4 r0, r1;
+    u32x4 r0, r1, l0, l1;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       float y1[2], y2[2];
@@ -185,8 +189,10 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
       }
       r0[w] = pack_bf16x2(y1[0], y1[1]);
       r1[w] = pack_bf16x2(y2[0], y2[1]);
+      l0[w] = pack_bf16x2(y1[0] - bf16_lo(r0[w]), y1[1] - bf16_hi(r0[w]));
+      l1[w] = pack_bf16x2(y2[0] - bf16_lo(r1[w]), y2[1] - bf16_hi(r1[w]));
     }
-    if (col < kGroup) { qf[0] = r0; qf[1] = r1; }
+    if (col < kGroup) { qf[0] = r0; qf[1] = r1; ql[0] = l0; ql[1] = l1; }
   }
 
   for (int t = t_begin; t < t_end; ++t) {
@@ -202,6 +208,8 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         sc[hv] = mfma_16x16x32(kh[hv][ks], qf[ks], sc[hv]);
+      sc[hv] = mfma_16x16x32(kh[hv][0], ql[0], sc[hv]);
+      sc[hv] = mfma_16x16x32(kh[hv][1], ql[1], sc[hv]);
     }
     float x[4 * kHalves];
 #pragma unroll
@@ -257,12 +265,15 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     l_run += ps;
 
     {
-      // P k-slice of 8 tokens (2 micro-blocks) per lane: MFMA 16x16x32
-      u32x4 pa;
-      pa[0] = pack_bf16x2(p[0], p[1]);
-      pa[1] = pack_bf16x2(p[2], p[3]);
-      pa[2] = pack_bf16x2(p[4], p[5]);
-      pa[3] = pack_bf16x2(p[6], p[7]);
+      // P k-slice of 8 tokens (2 micro-blocks) per lane: MFMA 16x16x32.  P
+      // goes in as two bf16 terms (value and residual), so the product with
+      // V carries no bf16 rounding of the weights.
+      u32x4 pa, pl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pa[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+        pl[e] = pack_bf16x2(p[2 * e] - bf16_lo(pa[e]), p[2 * e + 1] - bf16_hi(pa[e]));
+      }
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         // dims 32c + 2*col (even tile) and 32c + 2*col + 1 (odd tile)
@@ -270,6 +281,8 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
         u32x4 bo = {vh[0][c][2], vh[0][c][3], vh[1][c][2], vh[1][c][3]};
         o[2 * c] = mfma_16x16x32(pa, be, o[2 * c]);
         o[2 * c + 1] = mfma_16x16x32(pa, bo, o[2 * c + 1]);
+        o[2 * c] = mfma_16x16x32(pl, be, o[2 * c]);
+        o[2 * c + 1] = mfma_16x16x32(pl, bo, o[2 * c + 1]);
       }
     }
   }

@@ -266,7 +266,7 @@ def make_decode(*, seq_lens, budget: int, n_plant: int, seed: int, device="cpu",
                                     dtype=torch.float32)
         u = _unit((w[s].double()[:, None] * idx_q_bf[s].double()).sum(0).cpu())
         n_c = lens[s] // R
-        if near_tie[s]:
+        if near_tie[s] and n_c > 0:
             n_t = min(tie_count + 1, n_c)
             blocks = sorted(torch.randperm(n_c, generator=gh)[:n_t].tolist())
             low = int(torch.randint(0, max(1, n_t - 1), (), generator=gh))

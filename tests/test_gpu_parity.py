@@ -770,3 +770,57 @@ def test_small_budget_decode():
     b = W.make_decode(seq_lens=[131073, 20001, 4099, 17], budget=16, n_plant=8, seed=92)
     kinds, worst = _end_to_end(b, range(4))
     print("decode, budget 16:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_randomized_parity_sweep():
+    # 40 seeded random batches: one-sequence prefill chunks (prefix 0 to 300K,
+    # 1 to 3,000 rows), decode (1 to 6 sequences of 1 to 400K tokens, some
+    # with near ties) and multi-token decode (1 to 4 rows per sequence), with
+    # budgets from 1 to 512, contiguous or paged caches, with and without the
+    # indexer transforms and YaRN; sampled rows against the oracle, and the
+    # overlapped-pieces prefill against the sequential one
+    import random
+    for c in range(40):
+        rng = random.Random(7100 + c)
+        kind = rng.choice(["prefill", "prefill", "decode", "mtp"])
+        budget = rng.choice([1, 7, 16, 100, 512, 512])
+        paged = rng.choice([None, None, 256, 1024])
+        transforms = rng.random() < 0.3
+        yarn = rng.random() < 0.2
+        if kind == "prefill":
+            prefix = rng.choice([0, rng.randint(1, 5000), rng.randint(5000, 300000)])
+            chunk = rng.randint(1, 3000)
+            b = W.make_prefill(prefix=prefix, chunk=chunk, budget=budget,
+                               seg=rng.choice([64, 512]), n_plant=rng.choice([8, 32]),
+                               seed=7100 + c, device="cuda",
+                               distance=rng.choice(["uniform", "loguniform"]))
+            desc = f"prefill prefix={prefix} chunk={chunk}"
+        elif kind == "decode":
+            lens = [rng.choice([rng.randint(1, 64), rng.randint(64, 20000), rng.randint(20000, 400000)])
+                    for _ in range(rng.randint(1, 6))]
+            b = W.make_decode(seq_lens=lens, budget=budget, n_plant=16, seed=7100 + c,
+                              device="cuda", near_tie=[rng.random() < 0.3 for _ in lens])
+            desc = f"decode {lens}"
+        else:
+            q_len = rng.randint(1, 4)
+            lens = [rng.choice([rng.randint(q_len, 64), rng.randint(64, 20000),
+                                rng.randint(20000, 300000)]) for _ in range(rng.randint(1, 5))]
+            b = W.make_mtp_decode(seq_lens=lens, q_len=q_len, budget=budget, n_plant=16,
+                                  seed=7100 + c, device="cuda")
+            desc = f"mtp q_len={q_len} {lens}"
+        print(f"case {c}: {desc} budget={budget} paged={paged} transforms={transforms} yarn={yarn}",
+              flush=True)
+        r = QSARunner(b, transforms=transforms, yarn=yarn, paged=paged, page_seed=c)
+        r.step()
+        _sync()
+        rows = sorted({0, b.n_q - 1} | {rng.randrange(b.n_q) for _ in range(4)})
+        _check_rows(r, OracleView(b, transforms=transforms, yarn=yarn), rows)
+        if kind == "prefill" and b.n_q >= 2:
+            seq = (r.sel.clone(), r.sel_count.clone(), r.out.clone(), r.lse.clone())
+            r.step_pipelined(rng.randint(2, 5))
+            _sync()
+            assert torch.equal(seq[0], r.sel) and torch.equal(seq[1], r.sel_count)
+            assert torch.equal(seq[2].view(torch.int16), r.out.view(torch.int16))
+            assert torch.equal(seq[3].view(torch.int32), r.lse.view(torch.int32))
+        del r, b
+        torch.cuda.empty_cache()

@@ -339,7 +339,7 @@ def rope(x: np.ndarray, pos, inv_freq=None) -> np.ndarray:
 
 
 def attend(q_i: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, tokens: np.ndarray,
-           i: int, inv_freq=None, scale=None):
+           i: int, inv_freq=None, scale=None, k_bf16: bool = False):
     """Exact GQA softmax attention of query i over the token set S_i.
 
     [ailearn] §03 fifth QSA step: the 24-query / 2-KV core attends exactly over
@@ -351,10 +351,17 @@ def attend(q_i: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, tokens: np.n
     [len(tokens)][2][256] the raw cache rows of those tokens (K not rotated).
     Returns (O [24][256], lse [24]) in float64, lse = log sum exp of the
     scaled logits.
+
+    k_bf16=True rounds the rotated keys to bf16 (through float32): the
+    values of a K cache that stores each key once, rotated at its position,
+    in bf16 (the cache format read from the same step; a bf16 cache of raw
+    keys would instead leave k_bf16 False).
     """
     S = np.asarray(tokens, dtype=np.int64)
     qr = rope(np.asarray(q_i, dtype=np.float64), i, inv_freq)
     kr = rope(np.asarray(k_rows, dtype=np.float64), S[:, None], inv_freq)     # [n][2][256]
+    if k_bf16:
+        kr = _to_bf16_via_f32(kr)
     sm = SOFTMAX_SCALE if scale is None else float(scale)
     vs = np.asarray(v_rows, dtype=np.float64)                       # [n][2][256]
     assert kr.shape[0] == S.shape[0] and vs.shape[0] == S.shape[0]

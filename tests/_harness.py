@@ -68,7 +68,9 @@ class OracleView:
         s, p = self.seq[row], self.pos[row]
         tokens = O.sparse_token_set(np.asarray(blocks, dtype=np.int64), p)
         k, v = self.rows(s, tokens)
-        return O.attend(np64(self.b.q[row]), k, v, tokens, p, self.inv_freq, self.scale)
+        # the library's K cache holds each key rotated at its position, in bf16
+        return O.attend(np64(self.b.q[row]), k, v, tokens, p, self.inv_freq, self.scale,
+                        k_bf16=True)
 
     def dense(self, row):
         """Textbook causal GQA over every token 0..pos (for budget >= n_c)."""

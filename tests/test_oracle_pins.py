@@ -543,3 +543,31 @@ def test_oracle_attend_scale_is_a_logit_multiplier():
     # (by a multiple of 4, so the block structure is unchanged) keeps the output
     o6, _ = O.attend(q, k, v, S + 4000, 12 + 4000, inv_freq=f)
     assert np.allclose(o5, o6, rtol=1e-9, atol=1e-9)
+
+
+def test_oracle_attend_bf16_key_cache():
+    # k_bf16 rounds the rotated keys the way a bf16 cache of rotated keys
+    # stores them.  Keys with nothing in the rotated dims and bf16 values in
+    # the others are stored exactly, so the flag changes nothing; keys at
+    # position 0 are not rotated, so bf16 keys there are stored exactly too.
+    rng = np.random.default_rng(44)
+    q, v = rng.standard_normal((24, 256)), rng.standard_normal((9, 2, 256))
+    k = O.round_to_bf16(rng.standard_normal((9, 2, 256)))
+    S = np.array([0, 1, 2, 3, 8, 9, 10, 11, 12])
+    k0 = k.copy()
+    k0[..., :64] = 0.0
+    a, la = O.attend(q, k0, v, S, 12)
+    b, lb = O.attend(q, k0, v, S, 12, k_bf16=True)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    a, _ = O.attend(q, k[:1], v[:1], S[:1], 12)
+    b, _ = O.attend(q, k[:1], v[:1], S[:1], 12, k_bf16=True)
+    assert np.array_equal(a, b)
+    # rotated keys are generally not bf16 values: the flag moves the logits by
+    # at most the bf16 rounding of each rotated key element (2^-9 relative)
+    a, la = O.attend(q, k, v, S, 12)
+    b, lb = O.attend(q, k, v, S, 12, k_bf16=True)
+    assert not np.array_equal(la, lb)
+    kr = O.rope(k, S[:, None])
+    qr = O.rope(q, 12)
+    bound = np.abs(kr[:, :, :64]).max() * 2.0 ** -9 * np.abs(qr[:, :64]).sum(1).max() / 16.0
+    assert np.abs(la - lb).max() <= bound

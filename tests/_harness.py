@@ -107,12 +107,25 @@ def check_selection(view: OracleView, row: int, gpu_ids, gpu_count: int, exact: 
     return "near"
 
 
+def max_abs_bound(ref_out):
+    """Per-element max-abs bound on a bf16 output: MAX_ABS, except where half
+    a bf16 ulp of the exact value already exceeds it (|x| >= 4, where bf16
+    values lie 2^-5 or more apart).  There no bf16 output can meet MAX_ABS,
+    and the bound is one ulp: the output must be one of the two bf16 values
+    around the exact one, up to the float32 arithmetic before the rounding."""
+    a = np.abs(np.asarray(ref_out, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    ulp = np.exp2(e - 7.0)
+    return np.where(ulp / 2 > MAX_ABS, ulp, MAX_ABS)
+
+
 def check_attention(gpu_out, gpu_lse, ref_out, ref_lse, label=""):
     """Max-abs and relative-L2 bounds on one row's [24][256] output."""
     o = np64(gpu_out)
     err = np.abs(o - ref_out)
     assert np.isfinite(o).all(), label
-    assert err.max() <= MAX_ABS, (label, err.max())
+    bound = max_abs_bound(ref_out)
+    assert (err <= bound).all(), (label, err.max(), float(np.abs(ref_out).max()))
     rel = np.linalg.norm(o - ref_out) / np.linalg.norm(ref_out)
     assert rel <= REL_L2, (label, rel)
     if gpu_lse is not None:

@@ -249,3 +249,13 @@ def test_bench_refuses_more_than_one_gpu():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode != 0
     assert "one GPU" in (res.stdout + res.stderr)
+
+
+def test_attention_max_abs_bound():
+    # 1e-2 wherever a bf16 output can meet it; one bf16 ulp where half an ulp
+    # alone exceeds 1e-2 (magnitudes of 4 and more)
+    import numpy as np
+    from tests._harness import max_abs_bound
+    x = np.array([0.0, 1e-30, 0.5, 1.999, 2.0, 3.99, 4.0, -5.5, 7.99, 8.0, -100.0])
+    want = np.array([1e-2] * 6 + [2.0 ** -5, 2.0 ** -5, 2.0 ** -5, 2.0 ** -4, 2.0 ** -1])
+    assert np.array_equal(max_abs_bound(x), want)

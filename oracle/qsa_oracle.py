@@ -50,7 +50,12 @@ representable in bf16 (the caller decodes bf16 losslessly).
 
 Parity pins: every function here is checked against facts that do not come
 from this file (closed forms, invariants, brute force, library routines); see
-the tests whose names start with test_oracle_.
+the tests whose names start with test_oracle_.  Two functions are comparison
+allowances rather than steps of the method, and are pinned the same way:
+selection_gap (a hand-worked boundary gap and allowance, and the allowance
+against float32 scores summed in other orders) and attend_error_bound
+(brute force over bf16-rounded and worst-case perturbed keys, and a
+two-token case where it is nearly reached).
 """
 from __future__ import annotations
 
@@ -354,8 +359,9 @@ def attend(q_i: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, tokens: np.n
 
     k_bf16=True rounds the rotated keys to bf16 (through float32): the
     values of a K cache that stores each key once, rotated at its position,
-    in bf16 (the cache format read from the same step; a bf16 cache of raw
-    keys would instead leave k_bf16 False).
+    in bf16.  The method's result is k_bf16=False (exact rotated keys);
+    k_bf16=True gives the exact attention over such a cache's stored values,
+    for checking a kernel that is handed that cache.
     """
     S = np.asarray(tokens, dtype=np.int64)
     qr = rope(np.asarray(q_i, dtype=np.float64), i, inv_freq)
@@ -414,6 +420,87 @@ def selection_gap(scores: np.ndarray, q_i, w_i, kbar, budget: int):
     mag = (np.asarray(w_i, np.float64)[:, None] * absdots).sum(0) / np.sqrt(128.0)
     delta = 2.0 ** -15 * (mag.max() if mag.size else 0.0)
     return gap, delta, s_k
+
+
+# Error model of an attention that reads a bf16 cache of rotated keys and
+# computes in float32 (used by attend_error_bound).
+BF16_U = 2.0 ** -8       # bf16 unit roundoff: |bf16(x) - x| <= 2^-8 |x| (8-bit significand, RNE)
+F32_ROTATION = 2.0 ** -21   # float32 cos/sin and rotation, relative to |x_j| + |x_{j+32}|
+F32_LOGIT = 2.0 ** -14      # float32 logits, relative to sum_d |q_d k_d| (256 terms, 4x slack)
+F32_WEIGHTED_SUM = 2.0 ** -12   # float32 softmax weights and sum_j p_j v_j, relative to sum_j p_j |v_j|
+
+
+def k_cache_rounding_allowance(k_rows: np.ndarray, tokens: np.ndarray, inv_freq=None) -> np.ndarray:
+    """Per-element bound on |stored key - exact rotated key| for a cache that
+    stores each key rotated at its position in bf16 ([ailearn] §03: the fifth
+    QSA step attends over the original tokens, the second rotates 64 dims).
+
+    Rotated dims (pair j, j+32) go through float32 cos/sin and arithmetic,
+    then bf16 RNE:  e_d = 2^-8 |k~_d| + 2^-21 (|k_j| + |k_{j+32}|), with k~
+    the exact rotation and k the raw key; dims 64..255 are stored as given
+    (e = 0).  k_rows: raw keys [n][2][256] at positions `tokens`.
+    """
+    S = np.asarray(tokens, dtype=np.int64)
+    k = np.asarray(k_rows, dtype=np.float64)
+    kr = rope(k, S[:, None], inv_freq)
+    e = np.zeros_like(kr)
+    h = D_ROPE // 2
+    pair = np.abs(k[..., :h]) + np.abs(k[..., h:D_ROPE])            # |x_j| + |x_{j+32}|
+    e[..., :h] = BF16_U * np.abs(kr[..., :h]) + F32_ROTATION * pair
+    e[..., h:D_ROPE] = BF16_U * np.abs(kr[..., h:D_ROPE]) + F32_ROTATION * pair
+    return e
+
+
+def attend_error_bound(q_i: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray,
+                       tokens: np.ndarray, i: int, inv_freq=None, scale=None,
+                       k_stored: bool = False):
+    """Per-element bound on how far an attention computed from a bf16 cache of
+    rotated keys, in float32, can sit from attend()'s float64 result (before
+    the output's own bf16 rounding).  Not a step of the method: the tolerance
+    the parity tests derive from the cache format.
+
+    Stored key element d differs from the exact rotated one by at most e_d
+    (k_cache_rounding_allowance); with k_stored=True the reference itself
+    attends over the stored values (attend(k_bf16=True)) and e = 0.  Logit t
+    of head h then moves by eps_t, |eps_t| <= beta_t with
+        beta_t = c * ( sum_{d<64} |q~_d| e_td + 2^-14 sum_d |q~_d| |k~_td| ),
+    the second term for float32 dot products.  The weights become
+    p'_t = p_t exp(eps_t - L), L = log sum_u p_u exp(eps_u) in [L-, L+] =
+    [log sum_u p_u exp(-beta_u), log sum_u p_u exp(beta_u)], so
+        |p'_t / p_t - 1| <= r_t = max(exp(beta_t - L-) - 1, 1 - exp(-beta_t - L+)),
+    and since sum_t (p'_t - p_t) = 0, for every dim
+        |O' - O| <= sum_t p_t r_t |v_t - O| + 2^-12 sum_t p_t |v_t|,
+    the last term for float32 weights and accumulation.  lse moves by L:
+    at most max(L+, -L-) plus the same float32 slack.
+
+    Same arguments as attend().  Returns (bound [24][256], lse_bound [24]).
+    """
+    S = np.asarray(tokens, dtype=np.int64)
+    qr = rope(np.asarray(q_i, dtype=np.float64), i, inv_freq)
+    kr = rope(np.asarray(k_rows, dtype=np.float64), S[:, None], inv_freq)   # [n][2][256]
+    if k_stored:
+        kr = _to_bf16_via_f32(kr)
+        ek = np.zeros_like(kr)
+    else:
+        ek = k_cache_rounding_allowance(k_rows, S, inv_freq)
+    sm = SOFTMAX_SCALE if scale is None else float(scale)
+    vs = np.asarray(v_rows, dtype=np.float64)
+    bound = np.empty((H_Q, D), dtype=np.float64)
+    lse_bound = np.empty(H_Q, dtype=np.float64)
+    for hq in range(H_Q):
+        g = hq // GROUP
+        aq = np.abs(qr[hq])
+        logits = (kr[:, g, :] @ qr[hq]) * sm
+        beta = sm * (ek[:, g, :] @ aq + F32_LOGIT * (np.abs(kr[:, g, :]) @ aq))
+        p = np.exp(logits - logits.max())
+        p /= p.sum()
+        o = p @ vs[:, g, :]
+        l_hi = np.log(p @ np.exp(beta))
+        l_lo = np.log(p @ np.exp(-beta))
+        r = np.maximum(np.expm1(beta - l_lo), -np.expm1(-beta - l_hi))
+        bound[hq] = (p * r) @ np.abs(vs[:, g, :] - o) + F32_WEIGHTED_SUM * (p @ np.abs(vs[:, g, :]))
+        lse_bound[hq] = max(l_hi, -l_lo) + F32_WEIGHTED_SUM
+    return bound, lse_bound
 
 
 def dense_causal_gqa(q_i: np.ndarray, k_raw: np.ndarray, v: np.ndarray, i: int):

@@ -42,6 +42,8 @@ def test_pool_bit_exact_and_bounded():
     n_seq, cap = 3, 1024
     idx_k = torch.randn(n_seq, cap, 128, generator=g).to(torch.bfloat16)
     idx_k[1, :8] = torch.tensor([16777216.0, 1.0, -16777216.0, 1.0] * 2).to(torch.bfloat16)[:, None]
+    # token order and a pairwise tree round this block differently (0 against 0.25)
+    idx_k[1, 8:12] = torch.tensor([1.0, 16777216.0, 1.0, -16777216.0]).to(torch.bfloat16)[:, None]
     begin, end = [0, 0, 100], [256, 77, 101]
     sentinel = torch.full((n_seq, cap // 4, 128), 0x1234, dtype=torch.int16)
     for max_span in (256, 16):            # 16: fewer workgroups than blocks
@@ -55,8 +57,10 @@ def test_pool_bit_exact_and_bounded():
             ref_bits = ref.to(torch.bfloat16).view(torch.int16).numpy()
             assert np.array_equal(got[s, begin[s]:end[s]], ref_bits[begin[s]:end[s]]), (s, max_span)
             assert np.all(got[s, :begin[s]] == 0x1234) and np.all(got[s, end[s]:] == 0x1234)
-    # the order-of-addition case: 2^24 + 1 - 2^24 + 1 pools to 0.25
+    # the order-of-addition cases: 2^24 + 1 - 2^24 + 1 pools to 0.25, and
+    # 1 + 2^24 + 1 - 2^24 to 0 (a pairwise tree would give 0.25)
     assert float(bk[1, 0, 0].float()) == 0.25
+    assert float(bk[1, 2, 0].float()) == 0.0
 
 
 # --------------------------------------------------------------------- RoPE
@@ -140,8 +144,9 @@ def test_attend_prefill_on_oracle_selection_tiny():
     _sync()
     worst = 0.0
     for row in range(b.n_q):
-        ref_o, ref_l = view.attend(row, chosen[row])
-        e, rel = check_attention(r.out[row], r.lse[row], ref_o, ref_l, f"row {row}")
+        # the attention's stated input is the stored (bf16, rotated) K cache
+        e, rel, _ = check_attention(r.out[row], r.lse[row],
+                                    view.attend(row, chosen[row], k_stored=True), f"row {row}")
         worst = max(worst, rel)
     print(f"tiny prefill attention: worst rel-L2 {worst:.2e}")
 
@@ -154,10 +159,10 @@ def test_attend_decode_on_oracle_selection():
     r.attend()
     _sync()
     for row in range(b.n_q):
-        ref_o, ref_l = view.attend(row, chosen[row])
-        check_attention(r.out[row], r.lse[row], ref_o, ref_l, f"decode row {row}")
-    # the workspace's arrival counters stay valid across calls of different
-    # sizes: a call on the first 2 sequences, then all 5 again
+        check_attention(r.out[row], r.lse[row], view.attend(row, chosen[row], k_stored=True),
+                        f"decode row {row}")
+    # calls of different sizes on one workspace: the first 2 sequences, then
+    # all 5 again
     out_all = r.out.clone()
     qsa.attend_decode(r.b.q[:2], r.b.seq_len[:2], r.k_cache, r.v_cache, r.sel[:2],
                       r.sel_count[:2], r.budget, r.out[:2], r.lse[:2], r.ws_decode)
@@ -301,6 +306,37 @@ def test_index_select_fallback_short_list():
     assert np.array_equal(r.sel.cpu().numpy()[0], np.arange(0, 8192, 16))
 
 
+def test_index_select_prefill_fallback_all_ties():
+    # the prefill path (more than 4 rows per sequence, more than 4096
+    # candidates): identical block keys make every score tie, the filtered
+    # list overflows, and the exact fallback that recomputes the scores must
+    # keep the lowest 512 block ids of every row
+    b = W.make_prefill(prefix=20000, chunk=40, budget=512, seg=64, n_plant=0, seed=33,
+                       exact_grid=True)
+    b.idx_k[:] = b.idx_k[0, 0].clone()
+    r, _, _ = _select_and_check(b, exact=True)
+    sel = r.sel.cpu().numpy()
+    assert all(np.array_equal(sel[row], np.arange(512)) for row in range(b.n_q))
+
+
+def test_index_select_prefill_fallback_short_list():
+    # the prefill path: only the blocks the sample pass scores (every 32nd)
+    # score high, so the sampled threshold lets fewer than K blocks through
+    # and the exact fallback takes over.  Exact-grid inputs: the fallback's
+    # float32 dot products (dims in order) then equal the oracle's scores,
+    # and the rest of the selection is decided among the low blocks
+    b = W.make_prefill(prefix=20000, chunk=40, budget=512, seg=64, n_plant=0, seed=34,
+                       exact_grid=True)
+    u = torch.sign(b.idx_q.float().sum((0, 1)))
+    n_c = 20000 // 4
+    for blk in range(0, n_c, 32):
+        b.idx_k[0, 4 * blk:4 * blk + 4] = (2.0 * u).to(torch.bfloat16)
+    r, _, _ = _select_and_check(b, exact=True)
+    sel = r.sel.cpu().numpy()
+    high = set(range(0, n_c, 32))
+    assert all(high <= set(sel[row].tolist()) for row in range(b.n_q))
+
+
 # ------------------------------------------------- indexer transforms (pages)
 
 def _rand_bf16(g, shape):
@@ -418,15 +454,13 @@ def _end_to_end(b, rows, dense=False, yarn=False, transforms=False):
     r.step()
     _sync()
     sel, cnt = r.sel.cpu().numpy(), r.sel_count.cpu().numpy()
-    kinds = {"exact": 0, "near": 0}
+    kinds = {"exact": 0, "near": 0, "rows_over_1e-2": 0}
     worst = 0.0
     for row in rows:
         kinds[check_selection(view, row, sel[row], int(cnt[row]))] += 1
-        if dense:
-            ref_o, ref_l = view.dense(row)
-        else:
-            ref_o, ref_l = view.attend(row, sel[row][:cnt[row]])
-        _, rel = check_attention(r.out[row], r.lse[row], ref_o, ref_l, f"row {row}")
+        ref = view.dense(row) if dense else view.attend(row, sel[row][:cnt[row]])
+        _, rel, n_over = check_attention(r.out[row], r.lse[row], ref, f"row {row}")
+        kinds["rows_over_1e-2"] += n_over > 0
         worst = max(worst, rel)
     return kinds, worst
 
@@ -500,11 +534,13 @@ def _same_results(a, b):
 
 def _check_rows(r, view, rows):
     sel, cnt = r.sel.cpu().numpy(), r.sel_count.cpu().numpy()
-    kinds, worst = {"exact": 0, "near": 0}, 0.0
+    kinds, worst = {"exact": 0, "near": 0, "rows_over_1e-2": 0}, 0.0
     for row in rows:
         kinds[check_selection(view, row, sel[row], int(cnt[row]))] += 1
-        ref_o, ref_l = view.attend(row, sel[row][:cnt[row]])
-        worst = max(worst, check_attention(r.out[row], r.lse[row], ref_o, ref_l, f"row {row}")[1])
+        _, rel, n_over = check_attention(r.out[row], r.lse[row],
+                                         view.attend(row, sel[row][:cnt[row]]), f"row {row}")
+        kinds["rows_over_1e-2"] += n_over > 0
+        worst = max(worst, rel)
     return kinds, worst
 
 
@@ -673,6 +709,25 @@ def test_full_size_chunked_prefill_1m_sampled_rows():
     _sync()
     kinds, worst = _check_rows(r, OracleView(b, transforms=True, yarn=True), rows[:8])
     print("1M prefill, transforms + YaRN, paged:", kinds, f"worst rel-L2 {worst:.2e}")
+
+
+def test_full_size_chunked_prefill_1m_exact_grid():
+    # the benchmark's 1M chunk in its launch configuration, on exact-grid
+    # indexer inputs: every float32 score is exact in any summation order, so
+    # the sampled-threshold selection must equal the oracle's bit for bit on
+    # every checked row (no allowance branch)
+    b = W.chunked_prefill_1m(device="cuda", exact_grid=True)
+    rows = _sampled(b.n_q, 12, 83, always=(0, 1, 1023, 1024, b.n_q - 1))
+    r = QSARunner(b)
+    r.step()
+    _sync()
+    view = OracleView(b)
+    sel, cnt = r.sel.cpu().numpy(), r.sel_count.cpu().numpy()
+    for row in rows:
+        assert check_selection(view, row, sel[row], int(cnt[row]), exact=True) == "exact"
+    for row in rows[:4]:
+        check_attention(r.out[row], r.lse[row], view.attend(row, sel[row][:cnt[row]]), f"row {row}")
+    print("1M prefill, exact grid:", len(rows), "rows bit-exact", flush=True)
 
 
 def test_max_context_4m_tokens():

@@ -571,3 +571,182 @@ def test_oracle_attend_bf16_key_cache():
     qr = O.rope(q, 12)
     bound = np.abs(kr[:, :, :64]).max() * 2.0 ** -9 * np.abs(qr[:, :64]).sum(1).max() / 16.0
     assert np.abs(la - lb).max() <= bound
+
+
+# ------------------------------------------ comparison allowances (pinned)
+
+def test_oracle_pool_order_separates_pairwise_tree(golden_dir):
+    # token order ((k0 + k1) + k2) + k3 and a pairwise tree (k0 + k1) + (k2 + k3)
+    # round differently on this block (0 against 0.25)
+    case = json.load(open(os.path.join(golden_dir, "hand_worked_query.json")))["pool_order_pairwise_case"]
+    keys = np.zeros((4, 128))
+    keys[:, 0] = case["tokens"]
+    assert O.pool_block_keys(keys, 1)[0, 0] == case["expected"]
+    assert case["pairwise_tree_would_give"] != case["expected"]
+
+
+def _gap_case(golden_dir):
+    c = json.load(open(os.path.join(golden_dir, "hand_worked_query.json")))["selection_gap_case"]
+    q = np.zeros((4, 128))
+    for h, d, v in c["q_nonzero"]:
+        q[h, d] = v
+    kb = np.zeros((c["n_blocks"], 128))
+    for b, d, v in c["kbar_nonzero"]:
+        kb[b, d] = v
+    return c, q, np.asarray(c["w"], np.float32), kb
+
+
+def test_oracle_selection_gap_hand_worked(golden_dir):
+    # gap = s_(K) - s_(K+1) (not s_(1) - s_(K+1)), s_k = s_(K), and the
+    # allowance from the weighted |q||kbar| sums (weights applied, absolute
+    # values taken, largest block), each against the hand-worked values
+    c, q, w, kb = _gap_case(golden_dir)
+    rs = math.sqrt(128.0)
+    s = O.block_scores(q, w, kb)
+    for case in c["cases"]:
+        gap, delta, s_k = O.selection_gap(s, q, w, kb, case["budget"])
+        if case["gap_times_sqrt128"] == "inf":
+            assert gap == np.inf
+        else:
+            assert gap == pytest.approx(case["gap_times_sqrt128"] / rs, rel=1e-6)
+        assert s_k == pytest.approx(case["s_k_times_sqrt128"] / rs, rel=1e-6, abs=1e-12)
+        assert delta == pytest.approx(c["delta_times_sqrt128_times_2^15"] * 2.0 ** -15 / rs, rel=1e-12)
+
+
+def _f32_dot(q, k, order):
+    """float32 dot product of two bf16 vectors, summed in the given way."""
+    p = (q.astype(np.float32) * k.astype(np.float32)).astype(np.float32)   # exact products
+    if order == "forward":
+        acc = np.float32(0)
+        for x in p:
+            acc = np.float32(acc + x)
+        return acc
+    if order == "backward":
+        return _f32_dot(q[::-1], k[::-1], "forward")
+    if order == "pairwise":
+        v = list(p)
+        while len(v) > 1:
+            v = [np.float32(v[2 * i] + v[2 * i + 1]) for i in range(len(v) // 2)]
+        return v[0]
+    # "blocks": 4 runs of 32 summed separately, then added (a k-split product)
+    parts = [_f32_dot(q[32 * i:32 * i + 32], k[32 * i:32 * i + 32], "forward") for i in range(4)]
+    acc = np.float32(0)
+    for x in parts:
+        acc = np.float32(acc + x)
+    return acc
+
+
+def test_oracle_selection_gap_allowance_covers_float32_orders():
+    # the exact branch of the selection check is sound only if every float32
+    # accumulation order stays within delta/2 of the oracle's score: brute
+    # force over four orders on bf16 inputs of mixed magnitude
+    rng = np.random.default_rng(51)
+    worst = 0.0
+    for trial in range(6):
+        q = O.round_to_bf16(rng.standard_normal((4, 128)) * 10.0 ** rng.uniform(-1, 1, (4, 1)))
+        kb = O.round_to_bf16(rng.standard_normal((40, 128)) * 10.0 ** rng.uniform(-1, 1, (40, 1)))
+        w = np.exp(rng.standard_normal(4)).astype(np.float32)
+        w = (w / w.sum()).astype(np.float32)
+        s = O.block_scores(q, w, kb).astype(np.float64)
+        _, delta, _ = O.selection_gap(s, q, w, kb, 8)
+        for order in ("forward", "backward", "pairwise", "blocks"):
+            for b in range(kb.shape[0]):
+                t = np.array([_f32_dot(q[h], kb[b], order) for h in range(4)], np.float32)
+                u = np.maximum(t, np.float32(0)) * O.SCORE_SCALE
+                acc = np.float32(0)
+                for h in range(4):
+                    acc = np.float32(acc + np.float32(w[h] * u[h]))
+                dev = abs(float(acc) - s[b])
+                worst = max(worst, dev / delta)
+                assert dev <= delta / 2, (trial, order, b, dev, delta)
+    assert worst > 0.0
+
+
+def test_oracle_k_cache_allowance_bounds_bf16_rounding():
+    # the allowance bounds the actual bf16 rounding of rotated keys, and is
+    # nearly reached: position 19591 turns key 1.0078125 in pair 16 into
+    # 1.0039157, which rounds to 1.0078125 with 0.994 of the 2^-8 allowance
+    rng = np.random.default_rng(52)
+    k = O.round_to_bf16(rng.standard_normal((300, 2, 256)) * 10.0 ** rng.uniform(-2, 2, (300, 1, 1)))
+    S = rng.integers(0, 1 << 22, 300)
+    for f in (None, O.yarn_inv_freq()):
+        exact = O.rope(k, S[:, None], f)
+        stored = O.round_to_bf16(exact.astype(np.float32))
+        e = O.k_cache_rounding_allowance(k, S, f)
+        assert (np.abs(stored - exact) <= e).all()
+        assert (e[..., 64:] == 0).all()
+    k1 = np.zeros((1, 2, 256))
+    k1[0, 0, 16] = 1.0078125
+    S1 = np.array([19591])
+    exact = O.rope(k1, S1[:, None])
+    stored = O.round_to_bf16(exact.astype(np.float32))
+    e = O.k_cache_rounding_allowance(k1, S1)
+    err = abs(stored[0, 0, 16] - exact[0, 0, 16])
+    assert 0.98 * e[0, 0, 16] <= err <= e[0, 0, 16]
+
+
+def _perturbed_attention(q, k, v, S, i, eps):
+    """attention with every logit moved by eps[h][t] (brute force)"""
+    qr, kr = O.rope(q, i), O.rope(k, S[:, None])
+    out = np.empty((24, 256))
+    lse = np.empty(24)
+    for h in range(24):
+        g = h // 12
+        z = kr[:, g] @ qr[h] / 16.0 + eps[h]
+        m = z.max()
+        p = np.exp(z - m)
+        out[h] = p @ v[:, g] / p.sum()
+        lse[h] = m + np.log(p.sum())
+    return out, lse
+
+
+def test_oracle_attend_error_bound_holds():
+    # brute force: a bf16 cache of rotated keys (k_bf16=True) and logits moved
+    # by the worst-case amount in random and in adversarial directions all
+    # stay within the bound
+    rng = np.random.default_rng(53)
+    for n, vs in ((1, 1.0), (2, 4.0), (4, 3.0), (7, 1.0), (33, 2.0), (300, 1.0)):
+        q = O.round_to_bf16(rng.standard_normal((24, 256)) * 1.5)
+        k = O.round_to_bf16(rng.standard_normal((n, 2, 256)))
+        v = O.round_to_bf16(rng.standard_normal((n, 2, 256)) * vs)
+        i = int(rng.integers(n, 1 << 20))
+        S = np.sort(rng.choice(i + 1, n, replace=False))
+        ref, ref_l = O.attend(q, k, v, S, i)
+        bound, lbound = O.attend_error_bound(q, k, v, S, i)
+        got, got_l = O.attend(q, k, v, S, i, k_bf16=True)
+        assert (np.abs(got - ref) <= bound).all() and (np.abs(got_l - ref_l) <= lbound).all(), n
+        # the K-rounding part of the logit bound, at its largest, with signs
+        # random or pushing every token's weight up or down
+        qr, e = O.rope(q, i), O.k_cache_rounding_allowance(k, S)
+        beta = np.stack([e[:, h // 12, :64] @ np.abs(qr[h, :64]) / 16.0 for h in range(24)])
+        for sgn in (rng.choice([-1.0, 1.0], beta.shape), np.ones_like(beta), -np.ones_like(beta)):
+            o2, l2 = _perturbed_attention(q, k, v, S, i, sgn * beta)
+            assert (np.abs(o2 - ref) <= bound).all() and (np.abs(l2 - ref_l) <= lbound).all(), n
+
+
+def test_oracle_attend_error_bound_nearly_reached():
+    # two tokens of nearly equal logits and values +-1 in one dim; token 0's
+    # key rounds with 0.994 of its allowance (pair 16 at position 19591),
+    # token 1 has nothing in the rotated dims.  Moving token 0's logit up by
+    # its allowance moves that output by about beta/2, while the bound is
+    # about beta: a bound at least 1.5x too loose, or one that misses the
+    # K rounding, fails one of the two asserts
+    q = np.zeros((24, 256))
+    q[:, 16] = 400.0                       # large rotated query dim: K rounding dominates
+    q[:, 200] = 400.0
+    k = np.zeros((2, 2, 256))
+    k[0, :, 16] = 1.0078125
+    k[1, :, 200] = 1.0                     # logit 25 against token 0's 25.1
+    v = np.zeros((2, 2, 256))
+    v[0, :, 100], v[1, :, 100] = 1.0, -1.0
+    S, i = np.array([19591, 19592]), 19592    # query next to token 0: their rotations nearly cancel
+    ref, _ = O.attend(q, k, v, S, i)
+    bound, _ = O.attend_error_bound(q, k, v, S, i)
+    got, _ = O.attend(q, k, v, S, i, k_bf16=True)         # the stored key, rounded up
+    qr, e = O.rope(q, i), O.k_cache_rounding_allowance(k, S)
+    eps = np.zeros((24, 2))
+    eps[:, 0] = e[0, 0, :64] @ np.abs(qr[0, :64]) / 16.0
+    o2, _ = _perturbed_attention(q, k, v, S, i, eps)
+    moved = abs(o2[0, 100] - ref[0, 100])
+    assert abs(got[0, 100] - ref[0, 100]) >= 0.95 * moved
+    assert moved <= bound[0, 100] <= 3.0 * moved, (moved, bound[0, 100])

@@ -7,7 +7,9 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libqsa.so")
-PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")   # micro-benchmarks, measurement only
+# micro-benchmarks of the achievable MFMA and HBM rates (measurement only,
+# never loaded by the path; built on request by build_probe())
+PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -37,11 +39,17 @@ def _link(srcs, out, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """libqsa.so (the QSA path) and libqsa_probe.so (micro-benchmarks)."""
+    """libqsa.so: the QSA path."""
     _link(sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip"))), LIB, verbose)
-    _link(sorted(glob.glob(os.path.join(PKG, "csrc", "probe", "*.hip"))), PROBE_LIB, verbose)
     return LIB
 
 
+def build_probe(verbose: bool = False) -> str:
+    """libqsa_probe.so: the micro-benchmarks behind measure.py's `peaks`."""
+    _link(sorted(glob.glob(os.path.join(PKG, "csrc", "probe", "*.hip"))), PROBE_LIB, verbose)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build_probe(verbose=True) if "probe" in sys.argv[1:] else build(verbose=True))

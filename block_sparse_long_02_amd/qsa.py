@@ -13,8 +13,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# QSA_LIB may point at another build of the same library (e.g. a variant)
-LIB_PATH = os.environ.get("QSA_LIB") or os.path.join(_PKG, "libqsa.so")
+LIB_PATH = os.path.join(_PKG, "libqsa.so")
 
 QSA_OK = 0
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID_ARG", 2: "QSA_ERR_UNSUPPORTED",

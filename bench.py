@@ -13,20 +13,27 @@ step for 32 sequences of 131,072 cached tokens + the new one; and
 Inputs are seeded synthetic tensors generated directly in HBM; the timed
 region starts with everything resident.  Timing uses HIP events on the stream
 the kernels run on.  `roofline` is for the dominant kernel (the attention
-kernel of the prefill step): algorithmic bytes per launch / its mean
-duration, against 8 TB/s, with the counted HBM-side bytes beside it
-(`traffic`, from profiles/traffic.json while the kernel source is unchanged).
-`rows` gives each hot-path row against its own roofline.  `index_transforms`
+kernel of the prefill step): its algorithmic flops per launch / its mean
+duration against the bf16 MFMA peak, the bound it cannot exceed (its
+zero-reuse gather bytes already exceed the HBM rate, through cache reuse);
+`memory_side` gives the counted bytes beyond L2 (`traffic`, from
+profiles/traffic.json while the kernel source is unchanged) against the
+HBM peak and the measured achievable read rate.  `rows` gives each hot-path
+row against its own roofline.  `prefill_8k` times an 8,192-token prefill
+(and the 2,048-token dense case); `ragged_decode` a decode step of 8
+sequences of log-uniform lengths up to 1M tokens, against that draw's own
+HBM floor.  `index_transforms`
 repeats the prefill step with the pages' indexer transforms (RMSNorm and
 partial RoPE of block keys and queries) and times each transform kernel;
 `yarn` repeats it with the transforms and the YaRN-extended rotations and
 softmax scale (the pages' configuration past the native 262,144 tokens).
 `paged` repeats the prefill and decode steps over caches kept in 256-token
 pages in a random physical order (block tables).
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+`cpu_baseline` times the CPU oracle on a bounded, stratified sample of the same
+workload, with all host threads and with one.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--only prefill|decode|mtp]
+                    [--only prefill|prefill8k|decode|ragged|mtp]
 """
 import argparse
 import hashlib
@@ -82,6 +89,24 @@ def traffic_from_profiles(kernel_file, key):
     return d.get("bytes_per_launch")
 
 
+def achievable_peaks():
+    """Measured achievable rates (profiles/achievable_peaks.json, micro-benchmarks
+    of the MFMA pipe and of HBM reads), or an empty dict."""
+    p = os.path.join(ROOT, "profiles", "achievable_peaks.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return {}
+    out = {}
+    reads = [v["gbs"] for k, v in d.items() if k.startswith("hbm_read_")]
+    mfma = [v["tflops"] for k, v in d.items() if k.startswith("mfma_bf16_")]
+    if reads:
+        out["hbm_read_gbs"] = max(reads)
+    if mfma:
+        out["mfma_bf16_tflops"] = max(mfma)
+    return out
+
+
 def decode_traffic():
     """HBM-side bytes of one decode step (sum over its kernels), or None."""
     csrc = os.path.join(ROOT, "block_sparse_long_02_amd", "csrc")
@@ -94,10 +119,11 @@ def decode_traffic():
     return None if any(v is None for v in vals) else int(sum(vals))
 
 
-def time_prefill(args, transforms=False, batch=None, yarn=False, paged=None):
-    """The chunked-prefill step; transforms=True runs it with the pages'
-    indexer transforms (normalised, rotated block keys and queries), yarn=True
-    with the YaRN-extended rotations and softmax scale."""
+def time_prefill(args, transforms=False, batch=None, yarn=False, paged=None, pipelined=True):
+    """The chunked-prefill step (or the prefill of `batch`); transforms=True
+    runs it with the pages' indexer transforms (normalised, rotated block keys
+    and queries), yarn=True with the YaRN-extended rotations and softmax
+    scale; pipelined=False skips the overlapped-pieces timing."""
     import torch
     from block_sparse_long_02_amd import workloads as W
     from block_sparse_long_02_amd.runner import QSARunner
@@ -133,20 +159,24 @@ def time_prefill(args, transforms=False, batch=None, yarn=False, paged=None):
     # selected (MFMA-bound).  Same calls, same results.  Its gain depends on
     # how the hardware interleaves the two kernels, and some steps come out
     # much slower, so the headline is the sequential step.
-    for _ in range(max(1, args.warmup)):
-        r.step_pipelined(PIPE_PARTS)
-    torch.cuda.synchronize()
-    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    p_start, p_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    p_start.record()
-    for k in range(args.steps):
-        pev[k][0].record()
-        r.step_pipelined(PIPE_PARTS)
-        pev[k][1].record()
-    p_stop.record()
-    torch.cuda.synchronize()
-    pipe_ms = p_start.elapsed_time(p_stop) / args.steps
-    pipe_steps = sorted(e[0].elapsed_time(e[1]) for e in pev)
+    pipe = None
+    if pipelined:
+        for _ in range(max(1, args.warmup)):
+            r.step_pipelined(PIPE_PARTS)
+        torch.cuda.synchronize()
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        p_start, p_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p_start.record()
+        for k in range(args.steps):
+            pev[k][0].record()
+            r.step_pipelined(PIPE_PARTS)
+            pev[k][1].record()
+        p_stop.record()
+        torch.cuda.synchronize()
+        pipe_steps = sorted(e[0].elapsed_time(e[1]) for e in pev)
+        pipe = dict(parts=PIPE_PARTS, ms_per_step=p_start.elapsed_time(p_stop) / args.steps,
+                    step_ms_median=pipe_steps[len(pipe_steps) // 2], step_ms_min=pipe_steps[0],
+                    step_ms_max=pipe_steps[-1])
     sum_s, sum_nc = set_sizes(r)
     n_q = r.n_q
     attend_bytes = sum_s * TOKEN_GATHER_BYTES + n_q * (2 * Q_ROW_BYTES + 24 * 4 + r.budget * 4)
@@ -159,9 +189,7 @@ def time_prefill(args, transforms=False, batch=None, yarn=False, paged=None):
         n_q=n_q, ms_per_step=total_ms / args.steps, stages_ms=stage,
         step_ms_median=per_step[len(per_step) // 2], step_ms_min=per_step[0],
         value=n_q / (total_ms / args.steps * 1e-3),
-        pipelined=dict(parts=PIPE_PARTS, ms_per_step=pipe_ms,
-                       step_ms_median=pipe_steps[len(pipe_steps) // 2],
-                       step_ms_min=pipe_steps[0], step_ms_max=pipe_steps[-1]),
+        pipelined=pipe,
         sum_set=sum_s, sum_candidates=sum_nc,
         attend=dict(bytes=attend_bytes, gbs=attend_gbs, flops=attend_flops),
         index=dict(flops=index_flops, tflops=index_flops / (stage["select"] * 1e-3) / 1e12),
@@ -221,15 +249,18 @@ def time_transforms(args, pre):
                           "frac": round(k_bytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
-def time_decode(args, mtp=False, paged=None):
+def time_decode(args, mtp=False, paged=None, ragged=False):
     """Decode step (one query per sequence), or with mtp=True a multi-token
-    decode step (4 query tokens per sequence); paged=P over P-token pages."""
+    decode step (4 query tokens per sequence), with ragged=True the ragged
+    decode (8 sequences, log-uniform lengths up to 1M tokens); paged=P over
+    P-token pages."""
     import torch
     from block_sparse_long_02_amd import workloads as W
     from block_sparse_long_02_amd.runner import QSARunner
 
     t0 = time.time()
-    b = W.mtp_decode_128k(device="cuda") if mtp else W.decode_128k(device="cuda")
+    b = (W.mtp_decode_128k(device="cuda") if mtp else
+         W.ragged_decode(device="cuda") if ragged else W.decode_128k(device="cuda"))
     r = QSARunner(b, paged=paged)
     # 512 MB > MALL, swept by a read before each step so that the step starts
     # with none of its data cached and no dirty lines to write back
@@ -278,16 +309,35 @@ def time_decode(args, mtp=False, paged=None):
                 runner=r, batch=b)
 
 
-def cpu_baseline(pre, budget_s):
-    """Time the CPU oracle on a bounded sample of the prefill workload."""
-    import numpy as np
-    from oracle import qsa_oracle as O
+def host_cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
-    b, r = pre["batch"], pre["runner"]
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def cpu_baseline(pre, budget_s):
+    """Time the CPU oracle on a bounded, stratified sample of the prefill
+    workload: rows at evenly spaced positions through the chunk, each through
+    the oracle's whole per-row pipeline.  Runs once with every host thread
+    available to numpy's BLAS and once with one thread."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import qsa_oracle as O
+    b = pre["batch"]
 
     def f64(t):
         return t.detach().float().cpu().double().numpy()
@@ -301,42 +351,112 @@ def cpu_baseline(pre, budget_s):
     kb_new = O.pool_block_keys(idx_k[prefix:prefix + chunk], chunk // 4)
     t_pool = time.time() - t0
     kbar = np.concatenate([kb_prefix, kb_new])
-    rng = np.random.default_rng(0)
-    rows = []
-    t_rows = 0.0
-    order = rng.permutation(chunk)
-    for row in order:
-        if t_rows > budget_s:
-            break
-        p = prefix + int(row)
-        t1 = time.time()
-        n_c = O.completed_blocks(p)
-        s = O.block_scores(f64(b.idx_q[row]), b.w[row].cpu().numpy(), kbar[:n_c])
-        blocks = O.select_blocks(s, b.budget)
-        tokens = O.sparse_token_set(blocks, p)
-        import torch
-        t = torch.as_tensor(tokens, device=b.k.device)
-        k_rows = f64(b.k[0][:, t, :]).transpose(1, 0, 2)
-        v_rows = f64(b.v[0][:, t, :]).transpose(1, 0, 2)
-        O.attend(f64(b.q[row]), k_rows, v_rows, tokens, p)
-        t_rows += time.time() - t1
-        rows.append(int(row))
-    per_row = t_rows / len(rows)
-    est = t_pool + per_row * chunk
-    cpu = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return dict(value=chunk / est, unit="tokens/s", cores=int(cores), kind="oracle", cpu=cpu,
-                host_cpus=os.cpu_count(),
-                sample=(f"{len(rows)} of {chunk} query rows (random), full per-row pipeline "
-                        f"(score {1015808 // 4}+ blocks, select, expand, attend) plus pooling of "
-                        f"the chunk's {chunk // 4} new blocks; time scaled to the whole chunk"),
-                seconds=round(t_pool + t_rows, 2))
+    host_threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+
+    def run(threads, seconds, n_strata):
+        # stratified: one row from each of n_strata equal slices of the chunk,
+        # slices visited in a shuffled order until the time budget is spent
+        rng = np.random.default_rng(threads)
+        starts = np.arange(n_strata) * chunk // n_strata
+        offs = rng.integers(0, max(1, chunk // n_strata), n_strata)
+        order = rng.permutation(n_strata)
+        done, t_rows = [], 0.0
+        with threadpool_limits(limits=threads):
+            used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            for st in order:
+                if t_rows > seconds:
+                    break
+                row = int(min(chunk - 1, starts[st] + offs[st]))
+                p = prefix + row
+                t1 = time.time()
+                n_c = O.completed_blocks(p)
+                sc = O.block_scores(f64(b.idx_q[row]), b.w[row].cpu().numpy(), kbar[:n_c])
+                blocks = O.select_blocks(sc, b.budget)
+                tokens = O.sparse_token_set(blocks, p)
+                t = torch.as_tensor(tokens, device=b.k.device)
+                k_rows = f64(b.k[0][:, t, :]).transpose(1, 0, 2)
+                v_rows = f64(b.v[0][:, t, :]).transpose(1, 0, 2)
+                O.attend(f64(b.q[row]), k_rows, v_rows, tokens, p)
+                t_rows += time.time() - t1
+                done.append(row)
+        est = t_pool + t_rows / len(done) * chunk
+        return dict(value=chunk / est, threads=int(used), rows=len(done),
+                    seconds=round(t_pool + t_rows, 2))
+
+    multi = run(host_threads, budget_s, 1024)
+    single = run(1, budget_s, 1024)
+    return dict(value=round(multi["value"], 2), unit="tokens/s", cores=multi["threads"],
+                kind="oracle", cpu=host_cpu_model(), host_cpus=host_threads,
+                sample=(f"{multi['rows']} of {chunk} query rows, stratified (one row from each of "
+                        f"{multi['rows']} of 1024 equal slices of the chunk), full per-row pipeline "
+                        f"(score {prefix // 4}+ blocks, select, expand, attend) plus pooling of the "
+                        f"chunk's {chunk // 4} new blocks; time scaled to the whole chunk"),
+                seconds=multi["seconds"],
+                single_thread=dict(value=round(single["value"], 2), unit="tokens/s", cores=1,
+                                   rows=single["rows"], seconds=single["seconds"]))
+
+
+def attend_roofline(pre, attend_file):
+    """Roofline of the dominant kernel, the prefill attention.  Its zero-reuse
+    gather bytes (every selected token once per query row) already exceed the
+    HBM rate -- rows that select the same blocks share them through L2 and the
+    Infinity Cache -- so the bound it cannot exceed is the MFMA rate of its
+    algorithmic flops.  memory_side gives the counted bytes beyond L2 per
+    launch (FETCH_SIZE + WRITE_SIZE, calibrated; L2 misses served by HBM or
+    the Infinity Cache) against the HBM peak and the measured achievable
+    streaming read."""
+    ms = pre["stages_ms"]["attend"]
+    tflops = pre["attend"]["flops"] / (ms * 1e-3) / 1e12
+    traffic = traffic_from_profiles(attend_file, "attend_prefill_1m")
+    ach = achievable_peaks()
+    mem = {"counted_bytes_per_launch": traffic}
+    if traffic:
+        gbs = traffic / (ms * 1e-3) / 1e9
+        mem.update(counted_gbs=round(gbs, 1), hbm_peak_gbs=HBM_PEAK_GBS,
+                   frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+        if "hbm_read_gbs" in ach:
+            mem.update(achievable_read_gbs=ach["hbm_read_gbs"],
+                       frac_of_achievable_read=round(gbs / ach["hbm_read_gbs"], 4))
+    mem["binds"] = ("the memory side: the kernel waits on its gathers (zero-reuse "
+                    f"{pre['attend']['gbs'] / 1e3:.1f} TB/s; the counted beyond-L2 bytes include "
+                    "Infinity Cache hits, so they can exceed the HBM read rate)")
+    return {"kernel": "attend_kernel<true> (sparse prefill attention)", "bound": "mfma",
+            "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic,
+            "algorithmic_flop_per_launch": pre["attend"]["flops"],
+            "mean_launch_ms": round(ms, 4),
+            "zero_reuse_gather_bytes_per_launch": pre["attend"]["bytes"],
+            "zero_reuse_gbs": round(pre["attend"]["gbs"], 1),
+            "memory_side": mem}
+
+
+def prefill_8k(args):
+    """The 8,192-token prefill from an empty cache (budget 512, 64 planted
+    blocks per 1,024-row segment) and its 2,048-token dense case: tokens/s,
+    and the index select and attention against the bf16 MFMA peak (the KV
+    cache, 17 MB, stays in L2 and the Infinity Cache)."""
+    import torch
+    from block_sparse_long_02_amd import workloads as W
+    res = {}
+    for T in (8192, 2048):
+        pr = time_prefill(args, batch=W.prefill_8k(device="cuda", T=T), pipelined=False)
+        st = pr["stages_ms"]
+        res[f"T{T}"] = {
+            "ms_per_step": round(pr["ms_per_step"], 4), "value": round(pr["value"], 1),
+            "unit": "tokens/s", "stages_ms": {k: round(v, 4) for k, v in st.items()},
+            "index_select_tflops": round(pr["index"]["tflops"], 1),
+            "index_select_frac_mfma": round(pr["index"]["tflops"] / MFMA_BF16_PEAK_TFS, 4),
+            "attend_tflops": round(pr["attend"]["flops"] / (st["attend"] * 1e-3) / 1e12, 1),
+            "attend_frac_mfma": round(pr["attend"]["flops"] / (st["attend"] * 1e-3) / 1e12
+                                      / MFMA_BF16_PEAK_TFS, 4),
+            "step_mfma_floor_ms": round((pr["index"]["flops"] + pr["attend"]["flops"])
+                                        / (MFMA_BF16_PEAK_TFS * 1e12) * 1e3, 4)}
+        log(f"prefill T={T}: {res[f'T{T}']}")
+        del pr
+        torch.cuda.empty_cache()
+    res["workload"] = ("prefill from an empty cache, batch 1, T=8192 (and T=2048, where every row "
+                       "keeps every completed block: dense causal attention), budget 512 blocks + tail")
+    return res
 
 
 def main():
@@ -346,7 +466,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "mtp"], default=None)
+    ap.add_argument("--only", choices=["prefill", "prefill8k", "decode", "ragged", "mtp"],
+                    default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the QSA path here is "
@@ -375,18 +496,7 @@ def main():
             "workload": "chunked prefill: 32768-token chunk on a 1015808-token cached prefix "
                         "(1048576 total), batch 1, budget 512 blocks + tail",
             "global_batch": 1, "seq_len": 1048576, "query_tokens": pre["n_q"], "budget": 512}
-        traffic = traffic_from_profiles(attend_file, "attend_prefill_1m")
-        out["roofline"] = {
-            "kernel": "attend_kernel (sparse prefill attention)",
-            "bound": "hbm", "achieved": round(pre["attend"]["gbs"], 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(pre["attend"]["gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": pre["attend"]["bytes"],
-            "mean_launch_ms": round(pre["stages_ms"]["attend"], 4),
-            # algorithmic bytes count every gathered token once per query (no
-            # reuse); the counters show what crossed the L2 boundary
-            "measured_gbs": (round(traffic / (pre["stages_ms"]["attend"] * 1e-3) / 1e9, 1)
-                             if traffic else None)}
+        out["roofline"] = attend_roofline(pre, attend_file)
         out["stages_ms"] = {k: round(v, 4) for k, v in pre["stages_ms"].items()}
         pool_bytes = (pre["n_q"] // 4) * (4 * BLOCK_KEY_BYTES + BLOCK_KEY_BYTES)
         out["rows"] = {
@@ -423,6 +533,8 @@ def main():
         torch.cuda.empty_cache()
         del pre
         torch.cuda.empty_cache()
+    if args.only in (None, "prefill8k"):
+        out["prefill_8k"] = prefill_8k(args)
     if args.only in (None, "decode"):
         dec = time_decode(args)
         log(f"decode: {dec['ms_per_step']:.4f} ms/step, stages {dec['stages_ms']}")
@@ -453,6 +565,31 @@ def main():
                                   "stages_ms": {k: round(v, 4) for k, v in dp["stages_ms"].items()},
                                   "hbm_frac": round(dp["hbm"]["gbs"] / HBM_PEAK_GBS, 4)}
         dp = None
+        torch.cuda.empty_cache()
+    if args.only in (None, "ragged"):
+        rg = time_decode(args, ragged=True)
+        lens = rg["batch"].seq_lens_host()
+        log(f"ragged decode {lens}: {rg['ms_per_step']:.4f} ms/step, stages {rg['stages_ms']}")
+        ach = achievable_peaks()
+        out["ragged_decode"] = {
+            "value": round(rg["value"], 1), "unit": "tokens/s",
+            "ms_per_step": round(rg["ms_per_step"], 4),
+            "step_ms_median": round(rg["step_ms_median"], 4),
+            "step_ms_min": round(rg["step_ms_min"], 4),
+            "config": {"workload": "ragged decode: 8 sequences, lengths log-uniform in "
+                                   "[4096, 1048572] plus 1-3 tokens past a block boundary, "
+                                   "near ties in half, budget 512 blocks + tail, MALL flushed "
+                                   "before each step", "seq_lens": lens},
+            # this draw's floor: its block keys and its rows' gathers at the HBM peak
+            "floor_ms_at_hbm_peak": round(rg["hbm"]["bytes"] / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+            "floor_ms_at_achievable_read": (round(rg["hbm"]["bytes"] / (ach["hbm_read_gbs"] * 1e9)
+                                                  * 1e3, 4) if "hbm_read_gbs" in ach else None),
+            "roofline": {"bound": "hbm", "scope": "whole step",
+                         "achieved": round(rg["hbm"]["gbs"], 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(rg["hbm"]["gbs"] / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": rg["hbm"]["bytes"]},
+            "stages_ms": {k: round(v, 4) for k, v in rg["stages_ms"].items()}}
+        rg = None
     dec = None
     torch.cuda.empty_cache()
     if args.only in (None, "mtp"):

@@ -19,6 +19,8 @@
 // accumulators in float32.
 #include <math.h>
 
+#include <mutex>
+
 #include "qsa_common.hpp"
 
 namespace qsa {
@@ -454,27 +456,37 @@ size_t qsa_attend_decode_workspace(int32_t n_seq) {
   return (size_t)n_seq * 2 * kDecodeSplits * qsa::kPartFloats * sizeof(float);
 }
 
-int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq, const void* k_cache,
-                      const void* v_cache, int64_t kv_seq_stride, int64_t kv_head_stride,
-                      const int32_t* sel, const int32_t* sel_count, int32_t budget, void* out,
-                      float* lse, void* workspace, size_t ws_bytes, const double* inv_freq,
-                      float softmax_scale, const int32_t* block_table, int64_t table_stride,
-                      int32_t page_tokens, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host checks shared by qsa_attend_decode and qsa_attend_decode_noalloc
+// (everything but the partials buffer).
+int check_decode(const void* q, const int32_t* seq_len, int32_t n_seq, const void* k_cache,
+                 const void* v_cache, int64_t kv_seq_stride, int64_t kv_head_stride,
+                 const int32_t* sel, const int32_t* sel_count, int32_t budget, const void* out,
+                 const double* inv_freq, float softmax_scale, const int32_t* block_table,
+                 int64_t table_stride, int32_t page_tokens, qsa::RopeFreq& fr, qsa::Pages& pg) {
   using namespace qsa_host;
   if (n_seq < 0) return QSA_ERR_INVALID_ARG;
-  qsa::RopeFreq fr;
   if (!make_rope_freq(inv_freq, fr) || !softmax_scale_ok(softmax_scale)) return QSA_ERR_INVALID_ARG;
-  qsa::Pages pg;
   if (!make_pages(block_table, table_stride, page_tokens, pg)) return QSA_ERR_INVALID_ARG;
   if (n_seq == 0) return QSA_OK;
   if (!seq_len) return QSA_ERR_INVALID_ARG;
   int st = check_attend_common(q, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
                                budget, out);
   if (st != QSA_OK) return st;
-  if (!workspace || !aligned16(workspace)) return QSA_ERR_INVALID_ARG;
-  if (ws_bytes < qsa_attend_decode_workspace(n_seq)) return QSA_ERR_WORKSPACE_TOO_SMALL;
   if ((int64_t)n_seq * 2 * qsa::kGroup > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
-  float* part = (float*)workspace;
+  return QSA_OK;
+}
+
+// The split-K partials and the combine pass of a decode step; `part` holds
+// n_seq * 2 * kDecodeSplits partials.
+int launch_decode(const void* q, const int32_t* seq_len, int32_t n_seq, const void* k_cache,
+                  const void* v_cache, int64_t kv_seq_stride, int64_t kv_head_stride,
+                  const int32_t* sel, const int32_t* sel_count, int32_t budget, void* out,
+                  float* lse, float* part, const qsa::RopeFreq& fr, float softmax_scale,
+                  const qsa::Pages& pg, void* stream) {
   hipLaunchKernelGGL(qsa::attend_kernel<false>, dim3(n_seq * 2 * kDecodeSplits), dim3(256), 0,
                      (hipStream_t)stream, (const uint16_t*)q, (const int32_t*)nullptr, seq_len,
                      n_seq, n_seq, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
@@ -482,7 +494,92 @@ int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq, cons
                      (uint16_t*)nullptr, (float*)nullptr, part, fr, softmax_scale, pg);
   hipLaunchKernelGGL(qsa::combine_kernel<kDecodeSplits>, dim3(n_seq * 2 * qsa::kGroup), dim3(256), 0,
                      (hipStream_t)stream, (const float*)part, n_seq, (uint16_t*)out, lse);
-  return launch_status();
+  return qsa_host::launch_status();
+}
+
+// ---------------------------------------------------- allocation-free decode
+// The partials of qsa_attend_decode_noalloc live in this file-scope device
+// array instead of a caller's workspace: every GPU the library runs on holds
+// its own copy (25.4 MB for QSA_NOALLOC_MAX_SEQ = 128 sequences) until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in symbol); it asks the runtime for the array's
+// address on each device once, with that device current, and uses that.
+constexpr size_t kNoAllocFloats =
+    (size_t)QSA_NOALLOC_MAX_SEQ * 2 * kDecodeSplits * qsa::kPartFloats;
+
+}  // namespace
+
+static __device__ __align__(256) float scratch[kNoAllocFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The address of the current device's copy of `scratch`, looked up on the
+// first call on that device.  The stream must belong to the current device.
+int scratch_on_current_device(void* stream, float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return QSA_ERR_INTERNAL;
+  if (dev < 0 || dev >= kMaxDevices) return QSA_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return QSA_ERR_INVALID_ARG;
+    if ((int)sdev != dev) return QSA_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QSA_ERR_INTERNAL;
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq, const void* k_cache,
+                      const void* v_cache, int64_t kv_seq_stride, int64_t kv_head_stride,
+                      const int32_t* sel, const int32_t* sel_count, int32_t budget, void* out,
+                      float* lse, void* workspace, size_t ws_bytes, const double* inv_freq,
+                      float softmax_scale, const int32_t* block_table, int64_t table_stride,
+                      int32_t page_tokens, void* stream) {
+  qsa::RopeFreq fr;
+  qsa::Pages pg;
+  int st = check_decode(q, seq_len, n_seq, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel,
+                        sel_count, budget, out, inv_freq, softmax_scale, block_table,
+                        table_stride, page_tokens, fr, pg);
+  if (st != QSA_OK || n_seq == 0) return st;
+  if (!workspace || !qsa_host::aligned16(workspace)) return QSA_ERR_INVALID_ARG;
+  if (ws_bytes < qsa_attend_decode_workspace(n_seq)) return QSA_ERR_WORKSPACE_TOO_SMALL;
+  return launch_decode(q, seq_len, n_seq, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel,
+                       sel_count, budget, out, lse, (float*)workspace, fr, softmax_scale, pg,
+                       stream);
+}
+
+int qsa_attend_decode_noalloc(const void* q, const int32_t* seq_len, int32_t n_seq,
+                              const void* k_cache, const void* v_cache, int64_t kv_seq_stride,
+                              int64_t kv_head_stride, const int32_t* sel,
+                              const int32_t* sel_count, int32_t budget, void* out, float* lse,
+                              const double* inv_freq, float softmax_scale,
+                              const int32_t* block_table, int64_t table_stride,
+                              int32_t page_tokens, void* stream) {
+  qsa::RopeFreq fr;
+  qsa::Pages pg;
+  int st = check_decode(q, seq_len, n_seq, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel,
+                        sel_count, budget, out, inv_freq, softmax_scale, block_table,
+                        table_stride, page_tokens, fr, pg);
+  if (st != QSA_OK || n_seq == 0) return st;
+  if (n_seq > QSA_NOALLOC_MAX_SEQ) return QSA_ERR_UNSUPPORTED;
+  float* part = nullptr;
+  st = scratch_on_current_device(stream, &part);
+  if (st != QSA_OK) return st;
+  return launch_decode(q, seq_len, n_seq, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel,
+                       sel_count, budget, out, lse, part, fr, softmax_scale, pg, stream);
 }
 
 }  // extern "C"

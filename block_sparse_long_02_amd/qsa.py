@@ -52,6 +52,10 @@ SIGNATURES = {
                                          _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p,
                                          _size, _c_void_p, ctypes.c_float, _c_void_p, _i64, _i32,
                                          _c_void_p]),
+    "qsa_attend_decode_noalloc": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p,
+                                                 _i64, _i64, _c_void_p, _c_void_p, _i32, _c_void_p,
+                                                 _c_void_p, _c_void_p, ctypes.c_float, _c_void_p,
+                                                 _i64, _i32, _c_void_p]),
     "qsa_attend_decode_multi_workspace": (_size, [_i32]),
     "qsa_attend_decode_multi": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
                                                _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32,
@@ -238,6 +242,22 @@ def attend_decode(q, seq_len, k_cache, v_cache, sel, sel_count, budget, out, lse
                                  workspace.numel() * workspace.element_size(), fp,
                                  float(softmax_scale), *_pages(pages), _stream(stream))
     _check("qsa_attend_decode", st)
+
+
+NOALLOC_MAX_SEQ = 128
+
+
+def attend_decode_noalloc(q, seq_len, k_cache, v_cache, sel, sel_count, budget, out, lse,
+                          inv_freq=None, softmax_scale=SOFTMAX_SCALE, pages=None, stream=None):
+    """qsa_attend_decode without a workspace (the library's own per-GPU buffer,
+    at most NOALLOC_MAX_SEQ sequences; overlapping calls on one GPU race)."""
+    _dev(q, seq_len, k_cache, v_cache, sel, sel_count, out, lse)
+    fp, _keep = _host_f64(inv_freq)
+    st = lib().qsa_attend_decode_noalloc(_p(q), _p(seq_len), seq_len.numel(), _p(k_cache),
+                                         _p(v_cache), *_kv_strides(k_cache, pages), _p(sel),
+                                         _p(sel_count), int(budget), _p(out), _p(lse), fp,
+                                         float(softmax_scale), *_pages(pages), _stream(stream))
+    _check("qsa_attend_decode_noalloc", st)
 
 
 def attend_decode_multi_workspace(n_q) -> int:

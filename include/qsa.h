@@ -23,7 +23,8 @@
  *    hold IEEE bfloat16 bit patterns (uint16).  The caller owns every buffer;
  *    the library allocates no device memory and keeps no pointer after a call
  *    returns.  Scratch space is passed in as `workspace`, sized by the matching
- *    *_workspace() query.
+ *    *_workspace() query; the one exception, qsa_attend_decode_noalloc, uses a
+ *    fixed-size array inside the library instead.
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Every
  *    call only enqueues work on it and returns; results are ready once the
  *    stream is synchronised.  Device-side faults surface at that sync.
@@ -96,6 +97,7 @@ enum qsa_status {
 #define QSA_ROPE_DIM 64        /* rotated dims of a core head             */
 #define QSA_MAX_BUDGET 512     /* K_B = ceil(2048 / 4)                    */
 #define QSA_MAX_TOKENS (1 << 22)
+#define QSA_NOALLOC_MAX_SEQ 128   /* sequences per qsa_attend_decode_noalloc call */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* qsa_status_string(int status);
@@ -292,6 +294,32 @@ int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq,
                       const double* inv_freq, float softmax_scale,
                       const int32_t* block_table, int64_t table_stride, int32_t page_tokens,
                       void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the split-K
+ * decode of qsa_attend_decode with no workspace argument.  Same arguments,
+ * mathematics, kernels and results (bit for bit) as qsa_attend_decode.
+ *
+ * The partials live in a device array inside the library, one copy per GPU
+ * it runs on, held until the process ends: n_seq * 2 * 8 * 12,416 bytes, at
+ * most QSA_NOALLOC_MAX_SEQ = 128 sequences (25.4 MB).  The call allocates
+ * nothing.  Its first call on a device looks the array up with that device
+ * current, so `stream` must belong to the current device (or be NULL).  Every
+ * call on one GPU shares that array: calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race, so
+ * order them.  Nothing in the array needs clearing between calls.
+ * Errors: QSA_ERR_UNSUPPORTED for n_seq > QSA_NOALLOC_MAX_SEQ (checked on
+ * the host before any HIP call); QSA_ERR_INVALID_ARG for a stream of another
+ * device; otherwise as qsa_attend_decode.
+ */
+int qsa_attend_decode_noalloc(const void* q, const int32_t* seq_len, int32_t n_seq,
+                              const void* k_cache, const void* v_cache,
+                              int64_t kv_seq_stride, int64_t kv_head_stride,
+                              const int32_t* sel, const int32_t* sel_count, int32_t budget,
+                              void* out, float* lse, const double* inv_freq,
+                              float softmax_scale, const int32_t* block_table,
+                              int64_t table_stride, int32_t page_tokens, void* stream);
 
 /*
  * f1 (multi-token decode) -- the split-K decode of qsa_attend_decode for a

@@ -31,7 +31,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
         assert n in qsa.SIGNATURES, n
@@ -100,6 +100,12 @@ def test_attention_and_pool_reject_bad_arguments(L):
     assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 100, None, 0.0625, None, 0, 0, None) == 3
     assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 600, A, A, A, 1 << 30, None, 0.0625, None, 0, 0, None) == 1
     assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, MISALIGNED, 1 << 30, None, 0.0625, None, 0, 0, None) == 1
+    # allocation-free decode: more than QSA_NOALLOC_MAX_SEQ (128) sequences is
+    # refused on the host, as are the arguments qsa_attend_decode refuses
+    assert L.qsa_attend_decode_noalloc(A, A, 129, A, A, 1024, 512, A, A, 16, A, A, None, 0.0625, None, 0, 0, None) == 2
+    assert L.qsa_attend_decode_noalloc(A, A, 4, A, A, 1024, 512, A, A, 600, A, A, None, 0.0625, None, 0, 0, None) == 1
+    assert L.qsa_attend_decode_noalloc(A, A, 4, A, A, 1024, 512, A, A, 16, MISALIGNED, A, None, 0.0625, None, 0, 0, None) == 1
+    assert L.qsa_attend_decode_noalloc(A, A, 0, A, A, 1024, 512, A, A, 16, A, A, None, 0.0625, None, 0, 0, None) == 0
     # multi-token decode: cu_q required, workspace sized by n_q
     assert L.qsa_attend_decode_multi(A, None, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 1 << 30, None, 0.0625, None, 0, 0, None) == 1
     assert L.qsa_attend_decode_multi(A, A, A, 2, 8, A, A, 1024, 512, A, A, 16, A, A, A, 100, None, 0.0625, None, 0, 0, None) == 3

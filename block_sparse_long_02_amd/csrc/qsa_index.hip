@@ -123,12 +123,16 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
                    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
                    int n_q, int max_blocks, const uint16_t* __restrict__ bk, int64_t bk_stride,
                    uint32_t* __restrict__ dense, int64_t dense_stride,
-                   uint32_t* __restrict__ dsmp, int64_t dsmp_stride, Pages pg) {
+                   uint32_t* __restrict__ dsmp, int64_t dsmp_stride, int n_chunks, Pages pg) {
   __shared__ float s_w[4][4];
   __shared__ int s_nc[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int s = blockIdx.x;
+  // one linear grid, sequence-major: a sequence's chunks take consecutive
+  // workgroup ids, which the dispatcher spreads over the XCDs (a grid of
+  // (sequences, chunks) would put every chunk of a sequence on one XCD
+  // whenever the sequence count is a multiple of 8)
+  const int s = blockIdx.x / n_chunks, chunk = blockIdx.x % n_chunks;
   const int qb = cu_q[s], qe_raw = cu_q[s + 1];
   const int qe = min(qe_raw, n_q);
   if (qb >= qe || qb < 0) return;
@@ -137,7 +141,7 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
   // rows with more than max_blocks candidates are reported by the select;
   // the others still need every score
   const int nc_last = min((pos0 + n_rows) >> 2, max_blocks);
-  const int v0 = blockIdx.y * kDenseChunk;
+  const int v0 = chunk * kDenseChunk;
   if (v0 >= nc_last) return;
   const int v1 = min(v0 + kDenseChunk, nc_last);
   if (threadIdx.x < 4) {
@@ -177,7 +181,7 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
 #endif
   // Workgroups start at different tiles of their chunk (rotated order) so
   // that the ones running together do not stream the same address offsets.
-  const int rot = QSA_DENSE_SKEW ? (int)((blockIdx.x * 7u + blockIdx.y * 3u) & (kDenseTiles - 1)) : 0;
+  const int rot = QSA_DENSE_SKEW ? (int)(((unsigned)s * 7u + (unsigned)chunk * 3u) & (kDenseTiles - 1)) : 0;
   auto tcol = [&](int t) { return c0 + 64 * ((t + rot) & (kDenseTiles - 1)); };
   // B fragment of tile t: column tcol(t) + col (clamped in bounds past v1)
   auto load_tile = [&](u32x4 (&bf)[4], int t) {
@@ -230,10 +234,9 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
 // a 2-stage LDS ring of 64 columns (16 KB) shared by the waves: every thread
 // loads 16/NW chunks of 16 bytes of the next stage into registers while the
 // current stage is multiplied, then writes them to LDS (each wave
-// instruction covers a 1 KB run of 4 columns).  Inside a stage,
-// chunk q (16 bytes) of column c sits at chunk slot q ^ (c % 16), which makes
-// the MFMA B-fragment reads (16 columns x one chunk) hit 16 distinct bank
-// groups.
+// instruction covers a 1 KB run of 4 columns).  Inside a stage, columns sit
+// 272 bytes apart (256 + 16 of padding), which makes the MFMA B-fragment
+// reads (16 columns x one 16-byte chunk) hit 16 distinct bank groups.
 //
 // Filter epilogue.  About 1% of candidates reach the threshold, so almost
 // every stage has a hit somewhere; handling hits in the SIMT stream would cost
@@ -244,6 +247,10 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
 // the exact tau test run once per workgroup over the pending lists, one entry
 // per lane.
 constexpr int kStageCols = 64;
+// bf16 elements per LDS column: 256 bytes of key plus 16 of padding, so the
+// 16 lanes of a 128-bit B-fragment read (16 columns, the same dims) hit 16
+// distinct bank groups
+constexpr int kColStride = kIdxDim + 8;
 
 // v_dot2_f32_bf16 with a destination of its own: for a loop-invariant
 // accumulator the compiler picks the accumulating form plus a register copy
@@ -280,7 +287,7 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
   // paged: the physical pages of the chunk's blocks (pages hold >= 64 blocks)
   constexpr int kPgSlots = kPaged ? kMaxChunkCols * stride / 64 + 1 : 1;
   __shared__ int s_pg[kPgSlots];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[2][kStageCols * kIdxDim];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[2][kStageCols * kColStride];
   __shared__ float s_w[QT][4];
   __shared__ f32x4 s_wc[QT];
   __shared__ float s_tlo[QT];
@@ -383,14 +390,13 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
   const __amdgpu_buffer_rsrc_t bk_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)bseq, (short)0, nrec, 0x00020000);
   // This thread carries CPT chunks of a stage: column c = kWaveCols*wave +
-  // 4*i + lane/16, chunk slot lane%16, which holds chunk (lane%16) ^ (c%16);
-  // its byte offsets relative to the stage's first column are fixed.
+  // 4*i + lane/16, 16-byte chunk lane%16; its byte offsets relative to the
+  // stage's first column are fixed.
   int loff[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = kWaveCols * wave + 4 * i + (lane >> 4);
-    const int q = (lane & 15) ^ (c & 15);
-    loff[i] = (c * stride * kIdxDim + q * 8) * 2;
+    loff[i] = (c * stride * kIdxDim + (lane & 15) * 8) * 2;
   }
   auto load_stage = [&](u32x4 (&r)[CPT], int st) {
     if constexpr (kPaged && !kSample) {
@@ -412,12 +418,11 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const int c = kWaveCols * wave + 4 * i + (lane >> 4);
-        const int q = (lane & 15) ^ (c & 15);
         const int vcol = v0 + st * kStageCols + c;
         const int64_t blk = (int64_t)min(vcol, v1 - 1) * stride;
         const int64_t pb = ((int64_t)s_pg[(int)(blk >> pg.shift) - pg0] << pg.shift) +
                            (blk & (((int64_t)1 << pg.shift) - 1));
-        const u32x4 v = ldg16(bseq + pb * kIdxDim + q * 8);
+        const u32x4 v = ldg16(bseq + pb * kIdxDim + (lane & 15) * 8);
         r[i] = vcol < v1 ? v : u32x4{0, 0, 0, 0};
       }
     } else {
@@ -434,7 +439,7 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = kWaveCols * wave + 4 * i + (lane >> 4);
-      *(u32x4*)(dst + c * kIdxDim + (lane & 15) * 8) = r[i];
+      *(u32x4*)(dst + c * kColStride + (lane & 15) * 8) = r[i];
     }
   };
   // the defined score of row j for block b, and where it goes
@@ -456,11 +461,13 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
   // One stage = 4 column tiles, explicitly pipelined: the B fragments of
   // tile t+1 are read from LDS before the MFMAs of tile t are issued, and the
   // epilogue of tile t runs after the MFMAs of tile t+1 are in flight.
+  // B fragment of column tile ct: column 16 ct + col, dims 32 ks + 8 grp ..
+  // +7; the lane's base address plus a constant per (ct, ks)
+  const int b_lane = col * kColStride + 8 * grp;
   auto read_b = [&](const uint16_t* sb, int ct, u32x4 (&bf)[4]) {
-    const int c = 16 * ct + col;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      bf[ks] = *(const u32x4*)(sb + c * kIdxDim + (((grp + 4 * ks) ^ col) * 8));
+      bf[ks] = *(const u32x4*)(sb + b_lane + 16 * ct * kColStride + 32 * ks);
   };
   auto mfma_b = [&](const u32x4 (&bf)[4], f32x4 (&acc)[MT]) {
 #pragma unroll
@@ -519,21 +526,25 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
       }
     }
   };
+  // The epilogue of a stage's last tile runs in the next stage, behind the
+  // MFMAs of its first tile (it reads only registers and this wave's rows).
   auto run = [&](auto mode_tag) {
     u32x4 stage_regs[CPT];
     load_stage(stage_regs, 0);
     store_stage(stage_regs, 0);
     __syncthreads();
+    f32x4 a1[MT];
     for (int st = 0; st < n_stages; ++st) {
       const bool more = st + 1 < n_stages;
       if (more) load_stage(stage_regs, st + 1);          // in flight during this stage
       const uint16_t* sb = s_b[st & 1];
       const int cbase = v0 + st * kStageCols;
       u32x4 b0[4], b1[4];
-      f32x4 a0[MT], a1[MT];
+      f32x4 a0[MT];
       read_b(sb, 0, b0);
       read_b(sb, 1, b1);
       mfma_b(b0, a0);                       // tile 0
+      if (st > 0) epi(mode_tag, a1, cbase - 16);   // tile 3 of the previous stage
       read_b(sb, 2, b0);
       mfma_b(b1, a1);                       // tile 1
       epi(mode_tag, a0, cbase);
@@ -542,10 +553,10 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
       epi(mode_tag, a1, cbase + 16);
       mfma_b(b1, a1);                       // tile 3
       epi(mode_tag, a0, cbase + 32);
-      epi(mode_tag, a1, cbase + 48);
       if (more) store_stage(stage_regs, st + 1);
       __syncthreads();   // stage st+1 visible; stage st's buffer free for st+2
     }
+    epi(mode_tag, a1, v0 + n_stages * kStageCols - 16);
   };
   // rows are in position order, so the first row has the fewest candidates
   const bool full_chunk = v1 <= min((pos0 + 1) >> 2, max_blocks) && (v1 - v0) % kStageCols == 0;
@@ -712,6 +723,96 @@ __device__ uint32_t kth_largest_fast(Get get, int n, int k, const KthLds& sh) {
         const uint32_t v = get(i);
         if (v >= blo && v <= bhi) sh.bin[atomicAdd(sh.bin_n, 1)] = v;
       }
+      __syncthreads();
+      if (tid < hb) {
+        const uint32_t x = sh.bin[tid];
+        int gt = 0, ge = 0;
+        for (int j = 0; j < hb; ++j) {
+          const uint32_t y = sh.bin[j];
+          gt += y > x;
+          ge += y >= x;
+        }
+        if (gt < k && k <= ge) sh.res[0] = (int)x;   // every writer has the same x
+      }
+      __syncthreads();
+      const uint32_t T = (uint32_t)sh.res[0];
+      __syncthreads();
+      return T;
+    }
+    lo = blo;
+    hi = blo + ((1u << s) - 1u);
+  }
+}
+
+// f(v) for each of the n uint32 values at p (16-byte aligned, readable up
+// to n rounded up to 4) by a 256-thread workgroup, 8 16-byte loads in flight
+// per thread: a pass over values in global memory then costs a few memory
+// round trips instead of one per 256 values.
+template <class F>
+__device__ __forceinline__ void for_each_u32(const uint32_t* __restrict__ p, int n, F f) {
+  const u32x4* p4 = reinterpret_cast<const u32x4*>(p);
+  const int nq = (n + 3) >> 2;
+  for (int q0 = 0; q0 < nq; q0 += 256 * 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int q = q0 + 256 * u + threadIdx.x;
+      v[u] = q < nq ? p4[q] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int q = q0 + 256 * u + threadIdx.x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * q + e < n) f(v[u][e]);
+    }
+  }
+}
+
+// kth_largest_fast for values in global memory, each pass through
+// for_each_u32.  Ends with a barrier.
+__device__ uint32_t kth_largest_global(const uint32_t* __restrict__ p, int n, int k,
+                                       const KthLds& sh) {
+  const int tid = threadIdx.x;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  for_each_u32(p, n, [&](uint32_t v) { lo = min(lo, v); hi = max(hi, v); });
+  block_min_max(lo, hi, sh.tmp, lo, hi);
+  for (;;) {
+    const uint32_t span = hi - lo;
+    const int s = span < (uint32_t)kBins ? 0 : 32 - __clz((int)(span >> 11));   // span >> s < 2048
+    for (int i = tid; i < kBins; i += 256) sh.hist[i] = 0;
+    if (tid == 0) *sh.bin_n = 0;
+    __syncthreads();
+    for_each_u32(p, n, [&](uint32_t v) {
+      if (v >= lo && v <= hi) atomicAdd(&sh.hist[(v - lo) >> s], 1);
+    });
+    __syncthreads();
+    constexpr int per = kBins / 256;
+    const int b0 = tid * per;
+    int local = 0;
+#pragma unroll
+    for (int b = 0; b < per; ++b) local += sh.hist[b0 + b];
+    int total;
+    const int excl = block_excl_scan_256(local, sh.tmp, total);
+    int run = total - excl - local;   // values in the bins above this thread's
+#pragma unroll
+    for (int b = per - 1; b >= 0; --b) {
+      const int h = sh.hist[b0 + b];
+      if (run < k && run + h >= k) { sh.res[0] = b0 + b; sh.res[1] = run; }
+      run += h;
+    }
+    __syncthreads();
+    const uint32_t B = (uint32_t)sh.res[0];
+    k -= sh.res[1];
+    const int hb = sh.hist[B];
+    __syncthreads();
+    const uint32_t blo = lo + (B << s);
+    if (s == 0) return blo;
+    if (hb <= kFinishCap) {
+      const uint32_t bhi = blo + ((1u << s) - 1u);
+      for_each_u32(p, n, [&](uint32_t v) {
+        if (v >= blo && v <= bhi) sh.bin[atomicAdd(sh.bin_n, 1)] = v;
+      });
       __syncthreads();
       if (tid < hb) {
         const uint32_t x = sh.bin[tid];
@@ -1197,8 +1298,7 @@ select_dense_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict_
     tau_s = kth_largest_fast([&](int i) { return sh.u.smp[i]; }, ns, r,
                              KthLds{sh.hist, sh.bin, sh.tmp, sh.res, &sh.bin_n});
   } else {
-    tau_s = kth_largest_fast([&](int i) { return srow[i]; }, ns, r,
-                             KthLds{sh.hist, sh.bin, sh.tmp, sh.res, &sh.bin_n});
+    tau_s = kth_largest_global(srow, ns, r, KthLds{sh.hist, sh.bin, sh.tmp, sh.res, &sh.bin_n});
   }
 
   // compaction; tau_s = 0 would pass every score (more than the list holds)
@@ -1336,12 +1436,14 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
   if (use_dense(max_q_len)) {
     // decode: dense scores, then one select per row
     if (max_blocks > 0) {
-      dim3 grid((unsigned)n_seq, (max_blocks + kDenseChunk - 1) / kDenseChunk);
-      if (grid.y > 65535) return QSA_ERR_UNSUPPORTED;
+      const int n_chunks = (max_blocks + kDenseChunk - 1) / kDenseChunk;
+      const int64_t n_wg = (int64_t)n_seq * n_chunks;
+      if (n_wg > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
       auto launch = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const uint16_t*)idx_q, w, cu_q, seq_len,
-                           n_q, max_blocks, (const uint16_t*)block_keys, bk_seq_stride, ws.dense,
-                           ws.dense_stride, ws.dsmp, ws.dsmp_stride, pg);
+        hipLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(256), 0, st, (const uint16_t*)idx_q, w,
+                           cu_q, seq_len, n_q, max_blocks, (const uint16_t*)block_keys,
+                           bk_seq_stride, ws.dense, ws.dense_stride, ws.dsmp, ws.dsmp_stride,
+                           n_chunks, pg);
       };
       if (pg.table) launch(score_dense_kernel<true>);
       else launch(score_dense_kernel<false>);

@@ -18,9 +18,16 @@ uses the figures only while that source is unchanged.
 
     python3 -m block_sparse_long_02_amd.measure peaks OUT_JSON
 
-times the micro-benchmarks of libqsa_probe.so: the sustained rate of the
+times the micro-benchmarks of libqsa_probe.so (built on request with
+`python3 -m block_sparse_long_02_amd.build probe`): the sustained rate of the
 16x16x32 bf16 MFMA and the sustained HBM read and copy bandwidth, beside the
 published peaks the roofline fractions use.
+
+    python3 -m block_sparse_long_02_amd.measure pmc OUT_MD CSV [CSV ...]
+
+turns counter runs of the same program (any SQ counters, e.g. the MFMA
+pipe's busy cycles) into a per-kernel table: each counter's value per
+dispatch and the utilisation ratios derived from them.
 """
 from __future__ import annotations
 
@@ -220,6 +227,67 @@ def peaks(out_json: str):
     print(json.dumps(res, indent=1))
 
 
+# utilisation ratios from SQ counters (all summed over the GPU's SIMDs or
+# CUs): MFMA pipe busy cycles per SIMD-cycle, VALU issue (4 cycles per wave64
+# instruction) per SIMD-cycle, and the shares of wave cycles spent waiting
+# (on anything, on instruction dependencies) or issuing
+SIMDS = 1024
+
+
+def pmc(out_md: str, *csvs: str):
+    """Per-kernel averages of every counter in the given counter runs, and
+    the derived ratios, as a markdown table for the kernels of this path."""
+    vals = {}
+    for path in csvs:
+        per = {}
+        for row in csv.DictReader(open(path)):
+            key = (int(row["Dispatch_Id"]), row["Kernel_Name"], row["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+        for (d, k, c), v in per.items():
+            vals.setdefault(k, {}).setdefault(c, []).append(v)
+    lines = []
+    for k in sorted(vals):
+        if "qsa::" not in k:
+            continue
+        name = k.split("(")[0].replace("void ", "")
+        c = {n: sum(v) / len(v) for n, v in vals[k].items()}
+        lines.append(f"### `{name}` ({max(len(v) for v in vals[k].values())} dispatches)")
+        lines.append("")
+        lines.append("| counter | per dispatch |")
+        lines.append("|---|---|")
+        for n in sorted(c):
+            lines.append(f"| {n} | {c[n]:.4g} |")
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs: per-XCD cycles of the dispatch
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+        derived = []
+        if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            derived.append(("MFMA pipe busy (of SIMD cycles)", c["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS / cyc))
+        if cyc and "SQ_INSTS_VALU" in c:
+            derived.append(("VALU issue (4 cycles per instruction, of SIMD cycles)",
+                            4.0 * c["SQ_INSTS_VALU"] / SIMDS / cyc))
+        if "SQ_INSTS_MFMA" in c and "SQ_INSTS_VALU" in c and c["SQ_INSTS_MFMA"]:
+            derived.append(("VALU instructions per MFMA (MFMA included)", c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"]))
+        if "SQ_INSTS_MFMA" in c and "SQ_INSTS_LDS" in c and c["SQ_INSTS_MFMA"]:
+            derived.append(("LDS instructions per MFMA", c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"]))
+        w = c.get("SQ_WAVE_CYCLES")
+        if w:
+            for n, label in (("SQ_WAIT_ANY", "wave cycles waiting on anything"),
+                             ("SQ_WAIT_INST_ANY", "wave cycles waiting on dependencies"),
+                             ("SQ_ACTIVE_INST_ANY", "wave cycles issuing")):
+                if n in c:
+                    derived.append((label, c[n] / w))
+        if derived:
+            lines.append("")
+            lines.append("| derived | value |")
+            lines.append("|---|---|")
+            for label, v in derived:
+                lines.append(f"| {label} | {v:.3f} |")
+        lines.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     if sys.argv[1:2] == ["probe"]:
         probe()
@@ -227,5 +295,8 @@ if __name__ == "__main__":
         peaks(sys.argv[2])
     elif sys.argv[1:2] == ["summarize"] and len(sys.argv) == 5:
         summarize(*sys.argv[2:5])
+    elif sys.argv[1:2] == ["pmc"] and len(sys.argv) >= 4:
+        pmc(*sys.argv[2:])
     else:
-        sys.exit("usage: measure.py probe | summarize FETCH_CSV WRITE_CSV OUT_JSON | peaks OUT_JSON")
+        sys.exit("usage: measure.py probe | summarize FETCH_CSV WRITE_CSV OUT_JSON | peaks OUT_JSON"
+                 " | pmc OUT_MD CSV [CSV ...]")

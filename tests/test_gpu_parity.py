@@ -229,10 +229,15 @@ def test_index_select_exact_grid_decode():
 
 
 def test_index_select_exact_grid_decode_long_rows():
-    # n_c = 32768 (largest row selected inside LDS), 35000 and 65536 (sampled
-    # threshold, then the candidate list)
-    b = W.make_decode(seq_lens=[131075, 140001, 262147], budget=512, n_plant=32, seed=29,
-                      exact_grid=True)
+    # n_c = 32768 (one compaction pass), 35000 and 65536 (passes of 32,768
+    # scores, threshold from samples in global memory), and a 1M-token row
+    # (262,143 blocks, near ties) beside a short one and one with no candidate
+    b = W.make_decode(seq_lens=[131075], budget=512, n_plant=32, seed=29, exact_grid=True)
+    _select_and_check(b, exact=True)
+    b = W.make_decode(seq_lens=[140001, 262147], budget=512, n_plant=32, seed=29, exact_grid=True)
+    _select_and_check(b, exact=True)
+    b = W.make_decode(seq_lens=[1048575, 9001, 3], budget=512, n_plant=32, seed=30,
+                      exact_grid=True, near_tie=[True, False, False])
     _select_and_check(b, exact=True)
 
 

@@ -23,6 +23,13 @@ times the micro-benchmarks of libqsa_probe.so (built on request with
 16x16x32 bf16 MFMA and the sustained HBM read and copy bandwidth, beside the
 published peaks the roofline fractions use.
 
+    python3 -m block_sparse_long_02_amd.measure stats TRACE_CSV OUT_MD STEPS WARMUP
+
+summarizes a `rocprofv3 --kernel-trace` run of bench.py: for the hot kernels
+of the headline prefill step, the mean duration over the timed steps (the
+first WARMUP + STEPS dispatches of the kernel at its first grid size, the
+last STEPS of them), and every kernel of this path by (name, grid size).
+
     python3 -m block_sparse_long_02_amd.measure pmc OUT_MD CSV [CSV ...]
 
 turns counter runs of the same program (any SQ counters, e.g. the MFMA
@@ -227,6 +234,57 @@ def peaks(out_json: str):
     print(json.dumps(res, indent=1))
 
 
+HEADLINE = ["pool_block_keys_kernel", "score_gemm_kernel<2, 4, true, false>", "threshold_kernel",
+            "score_gemm_kernel<2, 8, false, false>", "final_select_kernel", "attend_kernel<true>"]
+
+
+def stats(trace_csv: str, out_md: str, steps: str, warmup: str):
+    """Kernel durations of a bench.py kernel trace (see the module docstring)."""
+    steps, warmup = int(steps), int(warmup)
+    rows = list(csv.DictReader(open(trace_csv)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+
+    def dur(r):
+        return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3   # us
+
+    def grid(r):
+        return (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]))
+
+    # the headline step's boundaries: its first WARMUP + STEPS attention
+    # launches at the chunk's full grid; step i runs from the end of
+    # attention launch i - 1 to the end of attention launch i
+    att = [r for r in rows if "attend_kernel<true>" in r["Kernel_Name"]]
+    g0 = grid(att[0])
+    ends = [int(r["End_Timestamp"]) for r in att if grid(r) == g0][:warmup + steps]
+    windows = list(zip([0] + ends[:-1], ends))[warmup:]
+    lines = ["| kernel | timed steps | mean us | min us | max us |", "|---|---|---|---|---|"]
+    for sub in HEADLINE:
+        d = []
+        for lo, hi in windows:
+            d += [dur(r) for r in rows if sub in r["Kernel_Name"]
+                  and lo < int(r["Start_Timestamp"]) and int(r["End_Timestamp"]) <= hi]
+        if d:
+            lines.append(f"| `{sub}` | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
+    step = [(hi - lo) / 1e3 for lo, hi in windows[1:]]
+    if step:
+        lines.append(f"| (step, attention end to attention end) | {len(step)} | "
+                     f"{sum(step) / len(step):.1f} | {min(step):.1f} | {max(step):.1f} |")
+    lines += ["", "| kernel | grid (x, y) | dispatches | mean us | min us | max us |",
+              "|---|---|---|---|---|---|"]
+    groups = {}
+    for r in rows:
+        if "qsa::" not in r["Kernel_Name"]:
+            continue
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        groups.setdefault((name, grid(r)), []).append(dur(r))
+    for (name, g), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{name}` | {g[0]}, {g[1]} | {len(d)} | {sum(d) / len(d):.1f} | "
+                     f"{min(d):.1f} | {max(d):.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # utilisation ratios from SQ counters (all summed over the GPU's SIMDs or
 # CUs): MFMA pipe busy cycles per SIMD-cycle, VALU issue (4 cycles per wave64
 # instruction) per SIMD-cycle, and the shares of wave cycles spent waiting
@@ -297,6 +355,8 @@ if __name__ == "__main__":
         summarize(*sys.argv[2:5])
     elif sys.argv[1:2] == ["pmc"] and len(sys.argv) >= 4:
         pmc(*sys.argv[2:])
+    elif sys.argv[1:2] == ["stats"] and len(sys.argv) == 6:
+        stats(*sys.argv[2:6])
     else:
         sys.exit("usage: measure.py probe | summarize FETCH_CSV WRITE_CSV OUT_JSON | peaks OUT_JSON"
-                 " | pmc OUT_MD CSV [CSV ...]")
+                 " | pmc OUT_MD CSV [CSV ...] | stats TRACE_CSV OUT_MD STEPS WARMUP")

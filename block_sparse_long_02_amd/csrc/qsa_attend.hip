@@ -367,11 +367,52 @@ combine_kernel(const float* __restrict__ part, int n_rows, uint16_t* __restrict_
 
 namespace {
 
-// splits per (row, KV head) in decode
-#ifndef QSA_DECODE_SPLITS
-#define QSA_DECODE_SPLITS 8
+// Splits per (query row, KV head) of a split-K decode launch: the largest
+// power of two up to 16 that keeps the launch at most kDecodeSlots
+// (row, KV head, split) workgroups.  Few rows (a ragged batch dominated by one
+// long sequence) get many splits, many rows (multi-token decode) few: the
+// per-workgroup setup (list, angles, merge, partials) is then paid as few
+// times as the GPU's workgroup slots allow.
+#ifndef QSA_DECODE_SLOTS
+#define QSA_DECODE_SLOTS 256
 #endif
-constexpr int kDecodeSplits = QSA_DECODE_SPLITS;
+constexpr int kDecodeSlots = QSA_DECODE_SLOTS;
+constexpr int kMaxDecodeSplits = 16;
+
+inline int decode_splits(int64_t n_rows) {
+  int sp = kMaxDecodeSplits;
+  while (sp > 1 && 2 * n_rows * sp > kDecodeSlots) sp >>= 1;
+  return sp;
+}
+
+inline size_t decode_partials_bytes(int64_t n_rows) {
+  return (size_t)n_rows * 2 * decode_splits(n_rows) * qsa::kPartFloats * sizeof(float);
+}
+
+// The split workgroups of a decode launch write (m, l, O) partials to part;
+// the combine pass merges each (row, KV head)'s splits.
+void launch_split_decode(const void* q, const int32_t* cu_q, const int32_t* seq_len, int n_seq,
+                         int n_rows, int one_per_seq, const void* k_cache, const void* v_cache,
+                         int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
+                         const int32_t* sel_count, int budget, void* out, float* lse,
+                         float* part, const qsa::RopeFreq& fr, float softmax_scale,
+                         const qsa::Pages& pg, hipStream_t st) {
+  const int sp = decode_splits(n_rows);
+  hipLaunchKernelGGL(qsa::attend_kernel<false>, dim3(n_rows * 2 * sp), dim3(256), 0, st,
+                     (const uint16_t*)q, cu_q, seq_len, n_seq, n_rows, (const uint16_t*)k_cache,
+                     (const uint16_t*)v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
+                     budget, sp, one_per_seq, (uint16_t*)nullptr, (float*)nullptr, part, fr,
+                     softmax_scale, pg);
+  const dim3 g(n_rows * 2 * qsa::kGroup);
+  const float* cp = part;
+  switch (sp) {
+    case 1: hipLaunchKernelGGL(qsa::combine_kernel<1>, g, dim3(256), 0, st, cp, n_rows, (uint16_t*)out, lse); break;
+    case 2: hipLaunchKernelGGL(qsa::combine_kernel<2>, g, dim3(256), 0, st, cp, n_rows, (uint16_t*)out, lse); break;
+    case 4: hipLaunchKernelGGL(qsa::combine_kernel<4>, g, dim3(256), 0, st, cp, n_rows, (uint16_t*)out, lse); break;
+    case 8: hipLaunchKernelGGL(qsa::combine_kernel<8>, g, dim3(256), 0, st, cp, n_rows, (uint16_t*)out, lse); break;
+    default: hipLaunchKernelGGL(qsa::combine_kernel<16>, g, dim3(256), 0, st, cp, n_rows, (uint16_t*)out, lse); break;
+  }
+}
 
 int check_attend_common(const void* q, const void* k_cache, const void* v_cache,
                         int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
@@ -416,7 +457,7 @@ int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_le
 
 size_t qsa_attend_decode_multi_workspace(int32_t n_q) {
   if (n_q <= 0) return 0;
-  return (size_t)n_q * 2 * kDecodeSplits * qsa::kPartFloats * sizeof(float);
+  return decode_partials_bytes(n_q);
 }
 
 int qsa_attend_decode_multi(const void* q, const int32_t* cu_q, const int32_t* seq_len,
@@ -439,21 +480,16 @@ int qsa_attend_decode_multi(const void* q, const int32_t* cu_q, const int32_t* s
   if (st != QSA_OK) return st;
   if (!workspace || !aligned16(workspace)) return QSA_ERR_INVALID_ARG;
   if (ws_bytes < qsa_attend_decode_multi_workspace(n_q)) return QSA_ERR_WORKSPACE_TOO_SMALL;
-  if ((int64_t)n_q * 2 * kDecodeSplits > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
-  float* part = (float*)workspace;
-  hipLaunchKernelGGL(qsa::attend_kernel<false>, dim3(n_q * 2 * kDecodeSplits), dim3(256), 0,
-                     (hipStream_t)stream, (const uint16_t*)q, cu_q, seq_len, n_seq, n_q,
-                     (const uint16_t*)k_cache, (const uint16_t*)v_cache, kv_seq_stride,
-                     kv_head_stride, sel, sel_count, budget, kDecodeSplits, 0,
-                     (uint16_t*)nullptr, (float*)nullptr, part, fr, softmax_scale, pg);
-  hipLaunchKernelGGL(qsa::combine_kernel<kDecodeSplits>, dim3(n_q * 2 * qsa::kGroup), dim3(256), 0,
-                     (hipStream_t)stream, (const float*)part, n_q, (uint16_t*)out, lse);
+  if ((int64_t)n_q * 2 * qsa::kGroup > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  launch_split_decode(q, cu_q, seq_len, n_seq, n_q, 0, k_cache, v_cache, kv_seq_stride,
+                      kv_head_stride, sel, sel_count, budget, out, lse, (float*)workspace, fr,
+                      softmax_scale, pg, (hipStream_t)stream);
   return launch_status();
 }
 
 size_t qsa_attend_decode_workspace(int32_t n_seq) {
   if (n_seq <= 0) return 0;
-  return (size_t)n_seq * 2 * kDecodeSplits * qsa::kPartFloats * sizeof(float);
+  return decode_partials_bytes(n_seq);
 }
 
 }  // extern "C"
@@ -481,31 +517,28 @@ int check_decode(const void* q, const int32_t* seq_len, int32_t n_seq, const voi
 }
 
 // The split-K partials and the combine pass of a decode step; `part` holds
-// n_seq * 2 * kDecodeSplits partials.
+// decode_partials_bytes(n_seq).
 int launch_decode(const void* q, const int32_t* seq_len, int32_t n_seq, const void* k_cache,
                   const void* v_cache, int64_t kv_seq_stride, int64_t kv_head_stride,
                   const int32_t* sel, const int32_t* sel_count, int32_t budget, void* out,
                   float* lse, float* part, const qsa::RopeFreq& fr, float softmax_scale,
                   const qsa::Pages& pg, void* stream) {
-  hipLaunchKernelGGL(qsa::attend_kernel<false>, dim3(n_seq * 2 * kDecodeSplits), dim3(256), 0,
-                     (hipStream_t)stream, (const uint16_t*)q, (const int32_t*)nullptr, seq_len,
-                     n_seq, n_seq, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
-                     kv_seq_stride, kv_head_stride, sel, sel_count, budget, kDecodeSplits, 1,
-                     (uint16_t*)nullptr, (float*)nullptr, part, fr, softmax_scale, pg);
-  hipLaunchKernelGGL(qsa::combine_kernel<kDecodeSplits>, dim3(n_seq * 2 * qsa::kGroup), dim3(256), 0,
-                     (hipStream_t)stream, (const float*)part, n_seq, (uint16_t*)out, lse);
+  launch_split_decode(q, nullptr, seq_len, n_seq, n_seq, 1, k_cache, v_cache, kv_seq_stride,
+                      kv_head_stride, sel, sel_count, budget, out, lse, part, fr, softmax_scale,
+                      pg, (hipStream_t)stream);
   return qsa_host::launch_status();
 }
 
 // ---------------------------------------------------- allocation-free decode
 // The partials of qsa_attend_decode_noalloc live in this file-scope device
 // array instead of a caller's workspace: every GPU the library runs on holds
-// its own copy (25.4 MB for QSA_NOALLOC_MAX_SEQ = 128 sequences) until the
-// process ends.  Host code never passes the array's name to a kernel (on the
+// its own copy until the process ends.  A launch of up to
+// QSA_NOALLOC_MAX_SEQ = 128 rows writes at most kDecodeSlots partials
+// (3.2 MB).  Host code never passes the array's name to a kernel (on the
 // host it is only a stand-in symbol); it asks the runtime for the array's
 // address on each device once, with that device current, and uses that.
-constexpr size_t kNoAllocFloats =
-    (size_t)QSA_NOALLOC_MAX_SEQ * 2 * kDecodeSplits * qsa::kPartFloats;
+static_assert(2 * QSA_NOALLOC_MAX_SEQ <= kDecodeSlots, "the array holds every split of 128 rows");
+constexpr size_t kNoAllocFloats = (size_t)kDecodeSlots * qsa::kPartFloats;
 
 }  // namespace
 

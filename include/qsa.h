@@ -281,9 +281,10 @@ int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_le
 /*
  * a7 -- split-K decode attention plus combine.  Same mathematics as
  * qsa_attend_prefill for one query per sequence at position seq_len[s]-1
- * (row s of q, sel, out, lse).  The selected set is split across workgroups;
- * partial (max, sum, output) triples go to the workspace and a combine pass
- * merges them.  Needs qsa_attend_decode_workspace(n_seq) bytes.
+ * (row s of q, sel, out, lse).  The selected set is split across workgroups
+ * (1 to 16 per row and KV head, fewer for larger batches); partial (max,
+ * sum, output) triples go to the workspace and a combine pass merges them.
+ * Needs qsa_attend_decode_workspace(n_seq) bytes.
  */
 size_t qsa_attend_decode_workspace(int32_t n_seq);
 int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq,
@@ -302,9 +303,9 @@ int qsa_attend_decode(const void* q, const int32_t* seq_len, int32_t n_seq,
  * mathematics, kernels and results (bit for bit) as qsa_attend_decode.
  *
  * The partials live in a device array inside the library, one copy per GPU
- * it runs on, held until the process ends: n_seq * 2 * 8 * 12,416 bytes, at
- * most QSA_NOALLOC_MAX_SEQ = 128 sequences (25.4 MB).  The call allocates
- * nothing.  Its first call on a device looks the array up with that device
+ * it runs on, held until the process ends: 256 partials of 12,416 bytes
+ * (3.2 MB), enough for every split of QSA_NOALLOC_MAX_SEQ = 128 sequences.
+ * The call allocates nothing.  Its first call on a device looks the array up with that device
  * current, so `stream` must belong to the current device (or be NULL).  Every
  * call on one GPU shares that array: calls that overlap on one GPU (on
  * different streams, or from different threads without ordering) race, so

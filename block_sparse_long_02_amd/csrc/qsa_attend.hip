@@ -59,7 +59,7 @@ struct AttnShared {
 // mode kFinal: one workgroup per (row, KV head) writes out / lse.
 // otherwise: n_splits workgroups per (row, KV head) write partials.
 template <bool kFinal>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, kFinal ? 2 : 1)
 attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
               const int32_t* __restrict__ seq_len, int n_seq, int n_rows,
               const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
@@ -126,6 +126,9 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   // lane is token row `col` of the half; V / P k-slices: micro-block
   // t*kTileMB + 4hv + grp.
   u32x4 kh[kHalves][8], vh[kHalves][8];
+  // split-K partials (decode) run one wave per SIMD, which leaves the
+  // registers for the staggered loads below
+  constexpr bool kStagger = !kFinal;
   auto load_k = [&](int t) {
 #pragma unroll
     for (int hv = 0; hv < kHalves; ++hv) {
@@ -144,6 +147,16 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
       for (int c = 0; c < 8; ++c) vh[hv][c] = ldg16(vp + 128 * c);
     }
   };
+  // ---- query fragment: B operand of S^T = K Q^T.  Lane holds head `col` of
+  // this KV group, dims 32*ks + 8*grp .. +7.  Heads 12..15 are zero padding:
+  // their address is clamped to a real head and the value replaced by zero.
+  // Issued first, so that its latency overlaps the block-list load.
+  u32x4 qf[8];
+  const int head = g * kGroup + min(col, kGroup - 1);
+  const uint16_t* qrow = q + ((int64_t)row * kQHeads + head) * kHeadDim + 8 * grp;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = ldg16(qrow + 32 * ks);
+
   // ---- block list and the query's rotary angles into LDS
   for (int i = threadIdx.x; i < cnt; i += 256) {
     int id = sel[(int64_t)row * budget + i];
@@ -159,18 +172,18 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   }
   __syncthreads();
 
-  // ---- query fragment: B operand of S^T = K Q^T.  Lane holds head `col` of
-  // this KV group, dims 32*ks + 8*grp .. +7.  Heads 12..15 are zero padding.
-  u32x4 qf[8];
-  // heads 12..15 of the tile are padding: their address is clamped to a real
-  // head and the value replaced by zero
-  const int head = g * kGroup + min(col, kGroup - 1);
-  const uint16_t* qrow = q + ((int64_t)row * kQHeads + head) * kHeadDim + 8 * grp;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const u32x4 v = ldg16(qrow + 32 * ks);
-    qf[ks] = col < kGroup ? v : u32x4{0, 0, 0, 0};
+  // The K and V loads are staggered by half a tile: the keys of tile t + 1
+  // are requested as soon as the logits of tile t are formed, the values of
+  // tile t + 1 once P V of tile t has consumed vh.  Each wave thus always has
+  // one of the two operands in flight while it computes.
+  if (kStagger && t_begin < t_end) {
+    load_k(t_begin);
+    load_v(t_begin);
   }
+
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    if (col >= kGroup) qf[ks] = u32x4{0, 0, 0, 0};
   // The rotated dims 0..63 are carried as two bf16 terms (value and
   // residual), so the rotation adds no bf16 rounding to the logits; dims
   // 64..255 are the bf16 inputs themselves.
@@ -199,8 +212,10 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
 
   for (int t = t_begin; t < t_end; ++t) {
     const int base = t * kTileMB;
-    load_k(t);
-    load_v(t);
+    if (!kStagger) {
+      load_k(t);
+      load_v(t);
+    }
 
     // sc[hv][i]: token i of micro-block slot base + 4hv + grp, head col
     f32x4 sc[kHalves];
@@ -213,6 +228,7 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
       sc[hv] = mfma_16x16x32(kh[hv][0], ql[0], sc[hv]);
       sc[hv] = mfma_16x16x32(kh[hv][1], ql[1], sc[hv]);
     }
+    if (kStagger && t + 1 < t_end) load_k(t + 1);
     float x[4 * kHalves];
 #pragma unroll
     for (int hv = 0; hv < kHalves; ++hv)
@@ -287,6 +303,7 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
         o[2 * c + 1] = mfma_16x16x32(pl, bo, o[2 * c + 1]);
       }
     }
+    if (kStagger && t + 1 < t_end) load_v(t + 1);
   }
 
   // ---- merge the 4 waves in LDS

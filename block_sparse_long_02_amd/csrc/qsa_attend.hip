@@ -72,7 +72,13 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
 
-  const int wg = blockIdx.x;
+  // Split-K launches put each XCD on a contiguous range of (row, KV head,
+  // split) items: the dispatcher deals consecutive workgroup ids to the 8
+  // XCDs in turn, so without this the rows of one sequence (the query tokens
+  // of a multi-token decode) would each run on another XCD and could not
+  // share the blocks they have in common through one L2.
+  const int wg = (kFinal || (gridDim.x & 7)) ? (int)blockIdx.x
+                                             : (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3));
   const int split = wg % n_splits;
   const int g = (wg / n_splits) & 1;
   const int row = wg / (2 * n_splits);

@@ -1177,6 +1177,13 @@ final_select_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict_
 constexpr int kDenseList = 2560;
 constexpr int kDenseExtra = 768;
 constexpr int kDensePassQ = 8192;   // quads per pass (32768 scores; 32 per thread)
+// Rows longer than kLongRow scores are compacted in pieces of one pass each,
+// one workgroup per piece, into per-piece segments of the row's list (in
+// block order, so the list needs no sort); a second launch selects from the
+// segments.  A piece's workgroup finds tau_s from the samples itself.
+constexpr int kPieceScores = 4 * kDensePassQ;
+constexpr int kLongRow = 2 * kPieceScores;
+constexpr int kMaxPieces = 64;
 
 struct DenseShared {
   u32x4 rowq[kDensePassQ];
@@ -1247,11 +1254,15 @@ select_dense_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict_
                     int n_seq, int max_blocks, int budget, const uint32_t* __restrict__ dense,
                     int64_t dense_stride, const uint32_t* __restrict__ dsmp,
                     int64_t dsmp_stride, int32_t* __restrict__ sel,
-                    int32_t* __restrict__ sel_count) {
+                    int32_t* __restrict__ sel_count, int n_pieces, u32x2* __restrict__ seg,
+                    int32_t* __restrict__ segcnt) {
   __shared__ DenseShared sh;
   const int tid = threadIdx.x;
-  const int row = blockIdx.x;
+  const int row = blockIdx.x / n_pieces, piece = blockIdx.x - row * n_pieces;
   const RowGeom g = row_geom(cu_q, seq_len, n_seq, row, max_blocks);
+  // split rows: this workgroup compacts one piece; other rows: piece 0 does all
+  const bool split = seg != nullptr && g.ok && g.n_c > kLongRow;
+  if (split ? piece * kPieceScores >= g.n_c : piece != 0) return;
   int32_t* out = sel + (int64_t)row * budget;
   if (!g.ok) {
     for (int i = tid; i < budget; i += 256) out[i] = -1;
@@ -1264,7 +1275,7 @@ select_dense_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict_
   const uint32_t* drow = dense + (int64_t)row * dense_stride;
   const u32x4* drow4 = reinterpret_cast<const u32x4*>(drow);
   const uint32_t* srow = dsmp + (int64_t)row * dsmp_stride;
-  if (tid == 0) sel_count[row] = k;
+  if (tid == 0 && !split) sel_count[row] = k;
 
   if (n <= kDenseList) {   // short rows: the whole row is the list
     for (int i = tid; i < n; i += 256) { sh.u.l.key[i] = drow[i]; sh.u.l.pos[i] = i; }
@@ -1288,7 +1299,10 @@ select_dense_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict_
 #pragma unroll
     for (int u = 0; u < kQ; ++u) kv[u] = drow4[min(q0 + 256 * u + tid, nq - 1)];
   };
-  load_pass(0);
+  // quads of this workgroup: the whole row, or one piece of a split row
+  const int q_first = split ? piece * kDensePassQ : 0;
+  const int q_end = split ? min(nq, q_first + kDensePassQ) : nq;
+  load_pass(q_first);
   uint32_t tau_s;
   if (ns <= 2048) {
 #pragma unroll
@@ -1303,8 +1317,8 @@ select_dense_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict_
 
   // compaction; tau_s = 0 would pass every score (more than the list holds)
   int run = tau_s == 0 ? kDenseList + 1 : 0;
-  for (int q0 = 0; q0 < nq && tau_s != 0; q0 += kDensePassQ) {
-    if (q0 > 0) load_pass(q0);
+  for (int q0 = q_first; q0 < q_end && tau_s != 0; q0 += kDensePassQ) {
+    if (q0 > q_first) load_pass(q0);
     // stage: quad ql of the pass goes to thread ql/32's run, slot swizzled by
     // the owner so that both the writes here and the reads below are free of
     // bank conflicts; scores past n become 0 (never >= tau_s >= 1)
@@ -1348,9 +1362,72 @@ select_dense_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict_
     __syncthreads();   // rowq is rewritten by the next pass
   }
 
+  if (split) {
+    // the piece's entries, in block order, and their count (above
+    // kDenseList: the list cannot hold the row's candidates)
+    u32x2* sp = seg + ((int64_t)row * n_pieces + piece) * kDenseList;
+    const int m = run <= kDenseList ? run : 0;
+    for (int i = tid; i < m; i += 256) sp[i] = u32x2{sh.u.l.key[i], (uint32_t)sh.u.l.pos[i]};
+    if (tid == 0) segcnt[(int64_t)row * n_pieces + piece] = run;
+    return;
+  }
   if (run >= k && run <= kDenseList) {
     select_dense_list(run, k, sh, out, budget);
   } else {
+    select_ordered([&](int i) { return drow[i]; }, [](int i) { return i; }, n, k, sh.hist, sh.tmp,
+                   sh.res, sh.wcnt, out, budget);
+  }
+}
+
+// Second step for split rows: the pieces' segments, concatenated in piece
+// order, form the row's list of scores >= tau_s in block order; its exact
+// top K is emitted as for an unsplit row.  A piece that overflowed, or a
+// list short of K or longer than kDenseList, falls back to the exact ordered
+// select over the row's dense scores.
+__global__ void __launch_bounds__(256)
+dense_list_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
+                  int n_seq, int max_blocks, int budget, const uint32_t* __restrict__ dense,
+                  int64_t dense_stride, int n_pieces, const u32x2* __restrict__ seg,
+                  const int32_t* __restrict__ segcnt, int32_t* __restrict__ sel,
+                  int32_t* __restrict__ sel_count) {
+  __shared__ DenseShared sh;
+  __shared__ int s_off[kMaxPieces + 1];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const RowGeom g = row_geom(cu_q, seq_len, n_seq, row, max_blocks);
+  if (!g.ok || g.n_c <= kLongRow) return;   // done by select_dense_kernel
+  const int n = g.n_c;
+  const int k = min(budget, n);
+  const int np = (n + kPieceScores - 1) / kPieceScores;
+  int32_t* out = sel + (int64_t)row * budget;
+  if (tid == 0) {
+    int tot = 0;
+    bool ok = true;
+    for (int p = 0; p < np; ++p) {
+      const int c = segcnt[(int64_t)row * n_pieces + p];
+      ok = ok && c >= 0 && c <= kDenseList;
+      s_off[p] = tot;
+      tot += ok ? c : 0;
+    }
+    s_off[np] = (ok && tot >= k && tot <= kDenseList) ? tot : -1;
+    sel_count[row] = k;
+  }
+  __syncthreads();
+  const int c = s_off[np];
+  if (c >= 0) {
+    for (int p = 0; p < np; ++p) {
+      const int b0 = s_off[p], cnt = s_off[p + 1] - b0;   // s_off[np] = c
+      const u32x2* sp = seg + ((int64_t)row * n_pieces + p) * kDenseList;
+      for (int i = tid; i < cnt; i += 256) {
+        const u32x2 e = sp[i];
+        sh.u.l.key[b0 + i] = e[0];
+        sh.u.l.pos[b0 + i] = (int)e[1];
+      }
+    }
+    __syncthreads();
+    select_dense_list(c, k, sh, out, budget);
+  } else {
+    const uint32_t* drow = dense + (int64_t)row * dense_stride;
     select_ordered([&](int i) { return drow[i]; }, [](int i) { return i; }, n, k, sh.hist, sh.tmp,
                    sh.res, sh.wcnt, out, budget);
   }
@@ -1364,6 +1441,9 @@ struct IndexWs {
   uint16_t* samples;
   uint32_t* dense;
   uint32_t* dsmp;
+  u32x2* seg;          // split decode rows: per-piece list segments
+  int32_t* segcnt;
+  int n_pieces;
   int ns_stride;
   int64_t dense_stride, dsmp_stride;
   size_t bytes;
@@ -1374,6 +1454,14 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Small tiles (<= 4 queries per sequence) use dense scores; otherwise the
 // sampled-threshold path with per-row candidate lists.
 inline bool use_dense(int max_q_len) { return max_q_len <= 4; }
+
+// Pieces per row of a dense select launch: 1 unless rows may exceed kLongRow
+// scores (and the pieces fit the list kernel's table).
+inline int dense_pieces(int max_blocks) {
+  if (max_blocks <= kLongRow) return 1;
+  const int np = (max_blocks + kPieceScores - 1) / kPieceScores;
+  return np <= kMaxPieces ? np : 1;
+}
 
 inline IndexWs index_ws_layout(void* base, int n_q, int max_q_len, int max_blocks) {
   IndexWs ws = {};
@@ -1388,6 +1476,13 @@ inline IndexWs index_ws_layout(void* base, int n_q, int max_q_len, int max_block
     off = align256(off + (size_t)n_q * ws.dense_stride * 4);
     ws.dsmp = (uint32_t*)(p + off);
     off = align256(off + (size_t)n_q * ws.dsmp_stride * 4);
+    ws.n_pieces = dense_pieces(max_blocks);
+    if (ws.n_pieces > 1) {
+      ws.seg = (u32x2*)(p + off);
+      off = align256(off + (size_t)n_q * ws.n_pieces * kDenseList * 8);
+      ws.segcnt = (int32_t*)(p + off);
+      off = align256(off + (size_t)n_q * ws.n_pieces * 4);
+    }
   } else {
     ws.thresh = (uint32_t*)(p + off); off = align256(off + (size_t)n_q * 4);
     ws.cnt = (int32_t*)(p + off); off = align256(off + (size_t)n_q * 4);
@@ -1448,9 +1543,16 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
       if (pg.table) launch(score_dense_kernel<true>);
       else launch(score_dense_kernel<false>);
     }
-    hipLaunchKernelGGL(select_dense_kernel, dim3(n_q), dim3(256), 0, st, cu_q, seq_len, n_seq,
-                       max_blocks, budget, (const uint32_t*)ws.dense, ws.dense_stride,
-                       (const uint32_t*)ws.dsmp, ws.dsmp_stride, sel, sel_count);
+    const int np = ws.n_pieces;
+    if ((int64_t)n_q * np > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(select_dense_kernel, dim3((unsigned)((int64_t)n_q * np)), dim3(256), 0, st,
+                       cu_q, seq_len, n_seq, max_blocks, budget, (const uint32_t*)ws.dense,
+                       ws.dense_stride, (const uint32_t*)ws.dsmp, ws.dsmp_stride, sel, sel_count,
+                       np, np > 1 ? ws.seg : (u32x2*)nullptr, ws.segcnt);
+    if (np > 1)
+      hipLaunchKernelGGL(dense_list_kernel, dim3(n_q), dim3(256), 0, st, cu_q, seq_len, n_seq,
+                         max_blocks, budget, (const uint32_t*)ws.dense, ws.dense_stride, np,
+                         (const u32x2*)ws.seg, (const int32_t*)ws.segcnt, sel, sel_count);
     return launch_status();
   }
 

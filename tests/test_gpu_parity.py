@@ -267,6 +267,37 @@ def test_index_select_long_row_fallbacks():
     assert np.array_equal(r.sel.cpu().numpy()[0], np.arange(0, 8192, 16))
 
 
+def test_index_select_split_row_fallbacks():
+    # rows above 65,536 blocks are compacted in pieces of 32,768 scores.
+    # All ties: every piece overflows its segment, and the ordered select
+    # over the row's scores keeps the lowest 512 ids; beside it a short row
+    # of the same launch takes the unsplit path
+    b = W.make_decode(seq_lens=[300003, 5001], budget=512, n_plant=0, seed=33)
+    b.idx_k[0] = b.idx_k[0, 0].clone()
+    r, _, _ = _select_and_check(b, exact=True)
+    assert np.array_equal(r.sel.cpu().numpy()[0], np.arange(512))
+    # only sampled blocks below 8192 score high: piece 0 lists 80 of them,
+    # the others none, so the list is short of K and the row falls back
+    b = W.make_decode(seq_lens=[300001], budget=512, n_plant=0, seed=34)
+    u = b.idx_q[0].float().sum(0)
+    u = u / u.norm()
+    for blk in range(0, 8192, 16):
+        b.idx_k[0, 4 * blk:4 * blk + 4] = (math.sqrt(128) * (1 + blk / 1e4) * u).to(torch.bfloat16)
+    r, _, _ = _select_and_check(b, exact=True)
+    assert np.array_equal(r.sel.cpu().numpy()[0], np.arange(0, 8192, 16))
+    # high scores in all three pieces, one piece holding most: the
+    # segments concatenate in block order
+    b = W.make_decode(seq_lens=[300005], budget=512, n_plant=0, seed=35)
+    u = b.idx_q[0].float().sum(0)
+    u = u / u.norm()
+    hot = sorted(set(list(range(40000, 40000 + 400)) + list(range(1000, 60000, 600)) +
+                     list(range(70000, 75000, 500))))
+    for blk in hot:
+        b.idx_k[0, 4 * blk:4 * blk + 4] = (math.sqrt(128) * (1 + blk / 1e5) * u).to(torch.bfloat16)
+    r, _, _ = _select_and_check(b, exact=True)
+    assert set(hot) <= set(r.sel.cpu().numpy()[0].tolist())
+
+
 def test_index_select_decode_rule():
     b = W.make_decode(seq_lens=[131073, 20001, 4100, 99999], budget=512, n_plant=32, seed=24)
     _, _, kinds = _select_and_check(b)

@@ -834,18 +834,50 @@ __device__ uint32_t kth_largest_global(const uint32_t* __restrict__ p, int n, in
   }
 }
 
-// Ascending bitonic sort of 512 ints in LDS by 256 threads.
-__device__ void bitonic_sort_512(int* a) {
-  for (int k2 = 2; k2 <= 512; k2 <<= 1) {
-    for (int j = k2 >> 1; j > 0; j >>= 1) {
-      const int t = threadIdx.x;
-      const int i = 2 * t - (t & (j - 1));
-      const int p = i + j;
-      const bool up = (i & k2) == 0;
-      const int x = a[i], y = a[p];
-      if ((x > y) == up) { a[i] = y; a[p] = x; }
-      __syncthreads();
+// The k (<= kMaxBudget) distinct ids in ids[] (each < n), written to
+// out[0..k) in ascending order by a 256-thread workgroup: ids are bucketed on
+// their top 11 bits (counts, a scan, a scatter through LDS atomics), and an
+// id's place is its bucket's start plus the number of smaller ids in its
+// bucket (a bucket holds a few ids).  hist: kBins ints; tmp: k ints.
+__device__ void sort_ids_to(const int* ids, int k, int n, int* hist, int* tmp, int* scan_tmp,
+                            int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  const int top = 32 - __clz((n - 1) | 1);          // bits of the largest id
+  const int shift = top > 11 ? top - 11 : 0;
+  const int nb = ((n - 1) >> shift) + 1;            // <= kBins
+  for (int b = tid; b < nb; b += 256) hist[b] = 0;
+  __syncthreads();
+  for (int i = tid; i < k; i += 256) atomicAdd(&hist[ids[i] >> shift], 1);
+  __syncthreads();
+  // bucket starts: thread t owns buckets [per*t, per*t + per)
+  constexpr int per = kBins / 256;
+  const int b0 = tid * per;
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) local += b0 + j < nb ? hist[b0 + j] : 0;
+  int total;
+  int run = block_excl_scan_256(local, scan_tmp, total);
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    if (b0 + j < nb) {
+      const int h = hist[b0 + j];
+      hist[b0 + j] = run;
+      run += h;
     }
+  }
+  __syncthreads();
+  for (int i = tid; i < k; i += 256) {
+    const int id = ids[i];
+    tmp[atomicAdd(&hist[id >> shift], 1)] = id;   // hist[b] ends as bucket b's end
+  }
+  __syncthreads();
+  for (int p = tid; p < k; p += 256) {
+    const int id = tmp[p];
+    const int b = id >> shift;
+    const int s0 = b > 0 ? hist[b - 1] : 0, s1 = hist[b];
+    int rank = s0;
+    for (int q = s0; q < s1; ++q) rank += tmp[q] < id ? 1 : 0;
+    out[rank] = id;
   }
 }
 
@@ -1004,10 +1036,10 @@ __device__ void exact_select_recompute(const uint16_t* __restrict__ q4, const fl
 // Exact top-k (score desc, block asc) of an unordered list of c >= k
 // candidates held in LDS (key[], idx[]), written to out[0..k) in ascending
 // block order and -1 up to budget.  Radix select on the score key, then on
-// the block id among ties at the threshold; bitonic sort of the k ids.
+// the block id among ties at the threshold; the k ids sorted by buckets.
 __device__ void select_from_list(const uint32_t* key, const int* idx, int c, int k, int* ids,
-                                 int* n_out, const KthLds& lds, int32_t* __restrict__ out,
-                                 int budget) {
+                                 int* ids_tmp, int n_ids, int* n_out, const KthLds& lds,
+                                 int32_t* __restrict__ out, int budget) {
   int* hist = lds.hist;
   int* tmp = lds.tmp;
   int* res = lds.res;
@@ -1043,10 +1075,8 @@ __device__ void select_from_list(const uint32_t* key, const int* idx, int c, int
     }
   }
   __syncthreads();
-  for (int i = k + threadIdx.x; i < kMaxBudget; i += 256) ids[i] = 0x7FFFFFFF;
-  __syncthreads();
-  bitonic_sort_512(ids);
-  for (int i = threadIdx.x; i < budget; i += 256) out[i] = i < k ? ids[i] : -1;
+  if (k > 0) sort_ids_to(ids, k, n_ids, hist, ids_tmp, tmp, out);
+  for (int i = k + threadIdx.x; i < budget; i += 256) out[i] = -1;
 }
 
 // Sum over the 64 lanes of a wave.
@@ -1115,6 +1145,7 @@ struct SelectShared {
   int hist[kBins];
   uint32_t bin[kFinishCap];
   int ids[kMaxBudget];
+  int ids_tmp[kMaxBudget];
   int tmp[8];
   int res[2];
   int n_out;
@@ -1152,7 +1183,7 @@ final_select_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict_
     sh.idx[i] = (int)e[1];
   }
   __syncthreads();
-  select_from_list(sh.key, sh.idx, c, k, sh.ids, &sh.n_out,
+  select_from_list(sh.key, sh.idx, c, k, sh.ids, sh.ids_tmp, g.n_c, &sh.n_out,
                    KthLds{sh.hist, sh.bin, sh.tmp, sh.res, &sh.bin_n}, out, budget);
   if (threadIdx.x == 0) sel_count[row] = k;
 }

@@ -17,12 +17,17 @@ from .workloads import QSABatch, R, v_cache_layout
 
 def piece_bounds(n: int, parts: int) -> list[int]:
     """Row boundaries [0, ..., n] of a chunk cut into `parts` consecutive
-    pieces: the first an eighth of the rows, the rest equal (some pieces may
-    be empty when n < parts)."""
+    pieces: the first an eighth of the rows, so that the attention starts
+    early; with three or more pieces the last an eighth too, so that the
+    attention left running alone at the end is short; the pieces between
+    equal (some pieces may be empty when n < parts)."""
     if parts <= 1:
         return [0, n]
     first = (n + 7) // 8
-    return [0] + [first + (n - first) * i // (parts - 1) for i in range(parts)]
+    last = n // 8 if parts >= 3 else 0
+    mid = parts - 1 - (1 if parts >= 3 else 0)
+    span = n - first - last
+    return [0] + [first + span * i // mid for i in range(mid + 1)] + ([n] if parts >= 3 else [])
 
 
 class QSARunner:
@@ -183,8 +188,7 @@ class QSARunner:
         """One prefill step with the chunk's query rows in `parts` consecutive
         pieces: piece i's attention runs on a second stream while piece i+1
         is selected, so the memory-bound attention overlaps the MFMA-bound
-        score GEMM.  The first piece is an eighth of the rows, so that the
-        attention starts early; the rest are equal.  Same calls on the same
+        score GEMM (pieces as piece_bounds cuts them).  Same calls on the same
         rows, so the same results as step().  One-sequence prefill batches
         only."""
         assert not (self.decode or self.mtp) and self.n_seq == 1, "one-sequence prefill"

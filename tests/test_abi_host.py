@@ -240,14 +240,16 @@ def test_probe_library_exports_and_validates():
 
 def test_pipeline_piece_bounds():
     """The overlapped prefill schedule covers every row once, in order, with
-    a short first piece."""
+    a short first piece and, from three pieces on, a short last one."""
     from block_sparse_long_02_amd.runner import piece_bounds
     for n in (1, 3, 7, 8, 333, 32768):
         for parts in (1, 2, 3, 4, 7):
             b = piece_bounds(n, parts)
             assert b[0] == 0 and b[-1] == n and len(b) == max(parts, 1) + 1
             assert all(x <= y for x, y in zip(b, b[1:]))
-    assert piece_bounds(32768, 4) == [0, 4096, 13653, 23210, 32768]
+    assert piece_bounds(32768, 4) == [0, 4096, 16384, 28672, 32768]
+    assert piece_bounds(32768, 5) == [0, 4096, 12288, 20480, 28672, 32768]
+    assert piece_bounds(32768, 2) == [0, 4096, 32768]
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -112,7 +112,8 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   const int n_tiles = (n_mb + kTileMB - 1) / kTileMB;
   const int parts = n_splits * kWaves;
   const int my_part = split * kWaves + wave;
-  // even split: part p takes tiles [p*n/parts, (p+1)*n/parts)
+  // split decode: part p takes tiles [p*n/parts, (p+1)*n/parts) (prefill
+  // interleaves its waves' tiles instead, below)
   const int t_begin = (int)((int64_t)my_part * n_tiles / parts);
   const int t_end = (int)((int64_t)(my_part + 1) * n_tiles / parts);
   const int tail_slot = tail_len > 0 ? cnt : -1;
@@ -216,7 +217,16 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     if (col < kGroup) { qf[0] = r0; qf[1] = r1; ql[0] = l0; ql[1] = l1; }
   }
 
-  for (int t = t_begin; t < t_end; ++t) {
+  // Prefill: the waves take the row's tiles in turn (wave w: tiles w, w+4,
+  // ...), so the row sweeps its ascending list four tiles at a time.  Rows
+  // that run together share many blocks at nearby ranks of their lists; the
+  // faster sweep requests a shared block closer in time, while it is still
+  // in L2 (1M chunk: 12.53 -> 12.24 ms against contiguous quarters).  Split
+  // decode keeps contiguous ranges for its staggered loads.
+  const int t_first = kFinal ? wave : t_begin;
+  const int t_stop = kFinal ? n_tiles : t_end;
+  const int t_step = kFinal ? kWaves : 1;
+  for (int t = t_first; t < t_stop; t += t_step) {
     const int base = t * kTileMB;
     if (!kStagger) {
       load_k(t);

@@ -53,12 +53,18 @@ __device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
 constexpr int kWaitVmem16 = 0x4F70;   // vector memory loads in flight <= 16
 constexpr int kWaitVmem0 = 0x0F70;    // no vector memory load in flight
 constexpr int kWaitLds0 = 0xC07F;     // no LDS access in flight
+// Time-aligned prefill: expected sweep time per tile of a wave's share, in
+// ticks of the 100 MHz constant clock (1M chunk: 16 tiles per wave, 10.8 ms
+// at 6,000 ticks per sweep against 12.0 ms with the ordered sweep)
+constexpr int kSweepTicksPerTile = 400;
 
 struct AttnShared {
   int list[kMaxList + 8];            // micro-block ids, tail block last
   float cs[kRopeDim / 2][2];         // cos, sin of the query position
   float m[kWaves][16];
   float l[kWaves][16];
+  int sweep_at;                      // time-aligned prefill: the block id to start at
+  int k0;                            // ... and the list index of the first id at or past it
   union {
     float o[kWaves][kGroup][kHeadDim];   // the waves' outputs, merged at the end
     u32x4 kst[kWaves][kHalves][8][64];   // prefill: a tile's keys, per wave and lane
@@ -76,7 +82,7 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
               const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int budget,
               int n_splits, int one_per_seq, uint16_t* __restrict__ out,
               float* __restrict__ lse, float* __restrict__ part, RopeFreq fr, float sm_scale,
-              Pages pg) {
+              Pages pg, int aligned) {
   __shared__ AttnShared sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -145,6 +151,12 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   // split-K partials (decode) run one wave per SIMD, which leaves the
   // registers for the staggered loads below
   constexpr bool kStagger = !kFinal;
+  // list slot i of the sweep: selected blocks rotated by k0, the tail last
+  int k0 = 0;
+  auto lst = [&](int i) {
+    if (i < cnt) { i += k0; if (i >= cnt) i -= cnt; }
+    return sh.list[i];
+  };
   auto load_k = [&](int t) {
 #pragma unroll
     for (int hv = 0; hv < kHalves; ++hv) {
@@ -157,7 +169,7 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   auto load_v = [&](int t) {
 #pragma unroll
     for (int hv = 0; hv < kHalves; ++hv) {
-      const int idv = sh.list[min(t * kTileMB + 4 * hv + grp, n_mb - 1)];
+      const int idv = lst(min(t * kTileMB + 4 * hv + grp, n_mb - 1));
       const uint16_t* vp = vbase + (int64_t)idv * (kBlock * kHeadDim) + 8 * col;
 #pragma unroll
       for (int c = 0; c < 8; ++c) vh[hv][c] = ldg16(vp + 128 * c);
@@ -171,7 +183,7 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   auto dma_k = [&](int t) {
 #pragma unroll
     for (int hv = 0; hv < kHalves; ++hv) {
-      const int idk = sh.list[min(t * kTileMB + 4 * hv + (col >> 2), n_mb - 1)];
+      const int idk = lst(min(t * kTileMB + 4 * hv + (col >> 2), n_mb - 1));
       const uint16_t* kp = kbase + ((int64_t)idk * kBlock + (col & 3)) * kHeadDim + 8 * grp;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
@@ -190,11 +202,36 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) qf[ks] = ldg16(qrow + 32 * ks);
 
+  // ---- time-aligned prefill: the rows in flight sweep the cache together.
+  // A row normally walks its ascending list from the start, so rows that
+  // start at different times are at different block ids at any moment and
+  // rarely meet on a shared block while it is still in L2.  Here a row starts
+  // at the block id a shared clock points to (the clock runs over the row's
+  // candidates once per expected sweep time) and wraps around: the rows in
+  // flight are then near the same block ids together.  The row's blocks are
+  // the same; only the order of its float32 sums changes with timing.
+  const bool timed = kFinal && aligned;
+  if (timed) {
+    if (threadIdx.x == 0) {
+      const int64_t period = (int64_t)max((n_tiles + kWaves - 1) / kWaves, 1) * kSweepTicksPerTile;
+      const uint64_t clk = __builtin_amdgcn_s_memrealtime();   // constant 100 MHz
+      sh.sweep_at = (int)(((int64_t)(clk % (uint64_t)period) * n_c) / period);
+      sh.k0 = 0;
+    }
+    __syncthreads();
+  }
+
   // ---- block list and the query's rotary angles into LDS
   for (int i = threadIdx.x; i < cnt; i += 256) {
     int id = sel[(int64_t)row * budget + i];
     id = min(max(id, 0), n_c - 1);   // ids come ascending from the selection
     sh.list[i] = pg.table ? (int)phys_block(pg, s, id) : id;
+    if (timed) {
+      // list index of the first id at or past sweep_at = ids below it
+      const uint64_t below = __ballot(id < sh.sweep_at);
+      const uint64_t active = __ballot(1);
+      if (lane == __builtin_ctzll(active) && below) atomicAdd(&sh.k0, __popcll(below));
+    }
   }
   if (threadIdx.x == 0 && tail_len > 0) sh.list[cnt] = pg.table ? (int)phys_block(pg, s, n_c) : n_c;
   if (threadIdx.x < kRopeDim / 2) {
@@ -204,6 +241,8 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     sh.cs[threadIdx.x][1] = (float)sd;
   }
   __syncthreads();
+
+  k0 = timed ? sh.k0 % max(cnt, 1) : 0;
 
   // The K and V loads are staggered by half a tile: the keys of tile t + 1
   // are requested as soon as the logits of tile t are formed, the values of
@@ -487,7 +526,7 @@ void launch_split_decode(const void* q, const int32_t* cu_q, const int32_t* seq_
                      (const uint16_t*)q, cu_q, seq_len, n_seq, n_rows, (const uint16_t*)k_cache,
                      (const uint16_t*)v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
                      budget, sp, one_per_seq, (uint16_t*)nullptr, (float*)nullptr, part, fr,
-                     softmax_scale, pg);
+                     softmax_scale, pg, 0);
   const dim3 g(n_rows * 2 * qsa::kGroup);
   const float* cp = part;
   switch (sp) {
@@ -511,16 +550,14 @@ int check_attend_common(const void* q, const void* k_cache, const void* v_cache,
   return QSA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_len, int32_t n_seq,
-                       int32_t n_q, int32_t max_q_len, const void* k_cache, const void* v_cache,
-                       int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
-                       const int32_t* sel_count, int32_t budget, void* out, float* lse,
-                       const double* inv_freq, float softmax_scale, const int32_t* block_table,
-                       int64_t table_stride, int32_t page_tokens, void* stream) {
+// aligned: the time-aligned sweep of qsa_attend_prefill_aligned
+int attend_prefill_launch(int aligned, const void* q, const int32_t* cu_q,
+                          const int32_t* seq_len, int32_t n_seq, int32_t n_q, int32_t max_q_len,
+                          const void* k_cache, const void* v_cache, int64_t kv_seq_stride,
+                          int64_t kv_head_stride, const int32_t* sel, const int32_t* sel_count,
+                          int32_t budget, void* out, float* lse, const double* inv_freq,
+                          float softmax_scale, const int32_t* block_table, int64_t table_stride,
+                          int32_t page_tokens, void* stream) {
   if (n_q < 0 || n_seq < 0 || max_q_len < 0) return QSA_ERR_INVALID_ARG;
   qsa::RopeFreq fr;
   if (!qsa_host::make_rope_freq(inv_freq, fr) || !qsa_host::softmax_scale_ok(softmax_scale))
@@ -536,8 +573,38 @@ int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_le
   hipLaunchKernelGGL(qsa::attend_kernel<true>, dim3(n_q * 2), dim3(256), 0, (hipStream_t)stream,
                      (const uint16_t*)q, cu_q, seq_len, n_seq, n_q, (const uint16_t*)k_cache,
                      (const uint16_t*)v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
-                     budget, 1, 0, (uint16_t*)out, lse, (float*)nullptr, fr, softmax_scale, pg);
+                     budget, 1, 0, (uint16_t*)out, lse, (float*)nullptr, fr, softmax_scale, pg,
+                     aligned);
   return qsa_host::launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_len, int32_t n_seq,
+                       int32_t n_q, int32_t max_q_len, const void* k_cache, const void* v_cache,
+                       int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
+                       const int32_t* sel_count, int32_t budget, void* out, float* lse,
+                       const double* inv_freq, float softmax_scale, const int32_t* block_table,
+                       int64_t table_stride, int32_t page_tokens, void* stream) {
+  return attend_prefill_launch(0, q, cu_q, seq_len, n_seq, n_q, max_q_len, k_cache, v_cache,
+                               kv_seq_stride, kv_head_stride, sel, sel_count, budget, out, lse,
+                               inv_freq, softmax_scale, block_table, table_stride, page_tokens,
+                               stream);
+}
+
+int qsa_attend_prefill_aligned(const void* q, const int32_t* cu_q, const int32_t* seq_len,
+                               int32_t n_seq, int32_t n_q, int32_t max_q_len, const void* k_cache,
+                               const void* v_cache, int64_t kv_seq_stride, int64_t kv_head_stride,
+                               const int32_t* sel, const int32_t* sel_count, int32_t budget,
+                               void* out, float* lse, const double* inv_freq, float softmax_scale,
+                               const int32_t* block_table, int64_t table_stride,
+                               int32_t page_tokens, void* stream) {
+  return attend_prefill_launch(1, q, cu_q, seq_len, n_seq, n_q, max_q_len, k_cache, v_cache,
+                               kv_seq_stride, kv_head_stride, sel, sel_count, budget, out, lse,
+                               inv_freq, softmax_scale, block_table, table_stride, page_tokens,
+                               stream);
 }
 
 size_t qsa_attend_decode_multi_workspace(int32_t n_q) {

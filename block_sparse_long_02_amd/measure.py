@@ -54,7 +54,9 @@ COPY_BYTES = 1 << 30
 # decode step of 131,073 tokens completes no new block).  The transformed
 # pooling runs twice (prefix, then the step's new blocks).  The prefill
 # kernels run twice, in the plain step (dispatch 0) and in the step with the
-# indexer transforms (dispatch 1), which selects other blocks.
+# indexer transforms (dispatch 1), which selects other blocks; the prefill
+# attention three times: the plain step's (time-aligned), the ordered
+# attention on the same selection, the transformed step's (time-aligned).
 KERNELS = {
     "pool_block_keys_prefill_1m": ("pool_block_keys_kernel", "qsa_pool.hip", 1),
     "score_sample_prefill_1m": ("score_gemm_kernel<2, 4, true, false>", "qsa_index.hip", 0),
@@ -62,7 +64,8 @@ KERNELS = {
     "score_filter_prefill_1m": ("score_gemm_kernel<2, 8, false, false>", "qsa_index.hip", 0),
     "final_select_prefill_1m": ("final_select_kernel", "qsa_index.hip", 0),
     "attend_prefill_1m": ("attend_kernel<true>", "qsa_attend.hip", 0),
-    "attend_prefill_1m_transformed": ("attend_kernel<true>", "qsa_attend.hip", 1),
+    "attend_prefill_1m_ordered": ("attend_kernel<true>", "qsa_attend.hip", 1),
+    "attend_prefill_1m_transformed": ("attend_kernel<true>", "qsa_attend.hip", 2),
     "score_dense_decode_128k": ("score_dense_kernel<false>", "qsa_index.hip", None),
     "select_dense_decode_128k": ("select_dense_kernel", "qsa_index.hip", None),
     "key_transform_prefill_1m": ("pool_block_keys_normed_kernel", "qsa_index_transform.hip", 1),
@@ -78,8 +81,9 @@ def src_hash(name: str) -> str:
 
 
 def probe():
-    """The program the counter runs profile: copy, one prefill step (plain, then
-    with the indexer transforms), one decode step."""
+    """The program the counter runs profile: copy, one prefill step (plain, with
+    the time-aligned attention), the ordered attention on the same selection,
+    one prefill step with the indexer transforms, one decode step."""
     import torch
     from . import workloads as W
     from .runner import QSARunner
@@ -92,14 +96,18 @@ def probe():
     print("MARK copy done", flush=True)
 
     b = W.chunked_prefill_1m(device="cuda")
-    r = QSARunner(b)
+    r = QSARunner(b, time_aligned=True)
     torch.cuda.synchronize()
     print("MARK prefill step", flush=True)
     r.step()
     torch.cuda.synchronize()
+    print("MARK ordered attention", flush=True)
+    r.time_aligned = False
+    r.attend()
+    torch.cuda.synchronize()
     del r
     torch.cuda.empty_cache()
-    r = QSARunner(b, transforms=True)
+    r = QSARunner(b, transforms=True, time_aligned=True)
     torch.cuda.synchronize()
     print("MARK prefill step with indexer transforms", flush=True)
     r.step()

@@ -525,6 +525,48 @@ def test_end_to_end_prefill_8k_sampled():
     print("prefill 8k:", kinds, f"worst rel-L2 {worst:.2e}")
 
 
+def _within_one_bf16_ulp(a, b, label):
+    # the same sums in another float32 order: an output may cross one bf16
+    # rounding boundary (one ulp of the larger magnitude), plus float32
+    # rounding where the sum cancels to near zero
+    x, y = a.float(), b.float()
+    bound = torch.maximum(x.abs(), y.abs()) * 2.0 ** -7 + 1e-5
+    excess = ((x - y).abs() - bound).max().item()
+    assert excess <= 0, (label, (x - y).abs().max().item())
+
+
+def test_time_aligned_prefill_attention():
+    # qsa_attend_prefill_aligned attends every row over the same blocks as
+    # qsa_attend_prefill, each row starting its walk where a shared clock
+    # points: the float32 sums run in another order, so every output is within
+    # one bf16 ulp of the ordered kernel's and lse within float32 rounding, and
+    # the oracle checks the rows.  Tiny rows (fewer tiles than waves, partial
+    # tails), the dense 2,048-token case, 8K, and 8K over pages in random order.
+    cases = [("tiny", W.tiny_prefill(T=512), None, list(range(0, 512, 7))),
+             ("dense 2048", W.prefill_8k(T=2048), None, [0, 1, 5, 63, 1000, 2047]),
+             ("8k", W.prefill_8k(T=8192), None, [0, 2047, 2048, 4000, 8191]),
+             ("8k paged", W.prefill_8k(T=8192), 256, [1, 3000, 8190])]
+    for name, b, paged, rows in cases:
+        print(f"time-aligned prefill: {name}", flush=True)
+        bc = b.to("cuda")
+        r = QSARunner(bc, paged=paged, page_seed=5) if paged else QSARunner(bc)
+        r.step()
+        _sync()
+        ref_out, ref_lse = r.out.clone(), r.lse.clone()
+        r.time_aligned = True
+        for _ in range(2):   # two launches, started at other clock readings
+            r.out.zero_()
+            r.lse.zero_()
+            r.attend()
+            _sync()
+            _within_one_bf16_ulp(ref_out, r.out, name)
+            assert (ref_lse - r.lse).abs().max().item() <= 1e-4, name
+        kinds, worst = _check_rows(r, OracleView(b), rows)
+        print(f"  {kinds}, worst rel-L2 {worst:.2e}", flush=True)
+        del r
+        torch.cuda.empty_cache()
+
+
 def test_end_to_end_decode_reduced():
     b = W.decode_128k(n_seq=6, ctx=32768)
     kinds, worst = _end_to_end(b, range(6))
@@ -736,6 +778,16 @@ def test_full_size_chunked_prefill_1m_sampled_rows():
     assert torch.equal(seq[0], r.sel) and torch.equal(seq[1], r.sel_count)
     assert torch.equal(seq[2].view(torch.int16), r.out.view(torch.int16))
     assert torch.equal(seq[3].view(torch.int32), r.lse.view(torch.int32))
+    # and with the time-aligned attention: the same blocks per row, float32
+    # sums in another order
+    r.time_aligned = True
+    r.attend()
+    _sync()
+    _within_one_bf16_ulp(seq[2], r.out, "1M time-aligned")
+    assert (seq[3] - r.lse).abs().max().item() <= 1e-4
+    kinds, worst = _check_rows(r, OracleView(b), rows[:6])
+    print("1M prefill, time-aligned attention:", kinds, f"worst rel-L2 {worst:.2e}", flush=True)
+    r.time_aligned = False
     del seq
     del r
     torch.cuda.empty_cache()

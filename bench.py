@@ -3,11 +3,7 @@
 Headline (`value`): chunked prefill at 1M context -- a 32,768-token query
 chunk on a 1,015,808-token cached prefix (batch 1, budget 512 blocks + tail):
 query tokens per second for one step = pool the chunk's new blocks, select
-blocks for every query, sparse attention, call after call.  The attention is
-qsa_attend_prefill_aligned: each row walks its selected blocks from where a
-shared clock points, so the rows in flight share blocks in L2; the same
-attention as qsa_attend_prefill, whose float32 sums run in a fixed order
-(`ordered`: the same step with it, bit-reproducible).  `pipelined`
+blocks for every query, sparse attention, call after call.  `pipelined`
 times the same step with the chunk's rows in 4 pieces, each piece's
 attention overlapping the next piece's selection (two streams, same calls and
 results).  Alongside it (`decode`): a decode
@@ -150,32 +146,21 @@ def time_steps(r, args):
     return start.elapsed_time(stop), stage, per_step
 
 
-def time_prefill(args, transforms=False, batch=None, yarn=False, paged=None, pipelined=True,
-                 time_aligned=True, ordered_too=False):
+def time_prefill(args, transforms=False, batch=None, yarn=False, paged=None, pipelined=True):
     """The chunked-prefill step (or the prefill of `batch`); transforms=True
     runs it with the pages' indexer transforms (normalised, rotated block keys
     and queries), yarn=True with the YaRN-extended rotations and softmax
-    scale; pipelined=False skips the overlapped-pieces timing.
-    time_aligned=True attends with qsa_attend_prefill_aligned (the same
-    attention, float32 sums in a timing-dependent order); ordered_too=True
-    also times the step with qsa_attend_prefill (bit-reproducible)."""
+    scale; pipelined=False skips the overlapped-pieces timing."""
     import torch
     from block_sparse_long_02_amd import workloads as W
     from block_sparse_long_02_amd.runner import QSARunner
 
     t0 = time.time()
     b = W.chunked_prefill_1m(device="cuda") if batch is None else batch
-    r = QSARunner(b, transforms=transforms, yarn=yarn, paged=paged, time_aligned=time_aligned)
+    r = QSARunner(b, transforms=transforms, yarn=yarn, paged=paged)
     torch.cuda.synchronize()
     log(f"prefill workload ready in {time.time() - t0:.1f}s")
     total_ms, stage, per_step = time_steps(r, args)
-    ordered = None
-    if ordered_too and time_aligned:
-        r.time_aligned = False
-        o_total, o_stage, o_steps = time_steps(r, args)
-        r.time_aligned = True
-        ordered = dict(ms_per_step=o_total / args.steps, step_ms_median=o_steps[len(o_steps) // 2],
-                       step_ms_min=o_steps[0], stages_ms=o_stage)
     # For comparison: the chunk's rows in PIPE_PARTS pieces, each piece's
     # attention (memory-bound) on a second stream while the next piece is
     # selected (MFMA-bound).  Same calls, same results.  Its gain depends on
@@ -215,7 +200,7 @@ def time_prefill(args, transforms=False, batch=None, yarn=False, paged=None, pip
         sum_set=sum_s, sum_candidates=sum_nc,
         attend=dict(bytes=attend_bytes, gbs=attend_gbs, flops=attend_flops),
         index=dict(flops=index_flops, tflops=index_flops / (stage["select"] * 1e-3) / 1e12),
-        ordered=ordered, runner=r, batch=b)
+        runner=r, batch=b)
     return res
 
 
@@ -442,7 +427,7 @@ def attend_roofline(pre, attend_file):
     mem["binds"] = ("the memory side: the kernel waits on its gathers (zero-reuse "
                     f"{pre['attend']['gbs'] / 1e3:.1f} TB/s; the counted beyond-L2 bytes include "
                     "Infinity Cache hits, so they can exceed the HBM read rate)")
-    return {"kernel": "attend_kernel<true> (sparse prefill attention)", "bound": "mfma",
+    return {"kernel": "attend_rows_kernel (sparse prefill attention)", "bound": "mfma",
             "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
             "frac": round(tflops / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic,
             "algorithmic_flop_per_launch": pre["attend"]["flops"],
@@ -505,27 +490,15 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic"}
     if args.only in (None, "prefill"):
-        pre = time_prefill(args, ordered_too=True)
+        pre = time_prefill(args)
         log(f"prefill: {pre['ms_per_step']:.3f} ms/step, stages {pre['stages_ms']}; "
-            f"{PIPE_PARTS} overlapped pieces {pre['pipelined']['ms_per_step']:.3f} ms/step; "
-            f"ordered attention {pre['ordered']['ms_per_step']:.3f} ms/step")
+            f"{PIPE_PARTS} overlapped pieces {pre['pipelined']['ms_per_step']:.3f} ms/step")
         attend_file = os.path.join(ROOT, "block_sparse_long_02_amd", "csrc", "qsa_attend.hip")
         out.update(value=round(pre["value"], 1), unit="tokens/s",
                    ms_per_step=round(pre["ms_per_step"], 4),
                    step_ms_median=round(pre["step_ms_median"], 4),
                    step_ms_min=round(pre["step_ms_min"], 4))
         out["pipelined"] = {k: round(v, 4) for k, v in pre["pipelined"].items()}
-        o = pre["ordered"]
-        out["attention_order"] = (
-            "time-aligned (qsa_attend_prefill_aligned): each row walks its selected blocks from "
-            "where a shared clock points, so the rows in flight share blocks in L2; the same "
-            "attention, with float32 sums in a timing-dependent order. `ordered` is the same step "
-            "with qsa_attend_prefill (bit-reproducible).")
-        out["ordered"] = {"ms_per_step": round(o["ms_per_step"], 4),
-                          "value": round(pre["n_q"] / (o["ms_per_step"] * 1e-3), 1),
-                          "step_ms_median": round(o["step_ms_median"], 4),
-                          "step_ms_min": round(o["step_ms_min"], 4),
-                          "stages_ms": {k: round(v, 4) for k, v in o["stages_ms"].items()}}
         out["config"] = {
             "workload": "chunked prefill: 32768-token chunk on a 1015808-token cached prefix "
                         "(1048576 total), batch 1, budget 512 blocks + tail",

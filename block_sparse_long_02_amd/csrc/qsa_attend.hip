@@ -7,16 +7,20 @@
 // their 4 tokens plus the unfinished tail {4 n_c, ..., i}; 24 query heads share
 // 2 KV heads (head h reads KV head h/12); width 256, rotary on dims 0..63.
 //
-// Design (gfx950): one wave streams tiles of 8 micro-blocks (32 tokens)
-// straight from HBM into registers -- no LDS staging, since a micro-block of
-// one KV head is a single 2 KB run in both caches.  Per tile it computes
-// S^T = K Q^T with bf16 MFMA 16x16x32 (tokens as rows, the 12 heads of the
-// KV group padded to 16 as columns).  The MFMA output gives each lane the 4
-// tokens of one micro-block for one head, which is exactly the k-slice the
-// P V product needs from P, so P never leaves registers; the V cache is laid
-// out [block][dim][4 tokens] so the matching V operand is one 8-byte run per
-// (block, dim).  Online softmax in float32 (base-2 exponent), output
-// accumulators in float32.
+// Design (gfx950): a wave walks a row's selected micro-blocks in tiles of 8
+// (32 tokens); a micro-block of one KV head is a single 2 KB run in both
+// caches.  Per tile it computes S^T = K Q^T with bf16 MFMA 16x16x32 (tokens
+// as rows, the 12 heads of the KV group padded to 16 as columns).  The MFMA
+// output gives each lane the 4 tokens of one micro-block for one head, which
+// is exactly the k-slice the P V product needs from P, so P never leaves
+// registers; the V cache is laid out [block][dim][4 tokens] so the matching V
+// operand is one 8-byte run per (block, dim).  Online softmax in float32
+// (base-2 exponent), output accumulators in float32.
+//   prefill (attend_rows_kernel): one wave per query row and KV head, 4 rows
+//     per workgroup; the next tile's keys come through the LDS DMA, the next
+//     tile's values into registers, while the current tile computes.
+//   decode (attend_split_kernel + combine_kernel): a row's tiles are split
+//     over several workgroups that write (m, l, O) partials, merged after.
 #include <math.h>
 
 #include <mutex>
@@ -53,110 +57,396 @@ __device__ __forceinline__ float bf16_elem(const u32x4& v, int e) {
 constexpr int kWaitVmem16 = 0x4F70;   // vector memory loads in flight <= 16
 constexpr int kWaitVmem0 = 0x0F70;    // no vector memory load in flight
 constexpr int kWaitLds0 = 0xC07F;     // no LDS access in flight
-// Time-aligned prefill: expected sweep time per tile of a wave's share, in
-// ticks of the 100 MHz constant clock (1M chunk: 16 tiles per wave, 10.8 ms
-// at 6,000 ticks per sweep against 12.0 ms with the ordered sweep)
-constexpr int kSweepTicksPerTile = 400;
 
-struct AttnShared {
+// split decode: one row's list and rotary angles, and the 4 waves' partial
+// results merged at the end
+struct SplitShared {
   int list[kMaxList + 8];            // micro-block ids, tail block last
   float cs[kRopeDim / 2][2];         // cos, sin of the query position
   float m[kWaves][16];
   float l[kWaves][16];
-  int sweep_at;                      // time-aligned prefill: the block id to start at
-  int k0;                            // ... and the list index of the first id at or past it
-  union {
-    float o[kWaves][kGroup][kHeadDim];   // the waves' outputs, merged at the end
-    u32x4 kst[kWaves][kHalves][8][64];   // prefill: a tile's keys, per wave and lane
-  };
+  float o[kWaves][kGroup][kHeadDim];
 };
 
-// mode kFinal: one workgroup per (row, KV head) writes out / lse.
-// otherwise: n_splits workgroups per (row, KV head) write partials.
-template <bool kFinal>
-__global__ void __launch_bounds__(256, kFinal ? 2 : 1)
-attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
-              const int32_t* __restrict__ seq_len, int n_seq, int n_rows,
-              const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-              int64_t seq_stride, int64_t head_stride,
-              const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int budget,
-              int n_splits, int one_per_seq, uint16_t* __restrict__ out,
-              float* __restrict__ lse, float* __restrict__ part, RopeFreq fr, float sm_scale,
-              Pages pg, int aligned) {
-  __shared__ AttnShared sh;
+// prefill: one wave's row (its list, rotary angles and next-tile key slots)
+struct RowShared {
+  int list[kMaxList + 8];
+  float cs[kRopeDim / 2][2];
+  u32x4 kst[kHalves][8][64];
+};
+
+// ---- the per-tile arithmetic shared by the prefill and the split decode
+// kernels.  A tile is 8 micro-blocks (32 tokens) in two halves; in half hv,
+// lane (col, grp) holds K rows of token `col` (micro-block 4 hv + col / 4)
+// and the V / P k-slice of micro-block 4 hv + grp.
+
+// Query fragment: the B operand of S^T = K Q^T.  The lane holds head `col`
+// of this KV group (heads 12..15 are zero padding), dims 32 ks + 8 grp ..
+// +7.  Rotate-half RoPE on dims 0..63 (pair j = 8 grp + e sits in qf[0] (x1)
+// and qf[1] (x2)); the rotated dims are carried as two bf16 terms (value in
+// qf, residual in ql), so the rotation adds no bf16 rounding to the logits;
+// dims 64..255 are the bf16 inputs themselves.
+__device__ __forceinline__ void rotate_query(u32x4 (&qf)[8], u32x4 (&ql)[2],
+                                             const float (*cs)[2], int col, int grp) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    if (col >= kGroup) qf[ks] = u32x4{0, 0, 0, 0};
+  ql[0] = u32x4{0u, 0u, 0u, 0u};
+  ql[1] = u32x4{0u, 0u, 0u, 0u};
+  u32x4 r0, r1, l0, l1;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float y1[2], y2[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int e = 2 * w + h2, j = 8 * grp + e;
+      const float c = cs[j][0], sn = cs[j][1];
+      const float x1 = bf16_elem(qf[0], e), x2 = bf16_elem(qf[1], e);
+      y1[h2] = x1 * c - x2 * sn;
+      y2[h2] = x2 * c + x1 * sn;
+    }
+    r0[w] = pack_bf16x2(y1[0], y1[1]);
+    r1[w] = pack_bf16x2(y2[0], y2[1]);
+    l0[w] = pack_bf16x2(y1[0] - bf16_lo(r0[w]), y1[1] - bf16_hi(r0[w]));
+    l1[w] = pack_bf16x2(y2[0] - bf16_lo(r1[w]), y2[1] - bf16_hi(r1[w]));
+  }
+  if (col < kGroup) { qf[0] = r0; qf[1] = r1; ql[0] = l0; ql[1] = l1; }
+}
+
+// S^T = K Q^T on MFMA 16x16x32: sc[hv][i] is token 4 grp + i of half hv for
+// head col (the rotated dims twice: value and residual of the query).
+__device__ __forceinline__ void tile_logits(const u32x4 (&kh)[kHalves][8], const u32x4 (&qf)[8],
+                                            const u32x4 (&ql)[2], f32x4 (&sc)[kHalves]) {
+#pragma unroll
+  for (int hv = 0; hv < kHalves; ++hv) {
+    sc[hv] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) sc[hv] = mfma_16x16x32(kh[hv][ks], qf[ks], sc[hv]);
+    sc[hv] = mfma_16x16x32(kh[hv][0], ql[0], sc[hv]);
+    sc[hv] = mfma_16x16x32(kh[hv][1], ql[1], sc[hv]);
+  }
+}
+
+// Online softmax of one tile and O += P V.  Logits in log2 units (scale);
+// slots past the list (padding) and the tail block's tokens past the query
+// are masked.  Lazy rescale: the reference max m_run only moves when a
+// head's tile max exceeds it by more than 2^8, so p <= 256 and the float32
+// sums stay exact-enough; the 64 output rescales run only on those tiles.
+// P goes into the P V product as two bf16 terms (value and residual), so the
+// product carries no bf16 rounding of the weights.
+__device__ __forceinline__ void tile_softmax_pv(const f32x4 (&sc)[kHalves], u32x4 (&vh)[kHalves][8],
+                                                f32x4 (&o)[16], float& m_run, float& l_run,
+                                                int base, int cnt, int n_mb, int tail_slot,
+                                                int tail_len, float scale, int grp) {
+  float x[4 * kHalves];
+#pragma unroll
+  for (int hv = 0; hv < kHalves; ++hv)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[4 * hv + i] = sc[hv][i] * scale;
+  if (base + kTileMB > cnt) {
+    // the tile holds the tail block and/or padding slots (uniform branch)
+#pragma unroll
+    for (int hv = 0; hv < kHalves; ++hv) {
+      const int sv = base + 4 * hv + grp;
+      const int nv = sv >= n_mb ? 0 : (sv == tail_slot ? tail_len : 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * hv + i] = i < nv ? x[4 * hv + i] : -INFINITY;
+      // cache rows past the query inside the tail block (and padding slots)
+      // may hold anything: zero their V so that p = 0 cannot meet a NaN
+      const uint32_t m01 = (nv > 0 ? 0xFFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
+      const uint32_t m23 = (nv > 2 ? 0xFFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        vh[hv][c][0] &= m01; vh[hv][c][1] &= m23; vh[hv][c][2] &= m01; vh[hv][c][3] &= m23;
+      }
+    }
+  }
+  float mt = x[0];
+#pragma unroll
+  for (int i = 1; i < 4 * kHalves; ++i) mt = fmaxf(mt, x[i]);
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  if (__ballot(mt > m_run + 8.f)) {
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
+    l_run *= alpha;
+    m_run = m_new;
+    float a_row[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a_row[i] = __shfl(alpha, 4 * grp + i, 64);
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[n][i] *= a_row[i];
+    }
+  }
+  float p[4 * kHalves], ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4 * kHalves; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - m_run); ps += p[i]; }
+  ps += __shfl_xor(ps, 16, 64);
+  ps += __shfl_xor(ps, 32, 64);
+  l_run += ps;
+  // P k-slice of 8 tokens (2 micro-blocks) per lane: MFMA 16x16x32
+  u32x4 pa, pl;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pa[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+    pl[e] = pack_bf16x2(p[2 * e] - bf16_lo(pa[e]), p[2 * e + 1] - bf16_hi(pa[e]));
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    // dims 32c + 2*col (even tile) and 32c + 2*col + 1 (odd tile)
+    u32x4 be = {vh[0][c][0], vh[0][c][1], vh[1][c][0], vh[1][c][1]};
+    u32x4 bo = {vh[0][c][2], vh[0][c][3], vh[1][c][2], vh[1][c][3]};
+    o[2 * c] = mfma_16x16x32(pa, be, o[2 * c]);
+    o[2 * c + 1] = mfma_16x16x32(pa, bo, o[2 * c + 1]);
+    o[2 * c] = mfma_16x16x32(pl, be, o[2 * c]);
+    o[2 * c + 1] = mfma_16x16x32(pl, bo, o[2 * c + 1]);
+  }
+}
+
+// The row's geometry: its sequence, position, candidate count and tail, and
+// whether its selection is usable (a row with a bad selection gets NaN).
+struct RowGeo {
+  int s, pos, n_c, tail_len, cnt, n_mb, n_tiles;
+  bool bad;
+};
+__device__ __forceinline__ RowGeo row_geo(const int32_t* __restrict__ cu_q,
+                                          const int32_t* __restrict__ seq_len, int n_seq,
+                                          const int32_t* __restrict__ sel_count, int budget,
+                                          int row, bool one_per_seq) {
+  RowGeo r;
+  // one_per_seq: row s is the single query of sequence s (decode)
+  r.s = one_per_seq ? row : find_seq(cu_q, n_seq, row);
+  const int q_begin = one_per_seq ? row : cu_q[r.s];
+  const int q_end = one_per_seq ? row + 1 : cu_q[r.s + 1];
+  r.pos = seq_len[r.s] - (q_end - q_begin) + (row - q_begin);
+  r.n_c = (r.pos + 1) >> 2;
+  r.tail_len = (r.pos + 1) & 3;
+  r.cnt = sel_count[row];
+  r.bad = row >= q_end || r.pos < 0 || r.cnt < 0 || r.cnt > budget || r.cnt > r.n_c ||
+          (r.cnt < min(budget, r.n_c));
+  r.n_mb = r.cnt + (r.tail_len > 0 ? 1 : 0);
+  r.n_tiles = (r.n_mb + kTileMB - 1) / kTileMB;
+  return r;
+}
+
+// ---- prefill: one row per wave ---------------------------------------------
+// Each wave attends one query row for one KV head on its own: its block list,
+// rotary angles and key slots live in its own LDS region, it walks all of the
+// row's tiles in order, and it normalises and writes the row's output itself
+// (no workgroup barrier, no merge between waves).  A workgroup of 4 waves
+// takes 4 consecutive rows of one KV head; the dispatcher deals workgroups to
+// the 8 XCDs in turn, so each XCD holds one KV head and 256 rows of it in
+// flight.  Rows of the same chunk select many of the same blocks, and the 4
+// rows of a workgroup walk their ascending lists side by side, so a shared
+// block is often still in L2 when the next row needs it.
+// The keys of the next tile go straight from global memory into the wave's
+// LDS slots (the LDS DMA puts lane i's 16 bytes in slot i) while the current
+// tile computes, without the registers a second kh would take; the values of
+// the next tile are loaded into registers once P V has consumed vh.
+__global__ void __launch_bounds__(256, 2)
+attend_rows_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
+                   const int32_t* __restrict__ seq_len, int n_seq, int n_rows,
+                   const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                   int64_t seq_stride, int64_t head_stride,
+                   const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count,
+                   int budget, uint16_t* __restrict__ out, float* __restrict__ lse, RopeFreq fr,
+                   float sm_scale, Pages pg) {
+  __shared__ RowShared shw[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
+  const int g = blockIdx.x & 1;
+  const int row = (int)(blockIdx.x >> 1) * kWaves + wave;
+  if (row >= n_rows) return;   // waves are independent: no workgroup barrier below
+  RowShared& sh = shw[wave];
 
-  // Split-K launches put each XCD on a contiguous range of (row, KV head,
-  // split) items: the dispatcher deals consecutive workgroup ids to the 8
-  // XCDs in turn, so without this the rows of one sequence (the query tokens
-  // of a multi-token decode) would each run on another XCD and could not
-  // share the blocks they have in common through one L2.
-  const int wg = (kFinal || (gridDim.x & 7)) ? (int)blockIdx.x
-                                             : (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3));
-  const int split = wg % n_splits;
-  const int g = (wg / n_splits) & 1;
-  const int row = wg / (2 * n_splits);
-  if (row >= n_rows) return;
-
-  // ---- which sequence / position, and is the selection usable?
-  // one_per_seq: row s is the single query of sequence s (decode)
-  const int s = one_per_seq ? row : find_seq(cu_q, n_seq, row);
-  const int q_begin = one_per_seq ? row : cu_q[s], q_end = one_per_seq ? row + 1 : cu_q[s + 1];
-  const int L = seq_len[s];
-  const int pos = L - (q_end - q_begin) + (row - q_begin);
-  const int n_c = (pos + 1) >> 2;
-  const int tail_len = (pos + 1) & 3;
-  const int cnt = sel_count[row];
-  const bool bad = row >= q_end || pos < 0 || cnt < 0 || cnt > budget || cnt > n_c ||
-                   (cnt < min(budget, n_c));
-  if (bad) {
-    if (kFinal) {
-      for (int i = threadIdx.x; i < kGroup * kHeadDim; i += 256)
-        out[((int64_t)row * kQHeads + g * kGroup) * kHeadDim + i] = 0x7FC0;  // NaN
-      if (lse && threadIdx.x < kGroup) lse[(int64_t)row * kQHeads + g * kGroup + threadIdx.x] = __int_as_float(0x7FC00000);
-    } else {
-      float* pp = part + ((int64_t)(row * 2 + g) * n_splits + split) * kPartFloats;
-      for (int i = threadIdx.x; i < kPartFloats; i += 256) pp[i] = __int_as_float(0x7FC00000);
-    }
+  const RowGeo r = row_geo(cu_q, seq_len, n_seq, sel_count, budget, row, false);
+  if (r.bad) {
+    for (int i = lane; i < kGroup * kHeadDim; i += 64)
+      out[((int64_t)row * kQHeads + g * kGroup) * kHeadDim + i] = 0x7FC0;  // NaN
+    if (lse && lane < kGroup)
+      lse[(int64_t)row * kQHeads + g * kGroup + lane] = __int_as_float(0x7FC00000);
     return;
   }
-  const int n_mb = cnt + (tail_len > 0 ? 1 : 0);
-
-  // ---- this wave's tiles
-  const int n_tiles = (n_mb + kTileMB - 1) / kTileMB;
-  const int parts = n_splits * kWaves;
-  const int my_part = split * kWaves + wave;
-  // split decode: part p takes tiles [p*n/parts, (p+1)*n/parts) (prefill
-  // interleaves its waves' tiles instead, below)
-  const int t_begin = (int)((int64_t)my_part * n_tiles / parts);
-  const int t_end = (int)((int64_t)(my_part + 1) * n_tiles / parts);
-  const int tail_slot = tail_len > 0 ? cnt : -1;
-
+  const int cnt = r.cnt, n_mb = r.n_mb, n_tiles = r.n_tiles;
+  const int tail_slot = r.tail_len > 0 ? cnt : -1;
   // paged caches: one pool per KV head, the list below holds physical blocks
-  const int64_t seq_off = pg.table ? 0 : (int64_t)s * seq_stride;
+  const int64_t seq_off = pg.table ? 0 : (int64_t)r.s * seq_stride;
   const uint16_t* kbase = kc + seq_off + (int64_t)g * head_stride;
   const uint16_t* vbase = vc + seq_off + (int64_t)g * head_stride;
   const float scale = kLog2e * sm_scale;   // logits in log2 units
+
+  // query fragment first, so that its latency overlaps the list load
+  u32x4 qf[8], ql[2];
+  const int head = g * kGroup + min(col, kGroup - 1);
+  const uint16_t* qrow = q + ((int64_t)row * kQHeads + head) * kHeadDim + 8 * grp;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = ldg16(qrow + 32 * ks);
+
+  // block list (ascending ids from the selection, the tail block last) and
+  // the query's rotary angles into this wave's LDS
+  for (int i = lane; i < cnt; i += 64) {
+    int id = sel[(int64_t)row * budget + i];
+    id = min(max(id, 0), r.n_c - 1);
+    sh.list[i] = pg.table ? (int)phys_block(pg, r.s, id) : id;
+  }
+  if (lane == 0 && r.tail_len > 0)
+    sh.list[cnt] = pg.table ? (int)phys_block(pg, r.s, r.n_c) : r.n_c;
+  if (lane < kRopeDim / 2) {
+    double sd, cd;
+    sincos((double)r.pos * freq_at(fr, lane), &sd, &cd);
+    sh.cs[lane][0] = (float)cd;
+    sh.cs[lane][1] = (float)sd;
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLds0);   // the wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  rotate_query(qf, ql, sh.cs, col, grp);
+
+  u32x4 kh[kHalves][8], vh[kHalves][8];
+  auto load_v = [&](int t) {
+#pragma unroll
+    for (int hv = 0; hv < kHalves; ++hv) {
+      const int idv = sh.list[min(t * kTileMB + 4 * hv + grp, n_mb - 1)];
+      const uint16_t* vp = vbase + (int64_t)idv * (kBlock * kHeadDim) + 8 * col;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) vh[hv][c] = ldg16(vp + 128 * c);
+    }
+  };
+  auto dma_k = [&](int t) {
+#pragma unroll
+    for (int hv = 0; hv < kHalves; ++hv) {
+      const int idk = sh.list[min(t * kTileMB + 4 * hv + (col >> 2), n_mb - 1)];
+      const uint16_t* kp = kbase + ((int64_t)idk * kBlock + (col & 3)) * kHeadDim + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(kp + 32 * ks),
+            (__attribute__((address_space(3))) void*)&sh.kst[hv][ks][0], 16, 0, 0);
+    }
+  };
 
   f32x4 o[16];
 #pragma unroll
   for (int n = 0; n < 16; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Half hv of tile t covers micro-blocks t*kTileMB + 4hv .. +3.  K rows:
-  // lane is token row `col` of the half; V / P k-slices: micro-block
-  // t*kTileMB + 4hv + grp.
+  if (n_tiles > 0) {
+    dma_k(0);
+    asm volatile("" ::: "memory");   // keep the DMA ahead of the value loads
+    load_v(0);
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    // outstanding here: this tile's key DMA, then its 16 value loads
+    __builtin_amdgcn_s_waitcnt(kWaitVmem16);   // the keys have landed
+#pragma unroll
+    for (int hv = 0; hv < kHalves; ++hv)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kh[hv][ks] = sh.kst[hv][ks][lane];
+    f32x4 sc[kHalves];
+    tile_logits(kh, qf, ql, sc);
+    // kh is consumed, so the slots can take the next tile's keys.  This
+    // tile's values are waited for first, on every path: the compiler counts
+    // an LDS DMA conservatively, and a wait for an older load behind it would
+    // become a wait for the DMA too.
+    __builtin_amdgcn_s_waitcnt(kWaitLds0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    if (t + 1 < n_tiles) dma_k(t + 1);
+    asm volatile("" ::: "memory");
+    tile_softmax_pv(sc, vh, o, m_run, l_run, t * kTileMB, cnt, n_mb, tail_slot, r.tail_len,
+                    scale, grp);
+    if (t + 1 < n_tiles) load_v(t + 1);
+  }
+
+  // output: the lane holds heads 4 grp + i, dims 32c + 2col and + 1; the
+  // softmax denominator and max of head h sit in lane h
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hr = 4 * grp + i;
+    const float inv = 1.f / __shfl(l_run, hr, 64);
+    if (hr < kGroup) {
+      uint16_t* op = out + ((int64_t)row * kQHeads + g * kGroup + hr) * kHeadDim + 2 * col;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        *(uint32_t*)(op + 32 * c) = (uint32_t)f32_to_bf16_bits(o[2 * c][i] * inv) |
+                                    ((uint32_t)f32_to_bf16_bits(o[2 * c + 1][i] * inv) << 16);
+    }
+  }
+  if (lse && grp == 0 && col < kGroup)
+    lse[(int64_t)row * kQHeads + g * kGroup + col] = (m_run + log2f(l_run)) * kLn2;
+}
+
+// ---- split decode -----------------------------------------------------------
+// n_splits workgroups per (row, KV head) write (m, l, O) partials; 4 waves
+// split each workgroup's contiguous range of tiles and merge in LDS.  The K
+// and V loads are staggered by half a tile: the keys of tile t + 1 are
+// requested as soon as the logits of tile t are formed, the values of tile
+// t + 1 once P V of tile t has consumed vh, so each wave always has one of the
+// two operands in flight while it computes (256 VGPRs: one wave per SIMD).
+__global__ void __launch_bounds__(256, 1)
+attend_split_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
+                    const int32_t* __restrict__ seq_len, int n_seq, int n_rows,
+                    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                    int64_t seq_stride, int64_t head_stride,
+                    const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count,
+                    int budget, int n_splits, int one_per_seq, float* __restrict__ part,
+                    RopeFreq fr, float sm_scale, Pages pg) {
+  __shared__ SplitShared sh;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+
+  // Each XCD takes a contiguous range of (row, KV head, split) items: the
+  // dispatcher deals consecutive workgroup ids to the 8 XCDs in turn, so
+  // without this the rows of one sequence (the query tokens of a multi-token
+  // decode) would each run on another XCD and could not share the blocks
+  // they have in common through one L2.
+  const int wg = (gridDim.x & 7) ? (int)blockIdx.x
+                                 : (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3));
+  const int split = wg % n_splits;
+  const int g = (wg / n_splits) & 1;
+  const int row = wg / (2 * n_splits);
+  if (row >= n_rows) return;
+
+  const RowGeo r = row_geo(cu_q, seq_len, n_seq, sel_count, budget, row, one_per_seq != 0);
+  float* pp = part + ((int64_t)(row * 2 + g) * n_splits + split) * kPartFloats;
+  if (r.bad) {
+    for (int i = threadIdx.x; i < kPartFloats; i += 256) pp[i] = __int_as_float(0x7FC00000);
+    return;
+  }
+  const int cnt = r.cnt, n_mb = r.n_mb;
+  const int tail_slot = r.tail_len > 0 ? cnt : -1;
+  // part p of this (row, KV head) takes tiles [p*n/parts, (p+1)*n/parts)
+  const int parts = n_splits * kWaves;
+  const int my_part = split * kWaves + wave;
+  const int t_begin = (int)((int64_t)my_part * r.n_tiles / parts);
+  const int t_end = (int)((int64_t)(my_part + 1) * r.n_tiles / parts);
+  const int64_t seq_off = pg.table ? 0 : (int64_t)r.s * seq_stride;
+  const uint16_t* kbase = kc + seq_off + (int64_t)g * head_stride;
+  const uint16_t* vbase = vc + seq_off + (int64_t)g * head_stride;
+  const float scale = kLog2e * sm_scale;
+
+  u32x4 qf[8], ql[2];
+  const int head = g * kGroup + min(col, kGroup - 1);
+  const uint16_t* qrow = q + ((int64_t)row * kQHeads + head) * kHeadDim + 8 * grp;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = ldg16(qrow + 32 * ks);
+
+  for (int i = threadIdx.x; i < cnt; i += 256) {
+    int id = sel[(int64_t)row * budget + i];
+    id = min(max(id, 0), r.n_c - 1);   // ids come ascending from the selection
+    sh.list[i] = pg.table ? (int)phys_block(pg, r.s, id) : id;
+  }
+  if (threadIdx.x == 0 && r.tail_len > 0)
+    sh.list[cnt] = pg.table ? (int)phys_block(pg, r.s, r.n_c) : r.n_c;
+  if (threadIdx.x < kRopeDim / 2) {
+    double sd, cd;
+    sincos((double)r.pos * freq_at(fr, threadIdx.x), &sd, &cd);
+    sh.cs[threadIdx.x][0] = (float)cd;
+    sh.cs[threadIdx.x][1] = (float)sd;
+  }
+  __syncthreads();
+
   u32x4 kh[kHalves][8], vh[kHalves][8];
-  // split-K partials (decode) run one wave per SIMD, which leaves the
-  // registers for the staggered loads below
-  constexpr bool kStagger = !kFinal;
-  // list slot i of the sweep: selected blocks rotated by k0, the tail last
-  int k0 = 0;
-  auto lst = [&](int i) {
-    if (i < cnt) { i += k0; if (i >= cnt) i -= cnt; }
-    return sh.list[i];
-  };
   auto load_k = [&](int t) {
 #pragma unroll
     for (int hv = 0; hv < kHalves; ++hv) {
@@ -169,251 +459,32 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
   auto load_v = [&](int t) {
 #pragma unroll
     for (int hv = 0; hv < kHalves; ++hv) {
-      const int idv = lst(min(t * kTileMB + 4 * hv + grp, n_mb - 1));
+      const int idv = sh.list[min(t * kTileMB + 4 * hv + grp, n_mb - 1)];
       const uint16_t* vp = vbase + (int64_t)idv * (kBlock * kHeadDim) + 8 * col;
 #pragma unroll
       for (int c = 0; c < 8; ++c) vh[hv][c] = ldg16(vp + 128 * c);
     }
   };
-  // Prefill: tile t's keys go straight from global memory into this wave's
-  // LDS slots (the LDS DMA puts lane i's 16 bytes in slot i) and are read
-  // into kh when the tile starts.  They are requested a tile ahead, while
-  // the current tile computes, without the registers a second kh would take
-  // (1M chunk 12.34 -> 12.01 ms, bit-identical results).
-  auto dma_k = [&](int t) {
-#pragma unroll
-    for (int hv = 0; hv < kHalves; ++hv) {
-      const int idk = lst(min(t * kTileMB + 4 * hv + (col >> 2), n_mb - 1));
-      const uint16_t* kp = kbase + ((int64_t)idk * kBlock + (col & 3)) * kHeadDim + 8 * grp;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(kp + 32 * ks),
-            (__attribute__((address_space(3))) void*)&sh.kst[wave][hv][ks][0], 16, 0, 0);
-    }
-  };
-  // ---- query fragment: B operand of S^T = K Q^T.  Lane holds head `col` of
-  // this KV group, dims 32*ks + 8*grp .. +7.  Heads 12..15 are zero padding:
-  // their address is clamped to a real head and the value replaced by zero.
-  // Issued first, so that its latency overlaps the block-list load.
-  u32x4 qf[8];
-  const int head = g * kGroup + min(col, kGroup - 1);
-  const uint16_t* qrow = q + ((int64_t)row * kQHeads + head) * kHeadDim + 8 * grp;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qf[ks] = ldg16(qrow + 32 * ks);
-
-  // ---- time-aligned prefill: the rows in flight sweep the cache together.
-  // A row normally walks its ascending list from the start, so rows that
-  // start at different times are at different block ids at any moment and
-  // rarely meet on a shared block while it is still in L2.  Here a row starts
-  // at the block id a shared clock points to (the clock runs over the row's
-  // candidates once per expected sweep time) and wraps around: the rows in
-  // flight are then near the same block ids together.  The row's blocks are
-  // the same; only the order of its float32 sums changes with timing.
-  const bool timed = kFinal && aligned;
-  if (timed) {
-    if (threadIdx.x == 0) {
-      const int64_t period = (int64_t)max((n_tiles + kWaves - 1) / kWaves, 1) * kSweepTicksPerTile;
-      const uint64_t clk = __builtin_amdgcn_s_memrealtime();   // constant 100 MHz
-      sh.sweep_at = (int)(((int64_t)(clk % (uint64_t)period) * n_c) / period);
-      sh.k0 = 0;
-    }
-    __syncthreads();
-  }
-
-  // ---- block list and the query's rotary angles into LDS
-  for (int i = threadIdx.x; i < cnt; i += 256) {
-    int id = sel[(int64_t)row * budget + i];
-    id = min(max(id, 0), n_c - 1);   // ids come ascending from the selection
-    sh.list[i] = pg.table ? (int)phys_block(pg, s, id) : id;
-    if (timed) {
-      // list index of the first id at or past sweep_at = ids below it
-      const uint64_t below = __ballot(id < sh.sweep_at);
-      const uint64_t active = __ballot(1);
-      if (lane == __builtin_ctzll(active) && below) atomicAdd(&sh.k0, __popcll(below));
-    }
-  }
-  if (threadIdx.x == 0 && tail_len > 0) sh.list[cnt] = pg.table ? (int)phys_block(pg, s, n_c) : n_c;
-  if (threadIdx.x < kRopeDim / 2) {
-    double sd, cd;
-    sincos((double)pos * freq_at(fr, threadIdx.x), &sd, &cd);
-    sh.cs[threadIdx.x][0] = (float)cd;
-    sh.cs[threadIdx.x][1] = (float)sd;
-  }
-  __syncthreads();
-
-  k0 = timed ? sh.k0 % max(cnt, 1) : 0;
-
-  // The K and V loads are staggered by half a tile: the keys of tile t + 1
-  // are requested as soon as the logits of tile t are formed, the values of
-  // tile t + 1 once P V of tile t has consumed vh.  Each wave thus always has
-  // one of the two operands in flight while it computes.
-  if (kStagger && t_begin < t_end) {
+  if (t_begin < t_end) {
     load_k(t_begin);
     load_v(t_begin);
   }
+  rotate_query(qf, ql, sh.cs, col, grp);
 
+  f32x4 o[16];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-    if (col >= kGroup) qf[ks] = u32x4{0, 0, 0, 0};
-  // The rotated dims 0..63 are carried as two bf16 terms (value and
-  // residual), so the rotation adds no bf16 rounding to the logits; dims
-  // 64..255 are the bf16 inputs themselves.
-  u32x4 ql[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-  {
-    // rotate-half on dims 0..63: pair j = 8*grp + e sits in qf[0] (x1) and qf[1] (x2)
-    u32x4 r0, r1, l0, l1;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      float y1[2], y2[2];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int e = 2 * w + h2, j = 8 * grp + e;
-        const float c = sh.cs[j][0], sn = sh.cs[j][1];
-        const float x1 = bf16_elem(qf[0], e), x2 = bf16_elem(qf[1], e);
-        y1[h2] = x1 * c - x2 * sn;
-        y2[h2] = x2 * c + x1 * sn;
-      }
-      r0[w] = pack_bf16x2(y1[0], y1[1]);
-      r1[w] = pack_bf16x2(y2[0], y2[1]);
-      l0[w] = pack_bf16x2(y1[0] - bf16_lo(r0[w]), y1[1] - bf16_hi(r0[w]));
-      l1[w] = pack_bf16x2(y2[0] - bf16_lo(r1[w]), y2[1] - bf16_hi(r1[w]));
-    }
-    if (col < kGroup) { qf[0] = r0; qf[1] = r1; ql[0] = l0; ql[1] = l1; }
-  }
-
-  // Prefill: the waves take the row's tiles in turn (wave w: tiles w, w+4,
-  // ...), so the row sweeps its ascending list four tiles at a time.  Rows
-  // that run together share many blocks at nearby ranks of their lists; the
-  // faster sweep requests a shared block closer in time, while it is still
-  // in L2 (1M chunk: 12.53 -> 12.24 ms against contiguous quarters).  Split
-  // decode keeps contiguous ranges for its staggered loads.
-  const int t_first = kFinal ? wave : t_begin;
-  const int t_stop = kFinal ? n_tiles : t_end;
-  const int t_step = kFinal ? kWaves : 1;
-  if (kFinal && t_first < t_stop) {
-    dma_k(t_first);
-    asm volatile("" ::: "memory");   // keep the DMA ahead of the value loads
-    load_v(t_first);
-  }
-  for (int t = t_first; t < t_stop; t += t_step) {
-    const int base = t * kTileMB;
-    const bool more = t + t_step < t_stop;
-    if (kFinal) {
-      // Outstanding here: this tile's key DMA, then its 16 value loads.
-      __builtin_amdgcn_s_waitcnt(kWaitVmem16);   // the keys have landed
-#pragma unroll
-      for (int hv = 0; hv < kHalves; ++hv)
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) kh[hv][ks] = sh.kst[wave][hv][ks][lane];
-    }
-
-    // sc[hv][i]: token i of micro-block slot base + 4hv + grp, head col
+  for (int n = 0; n < 16; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int t = t_begin; t < t_end; ++t) {
     f32x4 sc[kHalves];
-#pragma unroll
-    for (int hv = 0; hv < kHalves; ++hv) {
-      sc[hv] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        sc[hv] = mfma_16x16x32(kh[hv][ks], qf[ks], sc[hv]);
-      sc[hv] = mfma_16x16x32(kh[hv][0], ql[0], sc[hv]);
-      sc[hv] = mfma_16x16x32(kh[hv][1], ql[1], sc[hv]);
-    }
-    if (kStagger && t + 1 < t_end) load_k(t + 1);
-    if (kFinal) {
-      // kh is consumed, so the slots can take the next tile's keys.  This
-      // tile's values are waited for first, on every path: the compiler
-      // counts an LDS DMA conservatively, and a wait for an older load
-      // behind it would become a wait for the DMA too.
-      __builtin_amdgcn_s_waitcnt(kWaitLds0);
-      __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-      if (more) dma_k(t + t_step);
-      asm volatile("" ::: "memory");
-    }
-    float x[4 * kHalves];
-#pragma unroll
-    for (int hv = 0; hv < kHalves; ++hv)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[4 * hv + i] = sc[hv][i] * scale;
-    if (base + kTileMB > cnt) {
-      // the tile holds the tail block and/or padding slots (uniform branch)
-#pragma unroll
-      for (int hv = 0; hv < kHalves; ++hv) {
-        const int sv = base + 4 * hv + grp;
-        const int nv = sv >= n_mb ? 0 : (sv == tail_slot ? tail_len : 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[4 * hv + i] = i < nv ? x[4 * hv + i] : -INFINITY;
-        // Cache rows past the query inside the tail block (and padding
-        // slots) may hold anything: zero their V so that p = 0 cannot meet a
-        // NaN.
-        const uint32_t m01 = (nv > 0 ? 0xFFFFu : 0u) | (nv > 1 ? 0xFFFF0000u : 0u);
-        const uint32_t m23 = (nv > 2 ? 0xFFFFu : 0u) | (nv > 3 ? 0xFFFF0000u : 0u);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          vh[hv][c][0] &= m01; vh[hv][c][1] &= m23; vh[hv][c][2] &= m01; vh[hv][c][3] &= m23;
-        }
-      }
-    }
-    float mt = x[0];
-#pragma unroll
-    for (int i = 1; i < 4 * kHalves; ++i) mt = fmaxf(mt, x[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    // Lazy rescale: the reference max m_run only moves when a head's tile max
-    // exceeds it by more than 2^8, so p <= 256 and the float32 sums stay
-    // exact-enough; the 64 output rescales run only on those tiles.
-    if (__ballot(mt > m_run + 8.f)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
-      l_run *= alpha;
-      m_run = m_new;
-      float a_row[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a_row[i] = __shfl(alpha, 4 * grp + i, 64);
-#pragma unroll
-      for (int n = 0; n < 16; ++n) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[n][i] *= a_row[i];
-      }
-    }
-    float p[4 * kHalves], ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4 * kHalves; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - m_run); ps += p[i]; }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l_run += ps;
-
-    {
-      // P k-slice of 8 tokens (2 micro-blocks) per lane: MFMA 16x16x32.  P
-      // goes in as two bf16 terms (value and residual), so the product with
-      // V carries no bf16 rounding of the weights.
-      u32x4 pa, pl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pa[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
-        pl[e] = pack_bf16x2(p[2 * e] - bf16_lo(pa[e]), p[2 * e + 1] - bf16_hi(pa[e]));
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        // dims 32c + 2*col (even tile) and 32c + 2*col + 1 (odd tile)
-        u32x4 be = {vh[0][c][0], vh[0][c][1], vh[1][c][0], vh[1][c][1]};
-        u32x4 bo = {vh[0][c][2], vh[0][c][3], vh[1][c][2], vh[1][c][3]};
-        o[2 * c] = mfma_16x16x32(pa, be, o[2 * c]);
-        o[2 * c + 1] = mfma_16x16x32(pa, bo, o[2 * c + 1]);
-        o[2 * c] = mfma_16x16x32(pl, be, o[2 * c]);
-        o[2 * c + 1] = mfma_16x16x32(pl, bo, o[2 * c + 1]);
-      }
-    }
-    if (kStagger && t + 1 < t_end) load_v(t + 1);
-    if (kFinal && more) load_v(t + t_step);
-  }
-  if (kFinal) {
-    // every wave is done with its key slots before the merge reuses them
-    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-    __syncthreads();
+    tile_logits(kh, qf, ql, sc);
+    if (t + 1 < t_end) load_k(t + 1);
+    tile_softmax_pv(sc, vh, o, m_run, l_run, t * kTileMB, cnt, n_mb, tail_slot, r.tail_len,
+                    scale, grp);
+    if (t + 1 < t_end) load_v(t + 1);
   }
 
-  // ---- merge the 4 waves in LDS
+  // ---- merge the 4 waves in LDS and write this split's partial
   if (grp == 0) { sh.m[wave][col] = m_run; sh.l[wave][col] = l_run; }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -427,9 +498,7 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     }
   }
   __syncthreads();
-
   const int d = threadIdx.x;   // one output dim per thread
-  float* pp = kFinal ? nullptr : part + ((int64_t)(row * 2 + g) * n_splits + split) * kPartFloats;
   for (int h = 0; h < kGroup; ++h) {
     float mx = -INFINITY;
 #pragma unroll
@@ -441,14 +510,8 @@ attend_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
       lsum += sh.l[w][h] * f;
       acc += sh.o[w][h][d] * f;
     }
-    if (kFinal) {
-      out[((int64_t)row * kQHeads + g * kGroup + h) * kHeadDim + d] =
-          (uint16_t)f32_to_bf16_bits(acc / lsum);
-      if (lse && d == 0) lse[(int64_t)row * kQHeads + g * kGroup + h] = (mx + log2f(lsum)) * kLn2;
-    } else {
-      pp[h * kHeadDim + d] = acc;
-      if (d == 0) { pp[kGroup * kHeadDim + h] = mx; pp[kGroup * kHeadDim + 16 + h] = lsum; }
-    }
+    pp[h * kHeadDim + d] = acc;
+    if (d == 0) { pp[kGroup * kHeadDim + h] = mx; pp[kGroup * kHeadDim + 16 + h] = lsum; }
   }
 }
 
@@ -522,11 +585,10 @@ void launch_split_decode(const void* q, const int32_t* cu_q, const int32_t* seq_
                          float* part, const qsa::RopeFreq& fr, float softmax_scale,
                          const qsa::Pages& pg, hipStream_t st) {
   const int sp = decode_splits(n_rows);
-  hipLaunchKernelGGL(qsa::attend_kernel<false>, dim3(n_rows * 2 * sp), dim3(256), 0, st,
+  hipLaunchKernelGGL(qsa::attend_split_kernel, dim3(n_rows * 2 * sp), dim3(256), 0, st,
                      (const uint16_t*)q, cu_q, seq_len, n_seq, n_rows, (const uint16_t*)k_cache,
                      (const uint16_t*)v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
-                     budget, sp, one_per_seq, (uint16_t*)nullptr, (float*)nullptr, part, fr,
-                     softmax_scale, pg, 0);
+                     budget, sp, one_per_seq, part, fr, softmax_scale, pg);
   const dim3 g(n_rows * 2 * qsa::kGroup);
   const float* cp = part;
   switch (sp) {
@@ -550,14 +612,16 @@ int check_attend_common(const void* q, const void* k_cache, const void* v_cache,
   return QSA_OK;
 }
 
-// aligned: the time-aligned sweep of qsa_attend_prefill_aligned
-int attend_prefill_launch(int aligned, const void* q, const int32_t* cu_q,
-                          const int32_t* seq_len, int32_t n_seq, int32_t n_q, int32_t max_q_len,
-                          const void* k_cache, const void* v_cache, int64_t kv_seq_stride,
-                          int64_t kv_head_stride, const int32_t* sel, const int32_t* sel_count,
-                          int32_t budget, void* out, float* lse, const double* inv_freq,
-                          float softmax_scale, const int32_t* block_table, int64_t table_stride,
-                          int32_t page_tokens, void* stream) {
+}  // namespace
+
+extern "C" {
+
+int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_len, int32_t n_seq,
+                       int32_t n_q, int32_t max_q_len, const void* k_cache, const void* v_cache,
+                       int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
+                       const int32_t* sel_count, int32_t budget, void* out, float* lse,
+                       const double* inv_freq, float softmax_scale, const int32_t* block_table,
+                       int64_t table_stride, int32_t page_tokens, void* stream) {
   if (n_q < 0 || n_seq < 0 || max_q_len < 0) return QSA_ERR_INVALID_ARG;
   qsa::RopeFreq fr;
   if (!qsa_host::make_rope_freq(inv_freq, fr) || !qsa_host::softmax_scale_ok(softmax_scale))
@@ -569,42 +633,15 @@ int attend_prefill_launch(int aligned, const void* q, const int32_t* cu_q,
   int st = check_attend_common(q, k_cache, v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
                                budget, out);
   if (st != QSA_OK) return st;
-  if ((int64_t)n_q * 2 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(qsa::attend_kernel<true>, dim3(n_q * 2), dim3(256), 0, (hipStream_t)stream,
-                     (const uint16_t*)q, cu_q, seq_len, n_seq, n_q, (const uint16_t*)k_cache,
-                     (const uint16_t*)v_cache, kv_seq_stride, kv_head_stride, sel, sel_count,
-                     budget, 1, 0, (uint16_t*)out, lse, (float*)nullptr, fr, softmax_scale, pg,
-                     aligned);
+  // 4 rows (one per wave) of one KV head per workgroup
+  const int64_t n_wg = (((int64_t)n_q + qsa::kWaves - 1) / qsa::kWaves) * 2;
+  if (n_wg > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(qsa::attend_rows_kernel, dim3((unsigned)n_wg), dim3(256), 0,
+                     (hipStream_t)stream, (const uint16_t*)q, cu_q, seq_len, n_seq, n_q,
+                     (const uint16_t*)k_cache, (const uint16_t*)v_cache, kv_seq_stride,
+                     kv_head_stride, sel, sel_count, budget, (uint16_t*)out, lse, fr,
+                     softmax_scale, pg);
   return qsa_host::launch_status();
-}
-
-}  // namespace
-
-extern "C" {
-
-int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_len, int32_t n_seq,
-                       int32_t n_q, int32_t max_q_len, const void* k_cache, const void* v_cache,
-                       int64_t kv_seq_stride, int64_t kv_head_stride, const int32_t* sel,
-                       const int32_t* sel_count, int32_t budget, void* out, float* lse,
-                       const double* inv_freq, float softmax_scale, const int32_t* block_table,
-                       int64_t table_stride, int32_t page_tokens, void* stream) {
-  return attend_prefill_launch(0, q, cu_q, seq_len, n_seq, n_q, max_q_len, k_cache, v_cache,
-                               kv_seq_stride, kv_head_stride, sel, sel_count, budget, out, lse,
-                               inv_freq, softmax_scale, block_table, table_stride, page_tokens,
-                               stream);
-}
-
-int qsa_attend_prefill_aligned(const void* q, const int32_t* cu_q, const int32_t* seq_len,
-                               int32_t n_seq, int32_t n_q, int32_t max_q_len, const void* k_cache,
-                               const void* v_cache, int64_t kv_seq_stride, int64_t kv_head_stride,
-                               const int32_t* sel, const int32_t* sel_count, int32_t budget,
-                               void* out, float* lse, const double* inv_freq, float softmax_scale,
-                               const int32_t* block_table, int64_t table_stride,
-                               int32_t page_tokens, void* stream) {
-  return attend_prefill_launch(1, q, cu_q, seq_len, n_seq, n_q, max_q_len, k_cache, v_cache,
-                               kv_seq_stride, kv_head_stride, sel, sel_count, budget, out, lse,
-                               inv_freq, softmax_scale, block_table, table_stride, page_tokens,
-                               stream);
 }
 
 size_t qsa_attend_decode_multi_workspace(int32_t n_q) {

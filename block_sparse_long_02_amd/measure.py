@@ -54,23 +54,20 @@ COPY_BYTES = 1 << 30
 # decode step of 131,073 tokens completes no new block).  The transformed
 # pooling runs twice (prefix, then the step's new blocks).  The prefill
 # kernels run twice, in the plain step (dispatch 0) and in the step with the
-# indexer transforms (dispatch 1), which selects other blocks; the prefill
-# attention three times: the plain step's (time-aligned), the ordered
-# attention on the same selection, the transformed step's (time-aligned).
+# indexer transforms (dispatch 1), which selects other blocks.
 KERNELS = {
     "pool_block_keys_prefill_1m": ("pool_block_keys_kernel", "qsa_pool.hip", 1),
     "score_sample_prefill_1m": ("score_gemm_kernel<2, 4, true, false>", "qsa_index.hip", 0),
     "threshold_prefill_1m": ("threshold_kernel", "qsa_index.hip", 0),
     "score_filter_prefill_1m": ("score_gemm_kernel<2, 8, false, false>", "qsa_index.hip", 0),
     "final_select_prefill_1m": ("final_select_kernel", "qsa_index.hip", 0),
-    "attend_prefill_1m": ("attend_kernel<true>", "qsa_attend.hip", 0),
-    "attend_prefill_1m_ordered": ("attend_kernel<true>", "qsa_attend.hip", 1),
-    "attend_prefill_1m_transformed": ("attend_kernel<true>", "qsa_attend.hip", 2),
+    "attend_prefill_1m": ("attend_rows_kernel", "qsa_attend.hip", 0),
+    "attend_prefill_1m_transformed": ("attend_rows_kernel", "qsa_attend.hip", 1),
     "score_dense_decode_128k": ("score_dense_kernel<false>", "qsa_index.hip", None),
     "select_dense_decode_128k": ("select_dense_kernel", "qsa_index.hip", None),
     "key_transform_prefill_1m": ("pool_block_keys_normed_kernel", "qsa_index_transform.hip", 1),
     "query_transform_prefill_1m": ("index_query_transform_kernel", "qsa_index_transform.hip", None),
-    "attend_decode_128k": ("attend_kernel<false>", "qsa_attend.hip", None),
+    "attend_decode_128k": ("attend_split_kernel", "qsa_attend.hip", None),
     "combine_decode_128k": ("combine_kernel", "qsa_attend.hip", None),
 }
 
@@ -81,9 +78,8 @@ def src_hash(name: str) -> str:
 
 
 def probe():
-    """The program the counter runs profile: copy, one prefill step (plain, with
-    the time-aligned attention), the ordered attention on the same selection,
-    one prefill step with the indexer transforms, one decode step."""
+    """The program the counter runs profile: copy, one prefill step (plain, then
+    with the indexer transforms), one decode step."""
     import torch
     from . import workloads as W
     from .runner import QSARunner
@@ -96,18 +92,14 @@ def probe():
     print("MARK copy done", flush=True)
 
     b = W.chunked_prefill_1m(device="cuda")
-    r = QSARunner(b, time_aligned=True)
+    r = QSARunner(b)
     torch.cuda.synchronize()
     print("MARK prefill step", flush=True)
     r.step()
     torch.cuda.synchronize()
-    print("MARK ordered attention", flush=True)
-    r.time_aligned = False
-    r.attend()
-    torch.cuda.synchronize()
     del r
     torch.cuda.empty_cache()
-    r = QSARunner(b, transforms=True, time_aligned=True)
+    r = QSARunner(b, transforms=True)
     torch.cuda.synchronize()
     print("MARK prefill step with indexer transforms", flush=True)
     r.step()
@@ -243,7 +235,7 @@ def peaks(out_json: str):
 
 
 HEADLINE = ["pool_block_keys_kernel", "score_gemm_kernel<2, 4, true, false>", "threshold_kernel",
-            "score_gemm_kernel<2, 8, false, false>", "final_select_kernel", "attend_kernel<true>"]
+            "score_gemm_kernel<2, 8, false, false>", "final_select_kernel", "attend_rows_kernel"]
 
 
 def stats(trace_csv: str, out_md: str, steps: str, warmup: str):
@@ -261,7 +253,7 @@ def stats(trace_csv: str, out_md: str, steps: str, warmup: str):
     # the headline step's boundaries: its first WARMUP + STEPS attention
     # launches at the chunk's full grid; step i runs from the end of
     # attention launch i - 1 to the end of attention launch i
-    att = [r for r in rows if "attend_kernel<true>" in r["Kernel_Name"]]
+    att = [r for r in rows if "attend_rows_kernel" in r["Kernel_Name"]]
     g0 = grid(att[0])
     ends = [int(r["End_Timestamp"]) for r in att if grid(r) == g0][:warmup + steps]
     windows = list(zip([0] + ends[:-1], ends))[warmup:]

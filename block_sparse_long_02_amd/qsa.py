@@ -47,10 +47,6 @@ SIGNATURES = {
                                           _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i32, _c_void_p,
                                           _c_void_p, _c_void_p, ctypes.c_float, _c_void_p, _i64,
                                           _i32, _c_void_p]),
-    "qsa_attend_prefill_aligned": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
-                                                  _c_void_p, _c_void_p, _i64, _i64, _c_void_p,
-                                                  _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p,
-                                                  ctypes.c_float, _c_void_p, _i64, _i32, _c_void_p]),
     "qsa_attend_decode_workspace": (_size, [_i32]),
     "qsa_attend_decode": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _i64, _i64,
                                          _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p,
@@ -220,19 +216,15 @@ def index_select(idx_q, w, cu_q, seq_len, max_q_len, max_blocks, block_keys, bud
 
 
 def attend_prefill(q, cu_q, seq_len, max_q_len, k_cache, v_cache, sel, sel_count, budget, out,
-                   lse=None, inv_freq=None, softmax_scale=SOFTMAX_SCALE, pages=None, stream=None,
-                   time_aligned=False):
-    """qsa_attend_prefill, or qsa_attend_prefill_aligned with time_aligned=True
-    (same attention; the order of its float32 sums follows timing)."""
+                   lse=None, inv_freq=None, softmax_scale=SOFTMAX_SCALE, pages=None, stream=None):
     _dev(q, cu_q, seq_len, k_cache, v_cache, sel, sel_count, out, lse)
     fp, _keep = _host_f64(inv_freq)
-    name = "qsa_attend_prefill_aligned" if time_aligned else "qsa_attend_prefill"
-    st = getattr(lib(), name)(_p(q), _p(cu_q), _p(seq_len), seq_len.numel(), q.shape[0],
-                              int(max_q_len), _p(k_cache), _p(v_cache),
-                              *_kv_strides(k_cache, pages), _p(sel), _p(sel_count), int(budget),
-                              _p(out), _p(lse), fp, float(softmax_scale), *_pages(pages),
-                              _stream(stream))
-    _check(name, st)
+    st = lib().qsa_attend_prefill(_p(q), _p(cu_q), _p(seq_len), seq_len.numel(), q.shape[0],
+                                  int(max_q_len), _p(k_cache), _p(v_cache),
+                                  *_kv_strides(k_cache, pages), _p(sel), _p(sel_count), int(budget),
+                                  _p(out), _p(lse), fp, float(softmax_scale), *_pages(pages),
+                                  _stream(stream))
+    _check("qsa_attend_prefill", st)
 
 
 def attend_decode_workspace(n_seq) -> int:

@@ -33,8 +33,7 @@ def piece_bounds(n: int, parts: int) -> list[int]:
 class QSARunner:
     def __init__(self, batch: QSABatch, decode: bool | None = None, transforms: bool = False,
                  gamma_k=None, gamma_q=None, eps: float = 1e-6, yarn: bool = False,
-                 paged: int | None = None, page_seed: int = 0, shared_pages=None,
-                 time_aligned: bool = False):
+                 paged: int | None = None, page_seed: int = 0, shared_pages=None):
         """transforms=True applies the pages' indexer transforms: block keys are
         pooled, RMS-normalised and rotated; each step first normalises and
         rotates the indexer queries into a buffer of its own.  yarn=True
@@ -44,11 +43,8 @@ class QSARunner:
         every cache in pools of P-token pages, in a seeded random physical
         order; shared_pages = {dst: (src, n)} maps the first n pages of
         sequence dst onto those of src (the caller makes their tokens equal),
-        as a prefix cache would.  time_aligned=True attends prefill rows with
-        qsa_attend_prefill_aligned (the same attention; the order of its
-        float32 sums follows timing, so results are not bit-reproducible)."""
+        as a prefix cache would."""
         b = batch
-        self.time_aligned = bool(time_aligned)
         assert b.idx_q.is_cuda, "batch must live on the GPU"
         self.b = b
         self.decode = (b.meta.get("kind") == "decode") if decode is None else decode
@@ -162,8 +158,7 @@ class QSARunner:
                                     **rope)
         else:
             qsa.attend_prefill(b.q, b.cu_q, b.seq_len, self.max_q_len, self.k_cache, self.v_cache,
-                               self.sel, self.sel_count, self.budget, self.out, self.lse,
-                               time_aligned=self.time_aligned, **rope)
+                               self.sel, self.sel_count, self.budget, self.out, self.lse, **rope)
 
     def step(self, stream=None):
         self.pool(stream)

@@ -279,27 +279,6 @@ int qsa_attend_prefill(const void* q, const int32_t* cu_q, const int32_t* seq_le
                        void* stream);
 
 /*
- * a6, time-aligned -- the same attention as qsa_attend_prefill ([ailearn]
- * §03 CAUSAL SPARSE SET equation and fifth QSA step), with the same
- * arguments, layouts, ownership and errors.  Each row walks its selected
- * blocks starting at the block id a shared clock points to and wraps around,
- * so that the rows in flight fetch the same cache blocks at about the same
- * time and share them in L2 (1M-token chunk: about 10% faster than
- * qsa_attend_prefill).  Every row still attends over exactly S_i; only the
- * order of the float32 sums over S_i depends on timing, so results agree with
- * qsa_attend_prefill (and between runs) to float32 rounding, not bit for bit.
- * Use qsa_attend_prefill where bit-reproducible results are needed.
- */
-int qsa_attend_prefill_aligned(const void* q, const int32_t* cu_q, const int32_t* seq_len,
-                               int32_t n_seq, int32_t n_q, int32_t max_q_len,
-                               const void* k_cache, const void* v_cache,
-                               int64_t kv_seq_stride, int64_t kv_head_stride,
-                               const int32_t* sel, const int32_t* sel_count, int32_t budget,
-                               void* out, float* lse, const double* inv_freq,
-                               float softmax_scale, const int32_t* block_table,
-                               int64_t table_stride, int32_t page_tokens, void* stream);
-
-/*
  * a7 -- split-K decode attention plus combine.  Same mathematics as
  * qsa_attend_prefill for one query per sequence at position seq_len[s]-1
  * (row s of q, sel, out, lse).  The selected set is split across workgroups

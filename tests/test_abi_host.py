@@ -31,7 +31,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
         assert n in qsa.SIGNATURES, n
@@ -96,12 +96,7 @@ def test_attention_and_pool_reject_bad_arguments(L):
     assert L.qsa_attend_prefill(A, None, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, None, 0.0625, None, 0, 0, None) == 1
     assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1020, 512, A, A, 16, A, None, None, 0.0625, None, 0, 0, None) == 1
     assert L.qsa_attend_prefill(A, A, A, 1, 0, 4, A, A, 1024, 512, A, A, 16, A, None, None, 0.0625, None, 0, 0, None) == 0
-    # the time-aligned prefill checks its arguments the same way
-    for f in (L.qsa_attend_prefill, L.qsa_attend_prefill_aligned):
-        assert f(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 0, A, None, None, 0.0625, None, 0, 0, None) == 1
-        assert f(A, A, A, 1, 4, 4, A, MISALIGNED, 1024, 512, A, A, 16, A, None, None, 0.0625, None, 0, 0, None) == 1
-        assert f(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, None, -1.0, None, 0, 0, None) == 1
-        assert f(A, A, A, 1, 0, 4, A, A, 1024, 512, A, A, 16, A, None, None, 0.0625, None, 0, 0, None) == 0
+    assert L.qsa_attend_prefill(A, A, A, 1, 4, 4, A, A, 1024, 512, A, A, 16, A, None, None, -1.0, None, 0, 0, None) == 1
     # decode: workspace too small, bad budget
     assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 16, A, A, A, 100, None, 0.0625, None, 0, 0, None) == 3
     assert L.qsa_attend_decode(A, A, 4, A, A, 1024, 512, A, A, 600, A, A, A, 1 << 30, None, 0.0625, None, 0, 0, None) == 1

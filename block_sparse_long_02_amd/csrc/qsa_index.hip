@@ -1177,10 +1177,26 @@ final_select_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict_
     if (threadIdx.x == 0) sel_count[row] = k;
     return;
   }
-  for (int i = threadIdx.x; i < c; i += 256) {
-    const u32x2 e = cand[(int64_t)row * kCandCap + i];
-    sh.key[i] = e[0];
-    sh.idx[i] = (int)e[1];
+  // the list into LDS: every 16-byte load (two entries) is issued before the
+  // first LDS write, so the row costs one memory round trip, not one per 256
+  // entries.  Rows start 16-byte aligned and hold kCandCap (even) slots, so
+  // the pair holding entry c - 1 is readable whole.
+  {
+    constexpr int kPairsPer = kCandCap / 2 / 256;
+    const u32x4* src = reinterpret_cast<const u32x4*>(cand + (int64_t)row * kCandCap);
+    const int n_pairs = (c + 1) >> 1;
+    u32x4 e[kPairsPer];
+#pragma unroll
+    for (int u = 0; u < kPairsPer; ++u) {
+      const int q = threadIdx.x + 256 * u;
+      e[u] = q < n_pairs ? src[q] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kPairsPer; ++u) {
+      const int i = 2 * (threadIdx.x + 256 * u);
+      if (i < c) { sh.key[i] = e[u][0]; sh.idx[i] = (int)e[u][1]; }
+      if (i + 1 < c) { sh.key[i + 1] = e[u][2]; sh.idx[i + 1] = (int)e[u][3]; }
+    }
   }
   __syncthreads();
   select_from_list(sh.key, sh.idx, c, k, sh.ids, sh.ids_tmp, g.n_c, &sh.n_out,

@@ -601,11 +601,12 @@ score_gemm_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ 
 
 // ------------------------------------------------------ LDS radix select
 // k-th largest value (1-based) among the participating elements, where
-// get(i) -> {participates, value} for i < n and values have `nbits` bits.
-// 11-bit digits from the top.  Needs kBins ints of LDS in `hist`.
-template <class Get>
-__device__ uint32_t block_kth_largest(Get get, int n, int k, int nbits, int* hist, int* tmp,
-                                      int* res) {
+// each(f) calls f(participates, value) for every element this thread holds
+// and values have `nbits` bits.  11-bit digits from the top.  Needs kBins
+// ints of LDS in `hist`.
+template <class Each>
+__device__ uint32_t block_kth_largest_each(Each each, int k, int nbits, int* hist, int* tmp,
+                                           int* res) {
   uint32_t prefix = 0, pmask = 0;
   for (int top = nbits; top > 0;) {
     const int width = top >= 11 ? 11 : top;
@@ -613,11 +614,9 @@ __device__ uint32_t block_kth_largest(Get get, int n, int k, int nbits, int* his
     const int bins = 1 << width;
     for (int i = threadIdx.x; i < bins; i += 256) hist[i] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += 256) {
-      bool in;
-      uint32_t v = get(i, in);
+    each([&](bool in, uint32_t v) {
       if (in && (v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & (bins - 1)], 1);
-    }
+    });
     __syncthreads();
     // thread t owns bins [per*t, per*t + per)
     const int per = (bins + 255) / 256;
@@ -643,6 +642,22 @@ __device__ uint32_t block_kth_largest(Get get, int n, int k, int nbits, int* his
   return prefix;
 }
 
+// The same over get(i) -> {participates, value} for i < n, thread t taking
+// i = t, t + 256, ...
+template <class Get>
+__device__ uint32_t block_kth_largest(Get get, int n, int k, int nbits, int* hist, int* tmp,
+                                      int* res) {
+  return block_kth_largest_each(
+      [&](auto f) {
+        for (int i = threadIdx.x; i < n; i += 256) {
+          bool in;
+          const uint32_t v = get(i, in);
+          f(in, v);
+        }
+      },
+      k, nbits, hist, tmp, res);
+}
+
 // Block-wide min and max of one value per thread (ends with a barrier).
 __device__ void block_min_max(uint32_t lo, uint32_t hi, int* tmp, uint32_t& out_lo,
                               uint32_t& out_hi) {
@@ -659,7 +674,9 @@ __device__ void block_min_max(uint32_t lo, uint32_t hi, int* tmp, uint32_t& out_
   __syncthreads();
 }
 
-// k-th largest (1 <= k <= n) of get(0..n), keys < 2^31.  Range-adaptive
+// k-th largest (1 <= k <= n) of n keys < 2^31, where each(f) calls f(key)
+// for every key this thread holds (the workgroup's threads hold all n
+// between them, each key once).  Range-adaptive
 // histogram passes: the current key range [lo, hi] (first the keys' min and
 // max) is cut into at most 2048 bins of 2^s keys, bin = (key - lo) >> s, so
 // that keys crowded in a narrow range still spread over many bins.  Each pass
@@ -675,15 +692,11 @@ struct KthLds {
   int* bin_n;      // 1
 };
 
-template <class Get>
-__device__ uint32_t kth_largest_fast(Get get, int n, int k, const KthLds& sh) {
+template <class Each>
+__device__ uint32_t kth_largest_each(Each each, int k, const KthLds& sh) {
   const int tid = threadIdx.x;
   uint32_t lo = 0xFFFFFFFFu, hi = 0;
-  for (int i = tid; i < n; i += 256) {
-    const uint32_t v = get(i);
-    lo = min(lo, v);
-    hi = max(hi, v);
-  }
+  each([&](uint32_t v) { lo = min(lo, v); hi = max(hi, v); });
   block_min_max(lo, hi, sh.tmp, lo, hi);
   for (;;) {
     const uint32_t span = hi - lo;
@@ -691,10 +704,9 @@ __device__ uint32_t kth_largest_fast(Get get, int n, int k, const KthLds& sh) {
     for (int i = tid; i < kBins; i += 256) sh.hist[i] = 0;
     if (tid == 0) *sh.bin_n = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += 256) {
-      const uint32_t v = get(i);
+    each([&](uint32_t v) {
       if (v >= lo && v <= hi) atomicAdd(&sh.hist[(v - lo) >> s], 1);
-    }
+    });
     __syncthreads();
     constexpr int per = kBins / 256;
     const int b0 = tid * per;
@@ -719,10 +731,9 @@ __device__ uint32_t kth_largest_fast(Get get, int n, int k, const KthLds& sh) {
     if (s == 0) return blo;
     if (hb <= kFinishCap) {
       const uint32_t bhi = blo + ((1u << s) - 1u);
-      for (int i = tid; i < n; i += 256) {
-        const uint32_t v = get(i);
+      each([&](uint32_t v) {
         if (v >= blo && v <= bhi) sh.bin[atomicAdd(sh.bin_n, 1)] = v;
-      }
+      });
       __syncthreads();
       if (tid < hb) {
         const uint32_t x = sh.bin[tid];
@@ -742,6 +753,16 @@ __device__ uint32_t kth_largest_fast(Get get, int n, int k, const KthLds& sh) {
     lo = blo;
     hi = blo + ((1u << s) - 1u);
   }
+}
+
+// kth_largest_each over get(0..n), thread t taking i = t, t + 256, ...
+template <class Get>
+__device__ uint32_t kth_largest_fast(Get get, int n, int k, const KthLds& sh) {
+  return kth_largest_each(
+      [&](auto f) {
+        for (int i = threadIdx.x; i < n; i += 256) f(get(i));
+      },
+      k, sh);
 }
 
 // f(v) for each of the n uint32 values at p (16-byte aligned, readable up
@@ -769,69 +790,11 @@ __device__ __forceinline__ void for_each_u32(const uint32_t* __restrict__ p, int
   }
 }
 
-// kth_largest_fast for values in global memory, each pass through
+// kth_largest_each for values in global memory, each pass through
 // for_each_u32.  Ends with a barrier.
 __device__ uint32_t kth_largest_global(const uint32_t* __restrict__ p, int n, int k,
                                        const KthLds& sh) {
-  const int tid = threadIdx.x;
-  uint32_t lo = 0xFFFFFFFFu, hi = 0;
-  for_each_u32(p, n, [&](uint32_t v) { lo = min(lo, v); hi = max(hi, v); });
-  block_min_max(lo, hi, sh.tmp, lo, hi);
-  for (;;) {
-    const uint32_t span = hi - lo;
-    const int s = span < (uint32_t)kBins ? 0 : 32 - __clz((int)(span >> 11));   // span >> s < 2048
-    for (int i = tid; i < kBins; i += 256) sh.hist[i] = 0;
-    if (tid == 0) *sh.bin_n = 0;
-    __syncthreads();
-    for_each_u32(p, n, [&](uint32_t v) {
-      if (v >= lo && v <= hi) atomicAdd(&sh.hist[(v - lo) >> s], 1);
-    });
-    __syncthreads();
-    constexpr int per = kBins / 256;
-    const int b0 = tid * per;
-    int local = 0;
-#pragma unroll
-    for (int b = 0; b < per; ++b) local += sh.hist[b0 + b];
-    int total;
-    const int excl = block_excl_scan_256(local, sh.tmp, total);
-    int run = total - excl - local;   // values in the bins above this thread's
-#pragma unroll
-    for (int b = per - 1; b >= 0; --b) {
-      const int h = sh.hist[b0 + b];
-      if (run < k && run + h >= k) { sh.res[0] = b0 + b; sh.res[1] = run; }
-      run += h;
-    }
-    __syncthreads();
-    const uint32_t B = (uint32_t)sh.res[0];
-    k -= sh.res[1];
-    const int hb = sh.hist[B];
-    __syncthreads();
-    const uint32_t blo = lo + (B << s);
-    if (s == 0) return blo;
-    if (hb <= kFinishCap) {
-      const uint32_t bhi = blo + ((1u << s) - 1u);
-      for_each_u32(p, n, [&](uint32_t v) {
-        if (v >= blo && v <= bhi) sh.bin[atomicAdd(sh.bin_n, 1)] = v;
-      });
-      __syncthreads();
-      if (tid < hb) {
-        const uint32_t x = sh.bin[tid];
-        int gt = 0, ge = 0;
-        for (int j = 0; j < hb; ++j) {
-          const uint32_t y = sh.bin[j];
-          gt += y > x;
-          ge += y >= x;
-        }
-        if (gt < k && k <= ge) sh.res[0] = (int)x;   // every writer has the same x
-      }
-      __syncthreads();
-      const uint32_t T = (uint32_t)sh.res[0];
-      __syncthreads();
-      return T;
-    }
-    lo = blo;
-    hi = blo + ((1u << s) - 1u);
-  }
+  return kth_largest_each([&](auto f) { for_each_u32(p, n, f); }, k, sh);
 }
 
 // The k (<= kMaxBudget) distinct ids in ids[] (each < n), written to
@@ -1033,47 +996,67 @@ __device__ void exact_select_recompute(const uint16_t* __restrict__ q4, const fl
 }
 
 // ------------------------------------------------------ list selection
-// Exact top-k (score desc, block asc) of an unordered list of c >= k
-// candidates held in LDS (key[], idx[]), written to out[0..k) in ascending
-// block order and -1 up to budget.  Radix select on the score key, then on
-// the block id among ties at the threshold; the k ids sorted by buckets.
-__device__ void select_from_list(const uint32_t* key, const int* idx, int c, int k, int* ids,
-                                 int* ids_tmp, int n_ids, int* n_out, const KthLds& lds,
-                                 int32_t* __restrict__ out, int budget) {
+// A row's candidate list as the workgroup holds it: thread t keeps the
+// entries 2q and 2q + 1, q = t + 256 u (u < kPairsPer), as one 16-byte pair
+// {key, id, key, id} in registers; entries at or past c are not part of it.
+constexpr int kPairsPer = kCandCap / 2 / 256;
+struct RegList {
+  u32x4 e[kPairsPer];
+  int c;
+  // f(key, id) for every entry this thread holds
+  template <class F>
+  __device__ __forceinline__ void each(F f) const {
+#pragma unroll
+    for (int u = 0; u < kPairsPer; ++u) {
+      const int i = 2 * ((int)threadIdx.x + 256 * u);
+      if (i < c) f(e[u][0], (int)e[u][1]);
+      if (i + 1 < c) f(e[u][2], (int)e[u][3]);
+    }
+  }
+};
+
+// Exact top-k (score desc, block asc) of a list of c >= k candidates, written
+// to out[0..k) in ascending block order and -1 up to budget.  Radix select
+// on the score key, then on the block id among ties at the threshold; the k
+// ids sorted by buckets.
+__device__ void select_from_list(const RegList& L, int k, int* ids, int* ids_tmp, int n_ids,
+                                 int* n_out, const KthLds& lds, int32_t* __restrict__ out,
+                                 int budget) {
   int* hist = lds.hist;
   int* tmp = lds.tmp;
   int* res = lds.res;
   uint32_t tau = 0, iota_cut = 0xFFFFFFFFu;
-  const bool all = c == k;
+  const bool all = L.c == k;
   if (threadIdx.x == 0) *n_out = 0;
   if (!all) {
-    tau = kth_largest_fast([&](int i) { return key[i]; }, c, k, lds);
+    tau = kth_largest_each([&](auto f) { L.each([&](uint32_t key, int) { f(key); }); }, k, lds);
     int above = 0, ties = 0;
-    for (int i = threadIdx.x; i < c; i += 256) {
-      above += key[i] > tau;
-      ties += key[i] == tau;
-    }
+    L.each([&](uint32_t key, int) {
+      above += key > tau;
+      ties += key == tau;
+    });
     int tot_above, tot_ties;
     block_excl_scan_256(above, tmp, tot_above);
     block_excl_scan_256(ties, tmp, tot_ties);
     const int need = k - tot_above;
     if (need < tot_ties) {
       // the `need` lowest block ids among the ties: k-th largest of (2^22-1-id)
-      const uint32_t v = block_kth_largest(
-          [&](int i, bool& in) { in = key[i] == tau; return 0x3FFFFFu - (uint32_t)idx[i]; }, c,
+      const uint32_t v = block_kth_largest_each(
+          [&](auto f) {
+            L.each([&](uint32_t key, int id) { f(key == tau, 0x3FFFFFu - (uint32_t)id); });
+          },
           need, 22, hist, tmp, res);
       iota_cut = 0x3FFFFFu - v;
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < c; i += 256) {
-    const uint32_t kk = key[i];
-    const bool take = all || kk > tau || (kk == tau && (uint32_t)idx[i] <= iota_cut);
+  L.each([&](uint32_t key, int id) {
+    const bool take = all || key > tau || (key == tau && (uint32_t)id <= iota_cut);
     if (take) {
       const int slot = atomicAdd(n_out, 1);
-      if (slot < kMaxBudget) ids[slot] = idx[i];
+      if (slot < kMaxBudget) ids[slot] = id;
     }
-  }
+  });
   __syncthreads();
   if (k > 0) sort_ids_to(ids, k, n_ids, hist, ids_tmp, tmp, out);
   for (int i = k + threadIdx.x; i < budget; i += 256) out[i] = -1;
@@ -1140,8 +1123,6 @@ __device__ void select_ordered(Get get, Id id, int n, int k, int* hist, int* tmp
 
 // --------------------------------------------------------- final select
 struct SelectShared {
-  uint32_t key[kCandCap];
-  int idx[kCandCap];
   int hist[kBins];
   uint32_t bin[kFinishCap];
   int ids[kMaxBudget];
@@ -1177,29 +1158,21 @@ final_select_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict_
     if (threadIdx.x == 0) sel_count[row] = k;
     return;
   }
-  // the list into LDS: every 16-byte load (two entries) is issued before the
-  // first LDS write, so the row costs one memory round trip, not one per 256
-  // entries.  Rows start 16-byte aligned and hold kCandCap (even) slots, so
-  // the pair holding entry c - 1 is readable whole.
+  // the list into registers, every 16-byte load (two entries) in flight at
+  // once: one memory round trip per row.  Rows start 16-byte aligned and hold
+  // kCandCap (even) slots, so the pair holding entry c - 1 is readable whole.
+  RegList L;
+  L.c = c;
   {
-    constexpr int kPairsPer = kCandCap / 2 / 256;
     const u32x4* src = reinterpret_cast<const u32x4*>(cand + (int64_t)row * kCandCap);
     const int n_pairs = (c + 1) >> 1;
-    u32x4 e[kPairsPer];
 #pragma unroll
     for (int u = 0; u < kPairsPer; ++u) {
       const int q = threadIdx.x + 256 * u;
-      e[u] = q < n_pairs ? src[q] : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < kPairsPer; ++u) {
-      const int i = 2 * (threadIdx.x + 256 * u);
-      if (i < c) { sh.key[i] = e[u][0]; sh.idx[i] = (int)e[u][1]; }
-      if (i + 1 < c) { sh.key[i + 1] = e[u][2]; sh.idx[i + 1] = (int)e[u][3]; }
+      L.e[u] = q < n_pairs ? src[q] : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  __syncthreads();
-  select_from_list(sh.key, sh.idx, c, k, sh.ids, sh.ids_tmp, g.n_c, &sh.n_out,
+  select_from_list(L, k, sh.ids, sh.ids_tmp, g.n_c, &sh.n_out,
                    KthLds{sh.hist, sh.bin, sh.tmp, sh.res, &sh.bin_n}, out, budget);
   if (threadIdx.x == 0) sel_count[row] = k;
 }

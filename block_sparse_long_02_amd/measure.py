@@ -327,6 +327,15 @@ def pmc(out_md: str, *csvs: str):
             derived.append(("VALU instructions per MFMA (MFMA included)", c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"]))
         if "SQ_INSTS_MFMA" in c and "SQ_INSTS_LDS" in c and c["SQ_INSTS_MFMA"]:
             derived.append(("LDS instructions per MFMA", c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"]))
+        # L2 (TCC counters summed over every channel of the 8 XCDs)
+        hit, miss = c.get("TCC_HIT_sum"), c.get("TCC_MISS_sum")
+        if hit is not None and miss is not None and hit + miss > 0:
+            derived.append(("L2 hit rate (of L2 requests)", hit / (hit + miss)))
+        lvl, rd = c.get("TCC_EA0_RDREQ_LEVEL_sum"), c.get("TCC_EA0_RDREQ_sum")
+        if lvl is not None and rd:
+            derived.append(("cycles a read beyond L2 waits, average", lvl / rd))
+            if cyc:
+                derived.append(("reads beyond L2 in flight, average over the dispatch", lvl / cyc))
         w = c.get("SQ_WAVE_CYCLES")
         if w:
             for n, label in (("SQ_WAIT_ANY", "wave cycles waiting on anything"),

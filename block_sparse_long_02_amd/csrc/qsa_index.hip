@@ -109,46 +109,70 @@ __device__ __forceinline__ float block_score(f32x4 acc, const float* __restrict_
 // per block against the 256-byte block key the kernel must stream anyway, and
 // lets the select read scores instead of recomputing them; every 16th score
 // also goes to a contiguous sample row.  Workgroup = one
-// sequence's queries (m-tile rows 4*query + head) x kDenseChunk columns; wave
+// sequence's queries (m-tile rows 4*query + head) x one chunk of columns; wave
 // w takes the 16-column tiles w, w+4, ...  The tile loop is fully unrolled so
 // that kDenseDepth tiles of keys stay in flight with exact wait counts, and
 // the scores are stored after the last tile.
+//
+// Chunk size.  A launch whose 1024-column chunks fill the chip's workgroup
+// slots streams best in those chunks: each wave keeps 4 tiles in flight
+// through 16 tiles without a gap between workgroup rounds.  A launch whose
+// rows are few or mostly short (a ragged batch with one long row) leaves
+// most CUs with one such workgroup or none, and the long row's chunks each
+// take 4 memory round trips; 256-column chunks put 4 times as many of its
+// bytes in flight at once.  The kernel picks the size itself from the
+// sequence lengths (the host knows only the longest): every workgroup counts
+// the launch's active 1024-column chunks the same way and so takes the same
+// decision.
 constexpr int kDenseChunk = 1024;
-constexpr int kDenseTiles = kDenseChunk / 64;   // tiles per wave
+constexpr int kDenseChunkSmall = 256;
 constexpr int kDenseDepth = 4;
+// workgroup slots of the chip for this kernel (256 CUs x 4)
+constexpr int kDenseSlots = 1024;
+// launches of up to this many sequences choose their chunk size (one wave
+// counts the chunks, one sequence per lane)
+constexpr int kDenseAdaptSeqs = 64;
 
-template <bool kPaged>
-__global__ void __launch_bounds__(256, 4)
-score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
-                   const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
-                   int n_q, int max_blocks, const uint16_t* __restrict__ bk, int64_t bk_stride,
-                   uint32_t* __restrict__ dense, int64_t dense_stride,
-                   uint32_t* __restrict__ dsmp, int64_t dsmp_stride, int n_chunks, Pages pg) {
-  __shared__ float s_w[4][4];
-  __shared__ int s_nc[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  // one linear grid, sequence-major: a sequence's chunks take consecutive
-  // workgroup ids, which the dispatcher spreads over the XCDs (a grid of
-  // (sequences, chunks) would put every chunk of a sequence on one XCD
-  // whenever the sequence count is a multiple of 8)
-  const int s = blockIdx.x / n_chunks, chunk = blockIdx.x % n_chunks;
-  const int qb = cu_q[s], qe_raw = cu_q[s + 1];
-  const int qe = min(qe_raw, n_q);
-  if (qb >= qe || qb < 0) return;
-  const int pos0 = seq_len[s] - (qe_raw - qb);
-  const int n_rows = min(4, qe - qb);
+// Rows of sequence s scored by the dense pass: n_rows (<= 4) rows ending at
+// its last position, candidates up to nc_last; false if it has no query row.
+struct DenseSeq {
+  int qb, qe, qe_raw, pos0, n_rows, nc_last;
+};
+__device__ __forceinline__ bool dense_seq(const int32_t* __restrict__ cu_q,
+                                          const int32_t* __restrict__ seq_len, int n_q,
+                                          int max_blocks, int s, DenseSeq& d) {
+  d.qb = cu_q[s];
+  d.qe_raw = cu_q[s + 1];
+  d.qe = min(d.qe_raw, n_q);
+  if (d.qb >= d.qe || d.qb < 0) return false;
+  d.pos0 = seq_len[s] - (d.qe_raw - d.qb);
+  d.n_rows = min(4, d.qe - d.qb);
   // rows with more than max_blocks candidates are reported by the select;
   // the others still need every score
-  const int nc_last = min((pos0 + n_rows) >> 2, max_blocks);
-  const int v0 = chunk * kDenseChunk;
-  if (v0 >= nc_last) return;
-  const int v1 = min(v0 + kDenseChunk, nc_last);
+  d.nc_last = min((d.pos0 + d.n_rows) >> 2, max_blocks);
+  return true;
+}
+
+template <bool kPaged, int kChunk>
+__device__ __forceinline__ void dense_chunk(const uint16_t* __restrict__ idx_q,
+                                            const float* __restrict__ w, const DenseSeq& d, int s,
+                                            int chunk, const uint16_t* __restrict__ bk,
+                                            int64_t bk_stride, uint32_t* __restrict__ dense,
+                                            int64_t dense_stride, uint32_t* __restrict__ dsmp,
+                                            int64_t dsmp_stride, const Pages& pg,
+                                            float (&s_w)[4][4], int (&s_nc)[4]) {
+  constexpr int kTiles = kChunk / 64;   // tiles per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int qb = d.qb, qe = d.qe, n_rows = d.n_rows;
+  const int v0 = chunk * kChunk;
+  if (v0 >= d.nc_last) return;
+  const int v1 = min(v0 + kChunk, d.nc_last);
   if (threadIdx.x < 4) {
     const int j = threadIdx.x;
     const bool ok = j < n_rows;
     const int rj = min(qb + j, qe - 1);
-    s_nc[j] = ok ? (pos0 + j + 1) >> 2 : 0;
+    s_nc[j] = ok ? (d.pos0 + j + 1) >> 2 : 0;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const float wv = w[(int64_t)rj * 4 + h];
@@ -181,8 +205,8 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
 #endif
   // Workgroups start at different tiles of their chunk (rotated order) so
   // that the ones running together do not stream the same address offsets.
-  const int rot = QSA_DENSE_SKEW ? (int)(((unsigned)s * 7u + (unsigned)chunk * 3u) & (kDenseTiles - 1)) : 0;
-  auto tcol = [&](int t) { return c0 + 64 * ((t + rot) & (kDenseTiles - 1)); };
+  const int rot = QSA_DENSE_SKEW ? (int)(((unsigned)s * 7u + (unsigned)chunk * 3u) & (kTiles - 1)) : 0;
+  auto tcol = [&](int t) { return c0 + 64 * ((t + rot) & (kTiles - 1)); };
   // B fragment of tile t: column tcol(t) + col (clamped in bounds past v1)
   auto load_tile = [&](u32x4 (&bf)[4], int t) {
     const int b = min(tcol(t) + col, v1 - 1);
@@ -197,26 +221,26 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
   };
   u32x4 buf[kDenseDepth][4];
 #pragma unroll
-  for (int d = 0; d < kDenseDepth; ++d) load_tile(buf[d], d);
+  for (int dd = 0; dd < kDenseDepth; ++dd) load_tile(buf[dd], dd);
   __syncthreads();
   // lane holds the 4 heads of query grp for block c0 + 64t + col
   const int j = grp;
   const float wr[4] = {s_w[j][0], s_w[j][1], s_w[j][2], s_w[j][3]};
   const int nc_j = min(s_nc[j], v1);
-  float sc[kDenseTiles];
+  float sc[kTiles];
 #pragma unroll
-  for (int t = 0; t < kDenseTiles; ++t) {
+  for (int t = 0; t < kTiles; ++t) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) acc = mfma_16x16x32(af[ks], buf[t % kDenseDepth][ks], acc);
-    if (t + kDenseDepth < kDenseTiles) load_tile(buf[t % kDenseDepth], t + kDenseDepth);
+    if (t + kDenseDepth < kTiles) load_tile(buf[t % kDenseDepth], t + kDenseDepth);
     sc[t] = block_score(acc, wr);
   }
   if (j < n_rows) {
     uint32_t* drow = dense + (int64_t)(qb + j) * dense_stride;
     uint32_t* srow = dsmp + (int64_t)(qb + j) * dsmp_stride;
 #pragma unroll
-    for (int t = 0; t < kDenseTiles; ++t) {
+    for (int t = 0; t < kTiles; ++t) {
       const int b = tcol(t) + col;
       if (b < nc_j) {
         drow[b] = __float_as_uint(sc[t]);
@@ -224,6 +248,66 @@ score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__
       }
     }
   }
+}
+
+// Grid: n_seq x n_small workgroups (n_small = 256-column chunks of the
+// longest row) when adapt is set, else n_seq x 1024-column chunks.  One
+// linear grid, sequence-major: a sequence's chunks take consecutive
+// workgroup ids, which the dispatcher spreads over the XCDs (a grid of
+// (sequences, chunks) would put every chunk of a sequence on one XCD
+// whenever the sequence count is a multiple of 8).  With 1024-column chunks
+// in an adaptive launch the working workgroups are the first n_seq x
+// n_big ids and the rest exit at once.
+template <bool kPaged>
+__global__ void __launch_bounds__(256, 4)
+score_dense_kernel(const uint16_t* __restrict__ idx_q, const float* __restrict__ w,
+                   const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_len,
+                   int n_seq, int n_q, int max_blocks, const uint16_t* __restrict__ bk,
+                   int64_t bk_stride, uint32_t* __restrict__ dense, int64_t dense_stride,
+                   uint32_t* __restrict__ dsmp, int64_t dsmp_stride, int adapt, Pages pg) {
+  __shared__ float s_w[4][4];
+  __shared__ int s_nc[4];
+  const int n_big = (max_blocks + kDenseChunk - 1) / kDenseChunk;
+  const int id = blockIdx.x;
+  bool big = true;
+  // adaptive launches: lane i of every wave holds sequence i's geometry,
+  // from which the workgroup's own sequence is then taken by a shuffle
+  DenseSeq e = {};
+  bool e_ok = false;
+  if (adapt) {
+    // active 1024-column chunks of the launch (every wave of every
+    // workgroup computes the same sum)
+    const int lane = threadIdx.x & 63;
+    int n = 0;
+    if (lane < n_seq) {
+      e_ok = dense_seq(cu_q, seq_len, n_q, max_blocks, lane, e);
+      if (e_ok && e.nc_last > 0) n = (e.nc_last + kDenseChunk - 1) / kDenseChunk;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o, 64);
+    big = n >= kDenseSlots;
+  }
+  const int n_ch = big ? n_big : (max_blocks + kDenseChunkSmall - 1) / kDenseChunkSmall;
+  if (id >= n_seq * n_ch) return;
+  const int s = id / n_ch, chunk = id % n_ch;
+  DenseSeq d;
+  if (adapt) {
+    if (!__shfl((int)e_ok, s, 64)) return;
+    d.qb = __shfl(e.qb, s, 64);
+    d.qe = __shfl(e.qe, s, 64);
+    d.qe_raw = __shfl(e.qe_raw, s, 64);
+    d.pos0 = __shfl(e.pos0, s, 64);
+    d.n_rows = __shfl(e.n_rows, s, 64);
+    d.nc_last = __shfl(e.nc_last, s, 64);
+  } else if (!dense_seq(cu_q, seq_len, n_q, max_blocks, s, d)) {
+    return;
+  }
+  if (big)
+    dense_chunk<kPaged, kDenseChunk>(idx_q, w, d, s, chunk, bk, bk_stride, dense, dense_stride,
+                                     dsmp, dsmp_stride, pg, s_w, s_nc);
+  else
+    dense_chunk<kPaged, kDenseChunkSmall>(idx_q, w, d, s, chunk, bk, bk_stride, dense,
+                                          dense_stride, dsmp, dsmp_stride, pg, s_w, s_nc);
 }
 
 // ------------------------------------------------------- prefill GEMM
@@ -1551,14 +1635,18 @@ int qsa_index_select(const void* idx_q, const float* w, const int32_t* cu_q,
   if (use_dense(max_q_len)) {
     // decode: dense scores, then one select per row
     if (max_blocks > 0) {
-      const int n_chunks = (max_blocks + kDenseChunk - 1) / kDenseChunk;
+      // launches of few sequences pick their chunk size in the kernel (the
+      // grid then holds the 256-column chunks of every row)
+      const int adapt = n_seq <= kDenseAdaptSeqs ? 1 : 0;
+      const int chunk_cols = adapt ? kDenseChunkSmall : kDenseChunk;
+      const int n_chunks = (max_blocks + chunk_cols - 1) / chunk_cols;
       const int64_t n_wg = (int64_t)n_seq * n_chunks;
       if (n_wg > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
       auto launch = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(256), 0, st, (const uint16_t*)idx_q, w,
-                           cu_q, seq_len, n_q, max_blocks, (const uint16_t*)block_keys,
+                           cu_q, seq_len, n_seq, n_q, max_blocks, (const uint16_t*)block_keys,
                            bk_seq_stride, ws.dense, ws.dense_stride, ws.dsmp, ws.dsmp_stride,
-                           n_chunks, pg);
+                           adapt, pg);
       };
       if (pg.table) launch(score_dense_kernel<true>);
       else launch(score_dense_kernel<false>);

@@ -244,6 +244,17 @@ def test_index_select_exact_grid_decode_long_rows():
     _select_and_check(b, exact=True)
 
 
+def test_index_select_exact_grid_decode_many_sequences():
+    # more than 64 sequences: the dense score pass keeps 1024-column chunks
+    # without counting the launch's chunks (up to 64 sequences choose the
+    # chunk size from their lengths: 256 columns in the smaller decode tests
+    # and the ragged batch, 1024 in the full-size 32 x 128K batches)
+    g = np.random.default_rng(95)
+    lens = [int(x) for x in g.integers(3, 6000, size=70)]
+    b = W.make_decode(seq_lens=lens, budget=512, n_plant=16, seed=95, exact_grid=True)
+    _select_and_check(b, exact=True)
+
+
 def test_index_select_exact_grid_multi_token_tiles():
     # 4 and 3 query rows per sequence (multi-token decode shapes): dense scores
     for prefix, chunk in ((150000, 4), (20001, 3), (9, 4)):

@@ -252,7 +252,13 @@ def test_index_select_exact_grid_decode_many_sequences():
     g = np.random.default_rng(95)
     lens = [int(x) for x in g.integers(3, 6000, size=70)]
     b = W.make_decode(seq_lens=lens, budget=512, n_plant=16, seed=95, exact_grid=True)
-    _select_and_check(b, exact=True)
+    r, _, _ = _select_and_check(b, exact=True)
+    # the same batch over 256-token pages in a random order: same selections
+    rp = QSARunner(r.b, paged=256, page_seed=5)
+    rp.pool()
+    rp.select()
+    _sync()
+    assert torch.equal(rp.sel_count, r.sel_count) and torch.equal(rp.sel, r.sel)
 
 
 def test_index_select_exact_grid_multi_token_tiles():

@@ -885,9 +885,9 @@ def test_full_size_decode_128k_sampled_rows():
 def test_full_size_decode_selections_exact_grid():
     # the benchmarked decode shapes on exact-grid inputs, selections bit-exact:
     # 32 x 128K (1,024 active 1,024-block chunks, so the dense score pass
-    # keeps that size) on sampled rows, and the ragged batch to 1M (few
-    # active chunks: 256-block chunks; its long row compacted in pieces) on
-    # every row
+    # keeps that size) on sampled rows, the ragged batch to 1M (few active
+    # chunks: 256-block chunks; its long row compacted in pieces) on every
+    # row, and the 32 x 4-token multi-token decode on sampled rows
     b = W.decode_128k(device="cuda", exact_grid=True)
     _, _, kinds = _select_and_check(b, exact=True, rows=_sampled(b.n_q, 5, 83, always=(0, 31)))
     print("decode 32 x 128K exact grid:", kinds)
@@ -896,6 +896,12 @@ def test_full_size_decode_selections_exact_grid():
     b = W.ragged_decode(device="cuda", exact_grid=True)
     _, _, kinds = _select_and_check(b, exact=True)
     print("ragged decode exact grid:", kinds)
+    del b
+    torch.cuda.empty_cache()
+    b = W.mtp_decode_128k(device="cuda", exact_grid=True)
+    _, _, kinds = _select_and_check(b, exact=True,
+                                    rows=_sampled(b.n_q, 6, 84, always=(0, 3, b.n_q - 1)))
+    print("mtp decode 32 x 4 at 128K exact grid:", kinds)
 
 
 def test_full_size_mtp_decode_128k_sampled_rows():

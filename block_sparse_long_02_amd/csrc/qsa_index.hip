@@ -1288,6 +1288,8 @@ constexpr int kDensePassQ = 8192;   // quads per pass (32768 scores; 32 per thre
 constexpr int kPieceScores = 4 * kDensePassQ;
 constexpr int kLongRow = 2 * kPieceScores;
 constexpr int kMaxPieces = 64;
+// rows with up to this many samples find their threshold in LDS
+constexpr int kLdsSamples = 4096;
 
 struct DenseShared {
   u32x4 rowq[kDensePassQ];
@@ -1415,6 +1417,26 @@ select_dense_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict_
     __syncthreads();
     tau_s = kth_largest_fast([&](int i) { return sh.u.smp[i]; }, ns, r,
                              KthLds{sh.hist, sh.bin, sh.tmp, sh.res, &sh.bin_n});
+  } else if (ns <= kLdsSamples) {
+    // up to kLdsSamples samples (rows up to 65,536 blocks, e.g. multi-token
+    // rows one block past 32,768): staged in the pass buffer, which is free
+    // until the compaction, and searched in LDS
+    uint32_t* smp = reinterpret_cast<uint32_t*>(sh.rowq);
+    uint32_t tv[kLdsSamples / 256];
+#pragma unroll
+    for (int j = 0; j < kLdsSamples / 256; ++j) {
+      const int i = tid + 256 * j;
+      tv[j] = i < ns ? srow[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kLdsSamples / 256; ++j) {
+      const int i = tid + 256 * j;
+      if (i < ns) smp[i] = tv[j];
+    }
+    __syncthreads();
+    tau_s = kth_largest_fast([&](int i) { return smp[i]; }, ns, r,
+                             KthLds{sh.hist, sh.bin, sh.tmp, sh.res, &sh.bin_n});
+    __syncthreads();   // the pass buffer is rewritten by the compaction
   } else {
     tau_s = kth_largest_global(srow, ns, r, KthLds{sh.hist, sh.bin, sh.tmp, sh.res, &sh.bin_n});
   }
